@@ -1,0 +1,115 @@
+"""CPU oracle of the selective-SSM mixer core (fp64, sequential, slow, plain).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke entry point and the
+benchmark's CPU-baseline leg may use this package; the HIP library and its
+binding never import it, and it never imports them.
+
+``prefill`` and ``decode`` wrap the plain C routines in ``mamba_oracle.c``
+(one token at a time, double precision; see that file for the passages each
+step follows).  ``check`` holds the independent numpy pins (brute-force
+materialised sums, closed forms, library routines) the oracle is tested
+against.
+
+Every function here is pinned by tests that run without a GPU, except where
+"parity unpinned" is stated (none at present).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mamba_oracle.c")
+_LIB = os.path.join(_HERE, "libmamba_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-std=c99", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.oracle_prefill.argtypes = [i64, i32, i32, i32, i32] + [P] * 14 + [ctypes.c_int]
+        lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = [i32, i32, i32, i32] + [P] * 13 + [ctypes.c_int]
+        lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = [ctypes.c_int]
+        lib.oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads(n: int = 0) -> int:
+    """Set (n > 0) and return the OpenMP thread count the oracle uses."""
+    return _load().oracle_threads(int(n))
+
+
+def as_f64(a: np.ndarray, io: str | None = None) -> np.ndarray:
+    """float64 copy of an input; bf16 inputs arrive as uint16 bit patterns."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        a = (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state,
+            nthreads: int = 0):
+    """Run the mixer over packed sequences.  Returns (y, conv_state_out, ssm_state_out), all float64.
+
+    x, z, dt: [T, d]; B, C: [T, N]; A_log: [d, N]; D, dt_bias, conv_b: [d]; conv_w: [d, K];
+    cu_seqlens: [S+1]; conv_state: [S, d, K-1]; ssm_state: [S, d, N] (inputs are not modified).
+    """
+    x, z, dt, B, C = (as_f64(a) for a in (x, z, dt, B, C))
+    A_log, D, dt_bias, conv_w, conv_b = (as_f64(a) for a in (A_log, D, dt_bias, conv_w, conv_b))
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, d = x.shape
+    N = B.shape[1]
+    K = conv_w.shape[1]
+    S = cu.shape[0] - 1
+    cs = as_f64(conv_state).reshape(S, d, K - 1).copy()
+    ss = as_f64(ssm_state).reshape(S, d, N).copy()
+    y = np.zeros((T, d), dtype=np.float64)
+    rc = _load().oracle_prefill(T, S, d, N, K, _p(x), _p(z), _p(dt), _p(B), _p(C), _p(A_log), _p(D),
+                                _p(dt_bias), _p(conv_w), _p(conv_b), _p(cu), _p(cs), _p(ss), _p(y),
+                                int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments (cu_seqlens or dims)")
+    return y, cs, ss
+
+
+def decode(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, nthreads: int = 0):
+    """One decode step for Bs rows.  Returns (y, conv_state_out, ssm_state_out), all float64."""
+    x, z, dt, B, C = (as_f64(a) for a in (x, z, dt, B, C))
+    A_log, D, dt_bias, conv_w, conv_b = (as_f64(a) for a in (A_log, D, dt_bias, conv_w, conv_b))
+    Bs, d = x.shape
+    N = B.shape[1]
+    K = conv_w.shape[1]
+    cs = as_f64(conv_state).reshape(Bs, d, K - 1).copy()
+    ss = as_f64(ssm_state).reshape(Bs, d, N).copy()
+    y = np.zeros((Bs, d), dtype=np.float64)
+    rc = _load().oracle_decode(Bs, d, N, K, _p(x), _p(z), _p(dt), _p(B), _p(C), _p(A_log), _p(D),
+                               _p(dt_bias), _p(conv_w), _p(conv_b), _p(cs), _p(ss), _p(y), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_decode rejected its arguments")
+    return y, cs, ss

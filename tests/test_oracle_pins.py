@@ -1,0 +1,346 @@
+"""Pins of the fp64 CPU oracle against things other than itself (no GPU needed).
+
+Each test names what it pins and why a plausible mistake would fail it.
+"""
+from __future__ import annotations
+
+import json
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from selective_state_space_causal_amd import inputs
+from tests import pins
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand_case(seed, L, d, N, K=4, io="f32", nonzero_state=True):
+    rng = np.random.default_rng(seed)
+    p = inputs.params(seed, d, N, K)
+    tok = inputs.prefill_inputs(seed, L, d, N, io)
+    conv0 = rng.standard_normal((1, d, K - 1)) if nonzero_state else np.zeros((1, d, K - 1))
+    h0 = rng.standard_normal((1, d, N)) if nonzero_state else np.zeros((1, d, N))
+    return tok, p, conv0, h0
+
+
+def _rel(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# --- P1: brute-force materialised sum --------------------------------------------------------
+
+@pytest.mark.parametrize("L,d,N,seed", [(64, 16, 4, 0), (40, 5, 1, 1), (33, 3, 16, 2), (7, 2, 3, 3)])
+def test_oracle_matches_brute_force(oracle_lib, L, d, N, seed):
+    """The sequential oracle equals the unrolled product-sum form (different formula, library conv/softplus)."""
+    tok, p, conv0, h0 = _rand_case(seed, L, d, N)
+    cu = np.array([0, L], dtype=np.int32)
+    y, cs, ss = oracle_lib.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"], p["D"],
+                                   p["dt_bias"], p["conv_w"], p["conv_b"], cu, conv0, h0)
+    yb, csb, ssb = pins.brute_force_sequence(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"],
+                                            p["D"], p["dt_bias"], p["conv_w"], p["conv_b"], conv0[0], h0[0])
+    assert _rel(y, yb) < 1e-12
+    assert _rel(ss[0], ssb) < 1e-12
+    assert np.array_equal(cs[0], csb)
+
+
+def test_brute_force_catches_planted_mistakes(oracle_lib):
+    """Sanity of the pin itself: perturbing one term of the definition moves the brute force well past 1e-12."""
+    tok, p, conv0, h0 = _rand_case(5, 24, 4, 4)
+    cu = np.array([0, 24], dtype=np.int32)
+    y, _, _ = oracle_lib.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"], p["D"],
+                                 p["dt_bias"], p["conv_w"], p["conv_b"], cu, conv0, h0)
+    args = [tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"], p["D"], p["dt_bias"], p["conv_w"],
+            p["conv_b"], conv0[0], h0[0]]
+    # flipped conv taps, dropped D term, B/C swapped: each must disagree
+    flipped = list(args)
+    flipped[8] = p["conv_w"][:, ::-1].copy()
+    noD = list(args)
+    noD[6] = np.zeros_like(p["D"])
+    swapped = list(args)
+    swapped[3], swapped[4] = tok["C"], tok["B"]
+    for bad in (flipped, noD, swapped):
+        yb, _, _ = pins.brute_force_sequence(*bad)
+        assert _rel(y, yb) > 1e-6
+
+
+# --- P2: geometric closed form ----------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 4, 16])
+def test_oracle_geometric_closed_form(oracle_lib, N):
+    L, d, K = 300, 1, 4
+    x0, z0, dtv = 0.7, 1.3, -0.4
+    rng = np.random.default_rng(N)
+    Bv, Cv = rng.standard_normal(N), rng.standard_normal(N)
+    A_log = np.log(np.arange(1, N + 1, dtype=np.float64))[None, :] * 0.5
+    w = np.array([[0.3, -0.2, 0.1, 0.4]])
+    b = np.array([0.05])
+    D = np.array([0.9])
+    dtb = np.array([-1.5])
+    h0 = rng.standard_normal((1, d, N))
+    conv0 = np.full((1, d, K - 1), x0)
+    x = np.full((L, d), x0)
+    z = np.full((L, d), z0)
+    dt = np.full((L, d), dtv)
+    B = np.tile(Bv, (L, 1))
+    C = np.tile(Cv, (L, 1))
+    y, _, ss = oracle_lib.prefill(x, z, dt, B, C, A_log, D, dtb, w, b, np.array([0, L], np.int32), conv0, h0)
+    yc, hc = pins.geometric_closed_form(L, x0, z0, dtv, Bv, Cv, A_log[0], D[0], dtb[0], w[0], b[0], h0[0, 0])
+    assert _rel(y[:, 0], yc) < 1e-12
+    assert _rel(ss[0, 0], hc) < 1e-12
+
+
+# --- P3: library routines -------------------------------------------------------------------
+
+def test_oracle_scan_is_lfilter(oracle_lib):
+    """N = 1, constant delta, B = C = 1: the state is a first-order IIR filter of delta*u."""
+    L = 500
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((L, 1))
+    z = np.full((L, 1), 40.0)  # silu(40) = 40 to double precision
+    dt = np.zeros((L, 1))
+    dtb = np.array([-2.0])
+    A_log = np.array([[np.log(3.0)]])
+    w = np.array([[0.2, -0.1, 0.3, 0.5]])
+    b = np.array([0.1])
+    conv0 = rng.standard_normal((1, 1, 3))
+    h0 = np.array([[[0.6]]])
+    y, _, ss = oracle_lib.prefill(x, z, dt, np.ones((L, 1)), np.ones((L, 1)), A_log, np.zeros(1), dtb, w, b,
+                                  np.array([0, L], np.int32), conv0, h0)
+    X = np.concatenate([conv0[0].T, x])[:, 0]
+    xc = np.convolve(X, w[0, ::-1], mode="valid") + b[0]
+    u = xc * expit(xc)
+    delta = float(np.logaddexp(0.0, dtb[0]))
+    h = pins.lfilter_scan(u, delta, -3.0, 0.6)
+    gate = 40.0 * expit(40.0)
+    assert _rel(y[:, 0], h * gate) < 1e-12
+    assert abs(ss[0, 0, 0] - h[-1]) <= 1e-12 * abs(h[-1])
+
+
+def test_oracle_pure_decay_closed_form(oracle_lib):
+    """u == 0 (zero conv weights and bias): h_t = exp(A * sum_{r<=t} delta_r) h0; delta = logaddexp(0, v)."""
+    L, N = 200, 4
+    rng = np.random.default_rng(11)
+    v = np.linspace(-35.0, 35.0, L)  # also pins the softplus far in both tails
+    dt = v[:, None]
+    A_log = np.log(np.array([[0.01, 0.02, 0.003, 0.05]]))
+    h0 = rng.standard_normal((1, 1, N))
+    C = rng.standard_normal((L, N))
+    z = np.full((L, 1), 1.7)
+    y, _, ss = oracle_lib.prefill(rng.standard_normal((L, 1)), z, dt, rng.standard_normal((L, N)), C, A_log,
+                                  np.ones(1), np.zeros(1), np.zeros((1, 4)), np.zeros(1),
+                                  np.array([0, L], np.int32), np.zeros((1, 1, 3)), h0)
+    delta = np.logaddexp(0.0, v)
+    h = np.exp(np.cumsum(delta)[:, None] * (-np.exp(A_log[0]))[None, :]) * h0[0, 0][None, :]
+    yref = np.sum(C * h, axis=1) * (1.7 * expit(1.7))
+    np.testing.assert_allclose(y[:, 0], yref, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(ss[0, 0], h[-1], rtol=1e-12, atol=0)
+
+
+def test_oracle_softplus_tail_precision(oracle_lib):
+    """One token, u == 0: -log(h1/h0)/|A| recovers delta; it must match logaddexp to ~1e-13 even at v = -30.
+
+    |A| is set to 1/delta so that the decay exp(-delta |A|) = 1/e keeps full relative precision; a
+    naive log(exp(v) + 1) is off by ~1e-3 relative at v = -30 in double precision and fails here.
+    """
+    for v in (-30.0, -12.0, -1.0, 0.0, 2.5, 18.0):
+        ref = float(np.logaddexp(0.0, v))
+        h0 = np.array([[[1.0]]])
+        A_log = np.array([[np.log(1.0 / ref)]])
+        Aabs = float(np.exp(A_log[0, 0]))
+        _, _, ss = oracle_lib.prefill(np.zeros((1, 1)), np.zeros((1, 1)), np.array([[v]]), np.zeros((1, 1)),
+                                      np.zeros((1, 1)), A_log, np.ones(1), np.zeros(1), np.zeros((1, 4)),
+                                      np.zeros(1), np.array([0, 1], np.int32), np.zeros((1, 1, 3)), h0)
+        delta = -np.log(ss[0, 0, 0]) / Aabs
+        assert abs(delta - ref) <= 1e-13 * ref, (v, delta, ref)
+
+
+def test_oracle_conv_orientation_impulse(oracle_lib):
+    """An impulse at token 0 with zero state: token p sees tap K-1-p (the newest tap weights the current token)."""
+    K, L = 4, 6
+    w = np.array([[0.11, -0.23, 0.37, 0.53]])
+    x = np.zeros((L, 1))
+    x[0, 0] = 1.0
+    z = np.full((L, 1), 40.0)
+    y, _, _ = oracle_lib.prefill(x, z, np.zeros((L, 1)), np.zeros((L, 1)), np.zeros((L, 1)),
+                                 np.zeros((1, 1)), np.ones(1), np.zeros(1), w, np.zeros(1),
+                                 np.array([0, L], np.int32), np.zeros((1, 1, K - 1)), np.zeros((1, 1, 1)))
+    gate = 40.0 * expit(40.0)
+    for p in range(L):
+        xc = w[0, K - 1 - p] if p < K else 0.0
+        assert abs(y[p, 0] - xc * expit(xc) * gate) <= 1e-13
+
+
+def test_oracle_conv_window_golden(oracle_lib):
+    """The conv-state shift and first-token window of the TensorRT builder's step (tests/golden fixture)."""
+    with open(os.path.join(HERE, "golden", "conv_window_shift.json")) as f:
+        g = json.load(f)
+    w = np.array([g["conv_w"]])
+    for case in g["cases"]:
+        L = len(case["x"])
+        x = np.array(case["x"], dtype=np.float64).reshape(L, 1)
+        z = np.full((L, 1), 40.0)
+        y, cs, _ = oracle_lib.prefill(x, z, np.zeros((L, 1)), np.zeros((L, 1)), np.zeros((L, 1)),
+                                      np.zeros((1, 1)), np.ones(1), np.zeros(1), w, np.array([g["conv_b"]]),
+                                      np.array([0, L], np.int32), np.array(case["state_in"]).reshape(1, 1, 3),
+                                      np.zeros((1, 1, 1)))
+        assert cs[0, 0].tolist() == case["state_out"]
+        xc = case["xc_first"]
+        assert abs(y[0, 0] - xc * expit(xc) * 40.0 * expit(40.0)) <= 1e-13
+
+
+def test_oracle_one_step_high_precision(oracle_lib):
+    """One decode step evaluated independently with 50-digit decimal arithmetic."""
+    getcontext().prec = 50
+    N, K = 3, 4
+    win = [Decimal("0.25"), Decimal("-1.5"), Decimal("0.75")]
+    x, z, dt = Decimal("0.5"), Decimal("-0.8"), Decimal("0.3")
+    w = [Decimal("0.1"), Decimal("-0.2"), Decimal("0.3"), Decimal("0.4")]
+    b, D, dtb = Decimal("0.05"), Decimal("1.25"), Decimal("-0.6")
+    A_log = [Decimal("0"), Decimal("0.5"), Decimal("-0.7")]
+    Bv = [Decimal("0.9"), Decimal("-0.3"), Decimal("1.1")]
+    Cv = [Decimal("-0.4"), Decimal("0.8"), Decimal("0.2")]
+    h = [Decimal("0.3"), Decimal("-0.6"), Decimal("1.2")]
+    one = Decimal(1)
+
+    def sig(v):
+        return one / (one + (-v).exp())
+
+    xc = b + sum(wk * xk for wk, xk in zip(w, win + [x]))
+    u = xc * sig(xc)
+    delta = (one + (dt + dtb).exp()).ln()
+    hn = [(delta * -(al.exp())).exp() * hh + delta * bb * u for al, hh, bb in zip(A_log, h, Bv)]
+    y = (sum(c * hh for c, hh in zip(Cv, hn)) + D * u) * z * sig(z)
+    f = lambda v: np.array([[float(q) for q in v]])
+    yo, cso, sso = oracle_lib.decode(np.array([[float(x)]]), np.array([[float(z)]]), np.array([[float(dt)]]),
+                                     f(Bv), f(Cv), f(A_log), np.array([float(D)]), np.array([float(dtb)]),
+                                     f(w), np.array([float(b)]), f(win).reshape(1, 1, 3),
+                                     f(h).reshape(1, 1, N))
+    assert abs(yo[0, 0] - float(y)) <= 1e-15 * abs(float(y)) + 1e-17
+    assert cso[0, 0].tolist() == [float(win[1]), float(win[2]), float(x)]
+    for n in range(N):
+        assert abs(sso[0, 0, n] - float(hn[n])) <= 1e-15 * abs(float(hn[n]))
+    del K
+
+
+# --- P4/P5/P6: invariants, bit-exact in the oracle ------------------------------------------------
+
+def test_oracle_packed_equals_separate(oracle_lib):
+    lens = [17, 0, 1, 2, 40, 5]
+    d, N, K = 6, 4, 4
+    T = sum(lens)
+    tok, p, _, _ = _rand_case(21, T, d, N)
+    rng = np.random.default_rng(3)
+    S = len(lens)
+    conv0 = rng.standard_normal((S, d, K - 1))
+    h0 = rng.standard_normal((S, d, N))
+    cu = inputs.cu_from_lengths(lens)
+    y, cs, ss = oracle_lib.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"], p["D"],
+                                   p["dt_bias"], p["conv_w"], p["conv_b"], cu, conv0, h0)
+    for s in range(S):
+        g0, g1 = cu[s], cu[s + 1]
+        sl = slice(g0, g1)
+        ys, css, sss = oracle_lib.prefill(tok["x"][sl], tok["z"][sl], tok["dt"][sl], tok["B"][sl], tok["C"][sl],
+                                          p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"],
+                                          np.array([0, g1 - g0], np.int32), conv0[s:s + 1], h0[s:s + 1])
+        assert np.array_equal(y[sl], ys)
+        assert np.array_equal(cs[s], css[0]) and np.array_equal(ss[s], sss[0])
+    # the empty sequence leaves its slot untouched
+    assert np.array_equal(cs[1], conv0[1]) and np.array_equal(ss[1], h0[1])
+
+
+def test_oracle_chunked_equals_one_shot(oracle_lib):
+    L, d, N = 97, 5, 8
+    tok, p, conv0, h0 = _rand_case(31, L, d, N)
+    args = (p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"])
+    y, cs, ss = oracle_lib.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], *args,
+                                   np.array([0, L], np.int32), conv0, h0)
+    cs_c, ss_c = conv0, h0
+    ys = []
+    for a, b in [(0, 1), (1, 3), (3, 40), (40, 41), (41, 97)]:
+        sl = slice(a, b)
+        yk, cs_c, ss_c = oracle_lib.prefill(tok["x"][sl], tok["z"][sl], tok["dt"][sl], tok["B"][sl],
+                                            tok["C"][sl], *args, np.array([0, b - a], np.int32), cs_c, ss_c)
+        ys.append(yk)
+    assert np.array_equal(np.concatenate(ys), y)
+    assert np.array_equal(cs_c, cs) and np.array_equal(ss_c, ss)
+
+
+def test_oracle_decode_steps_equal_scan(oracle_lib):
+    Bs, L, d, N = 3, 12, 4, 16
+    T = Bs * L
+    tok, p, _, _ = _rand_case(41, T, d, N)
+    rng = np.random.default_rng(4)
+    conv0 = rng.standard_normal((Bs, d, 3))
+    h0 = rng.standard_normal((Bs, d, N))
+    args = (p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"])
+    cu = inputs.cu_from_lengths([L] * Bs)
+    y, cs, ss = oracle_lib.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], *args, cu, conv0, h0)
+    cs_d, ss_d = conv0, h0
+    for t in range(L):
+        rows = [r * L + t for r in range(Bs)]
+        yd, cs_d, ss_d = oracle_lib.decode(tok["x"][rows], tok["z"][rows], tok["dt"][rows], tok["B"][rows],
+                                           tok["C"][rows], *args, cs_d, ss_d)
+        assert np.array_equal(yd, y[rows])
+    assert np.array_equal(cs_d, cs) and np.array_equal(ss_d, ss)
+    # decode == prefill with one token per sequence
+    yp, csp, ssp = oracle_lib.prefill(tok["x"][:Bs], tok["z"][:Bs], tok["dt"][:Bs], tok["B"][:Bs],
+                                      tok["C"][:Bs], *args, np.arange(Bs + 1, dtype=np.int32), conv0, h0)
+    yd, csd, ssd = oracle_lib.decode(tok["x"][:Bs], tok["z"][:Bs], tok["dt"][:Bs], tok["B"][:Bs],
+                                     tok["C"][:Bs], *args, conv0, h0)
+    assert np.array_equal(yp, yd) and np.array_equal(csp, csd) and np.array_equal(ssp, ssd)
+
+
+def test_oracle_isolation_and_channel_subset(oracle_lib):
+    lens = [9, 30, 4]
+    d, N = 12, 4
+    T = sum(lens)
+    tok, p, _, _ = _rand_case(51, T, d, N)
+    rng = np.random.default_rng(5)
+    conv0 = rng.standard_normal((3, d, 3))
+    h0 = rng.standard_normal((3, d, N))
+    cu = inputs.cu_from_lengths(lens)
+    args = (p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"])
+    y, cs, ss = oracle_lib.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], *args, cu, conv0, h0)
+    # perturb sequence 1 only: sequences 0 and 2 are bit-identical
+    x2 = tok["x"].copy()
+    x2[cu[1]:cu[2]] += 1.0
+    h2 = h0.copy()
+    h2[1] *= -3.0
+    y2, cs2, ss2 = oracle_lib.prefill(x2, tok["z"], tok["dt"], tok["B"], tok["C"], *args, cu, conv0, h2)
+    for s in (0, 2):
+        sl = slice(cu[s], cu[s + 1])
+        assert np.array_equal(y[sl], y2[sl]) and np.array_equal(ss[s], ss2[s]) and np.array_equal(cs[s], cs2[s])
+    assert not np.array_equal(y[cu[1]:cu[2]], y2[cu[1]:cu[2]])
+    # channel subset
+    ch = np.array([1, 5, 6, 11])
+    ys, css, sss = oracle_lib.prefill(tok["x"][:, ch], tok["z"][:, ch], tok["dt"][:, ch], tok["B"], tok["C"],
+                                      p["A_log"][ch], p["D"][ch], p["dt_bias"][ch], p["conv_w"][ch],
+                                      p["conv_b"][ch], cu, conv0[:, ch], h0[:, ch])
+    assert np.array_equal(ys, y[:, ch]) and np.array_equal(css, cs[:, ch]) and np.array_equal(sss, ss[:, ch])
+
+
+def test_oracle_rejects_bad_cu(oracle_lib):
+    tok, p, conv0, h0 = _rand_case(1, 8, 2, 2)
+    args = (p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"])
+    for cu in ([0, 9], [1, 8], [0, 5, 3, 8]):
+        cu = np.array(cu, np.int32)
+        S = len(cu) - 1
+        with pytest.raises(ValueError):
+            oracle_lib.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], *args, cu,
+                               np.zeros((S, 2, 3)), np.zeros((S, 2, 2)))
+
+
+def test_oracle_bf16_inputs_are_widened_exactly(oracle_lib):
+    """bf16 inputs (uint16 bit patterns) enter the oracle as their exact values."""
+    v = np.array([1.0, -2.5, 3.140625, 1e-3, -65504.0], dtype=np.float32)
+    bits = inputs.f32_to_bf16_bits(v)
+    back = oracle_lib.as_f64(bits)
+    assert np.array_equal(back, inputs.bf16_bits_to_f32(bits).astype(np.float64))
+    # RNE: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> rounds to even (1.0)
+    assert inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(np.array([1.0 + 2.0 ** -8], np.float32)))[0] == 1.0
+    assert inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(np.array([1.0 + 3 * 2.0 ** -8], np.float32)))[0] == 1.0 + 2.0 ** -6
