@@ -1,0 +1,160 @@
+/*
+ * mambamix.h -- C ABI of libmambamix, the data-parallel core of the Mamba
+ * selective state-space mixer on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (per sequence s, token position p, channel c):
+ *
+ *   window   = [the K-1 previous raw inputs of channel c, x[p,c]]   (newest last)
+ *   u        = SiLU(conv_b[c] + sum_k conv_w[c,k] * window[k])
+ *   delta    = softplus(dt[p,c] + dt_bias[c])
+ *   A[c,n]   = -exp(A_log[c,n])
+ *   h[c,n]   = exp(delta * A[c,n]) * h[c,n] + delta * B[p,n] * u
+ *   y[p,c]   = (sum_n C[p,n] * h[c,n] + D[c] * u) * SiLU(z[p,c])
+ *
+ * This is the one-token step of the Mamba mixer as the TensorRT Mamba
+ * tensor-parallel builder spells it out (NVIDIA TensorRT-Model-Connect,
+ * families/mamba/tp_builder.py, _add_mamba_tp_layer: the conv window is the
+ * state's newest columns with x appended; softplus of the biased dt;
+ * A_bar = exp(dt * A); the state update; the readout from the updated state
+ * plus D * u; the SiLU(z) gate), applied token after token.  The input and
+ * output projections, the normalisation and the all-reduces around it are not
+ * part of this library.
+ *
+ * Packed variable-length sequences (PackMamba page, abstract): a prefill call
+ * takes S sequences laid end to end in one token stream, delimited by
+ * cu_seqlens; no state passes from one sequence to the next.  The state cache
+ * (tensor-parallel SSM page, abstract and Fig. 2 component (1)): sequence s
+ * starts from slot s of conv_state / ssm_state and leaves its final state
+ * there, so a later prefill call (a further chunk) or a decode step continues
+ * it.  A zeroed slot is a fresh sequence.
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are DEVICE pointers except where stated.  Arrays are
+ *    row-major with the last index contiguous.
+ *  - "io" arrays (x, z, dt, B, C, y) hold MM_IO_F32 (float) or MM_IO_BF16
+ *    (bfloat16 bit patterns, 2 bytes) elements; parameters and states are
+ *    always float32.  bf16 outputs are rounded to nearest even.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *    null stream).  The library allocates no memory, keeps no pointer and no
+ *    global mutable state; calls on different streams may run concurrently
+ *    provided their output buffers do not overlap.
+ *  - The caller owns every buffer.  The states are read as the initial state
+ *    and overwritten in place with the final state.
+ *  - Return value: MM_OK (0) or a negative MM_ERR_* code.  Argument errors are
+ *    detected on the host before anything is enqueued, and nothing is written
+ *    then.  MM_ERR_HIP reports a failed kernel launch.
+ *  - Preconditions NOT checked (checking would need a device sync):
+ *    cu_seqlens[0] == 0, cu_seqlens non-decreasing, cu_seqlens[S] == T.
+ *    Violating them is undefined behaviour.
+ */
+#ifndef MAMBAMIX_H
+#define MAMBAMIX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MM_OK               0
+#define MM_ERR_NULL        -1  /* a required pointer is NULL                                  */
+#define MM_ERR_DIM         -2  /* a negative size, T > INT32_MAX, or S == 0 with T > 0          */
+#define MM_ERR_UNSUPPORTED -3  /* K != 4, N outside 1..16, or unknown io dtype                  */
+#define MM_ERR_ALIGN       -4  /* a pointer not aligned to its element size                    */
+#define MM_ERR_WORKSPACE   -5  /* workspace smaller than the size query returns (or NULL)      */
+#define MM_ERR_ALIAS       -6  /* y overlaps an input, or conv_state overlaps ssm_state         */
+#define MM_ERR_HIP         -7  /* a kernel launch failed                                        */
+
+/* io element types */
+#define MM_IO_F32  0
+#define MM_IO_BF16 1
+
+/* limits of this build */
+#define MM_MAX_N 16
+#define MM_CONV_K 4
+
+/*
+ * mamba_mixer_prefill -- run the mixer over S packed sequences.
+ *
+ *   x, z, dt      [T, d]      io     token inputs: SSM-path input (pre-conv), gate input,
+ *                                    and the dt-projection output before dt_bias
+ *   B, C          [T, N]      io     input and readout vectors, shared by all channels
+ *   A_log         [d, N]      f32    A = -exp(A_log)
+ *   D, dt_bias    [d]         f32
+ *   conv_w        [d, K]      f32    conv_w[c, K-1] weights the current token
+ *   conv_b        [d]         f32
+ *   cu_seqlens    [S+1]       int32  sequence s is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1
+ *   conv_state    [S, d, K-1] f32    in/out: the K-1 newest raw inputs x, oldest first
+ *   ssm_state     [S, d, N]   f32    in/out: the SSM state h
+ *   y             [T, d]      io     out
+ *   workspace     device scratch of at least mamba_mixer_prefill_workspace_bytes(S,T,d,N,K)
+ *                 bytes, 256-byte aligned; its contents on entry do not matter.
+ *
+ * An empty sequence (cu_seqlens[s] == cu_seqlens[s+1]) leaves slot s unchanged.
+ * A sequence shorter than K-1 tokens keeps the older entries of its conv state
+ * (they shift towards the front).  T == 0 or d == 0 is a successful no-op.
+ */
+int mamba_mixer_prefill(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                        const float* A_log, const float* D, const float* dt_bias,
+                        const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                        float* conv_state, float* ssm_state, void* y,
+                        int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mamba_mixer_prefill needs for these sizes (0 is possible).  Host only. */
+size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
+
+/*
+ * mamba_mixer_prefill_chunked -- mamba_mixer_prefill with an explicit time-chunk
+ * length.  The token stream is cut into chunks of `chunk_len` tokens that are
+ * processed in parallel and stitched with the associative combine of the
+ * recurrence; chunk_len <= 0 picks the length mamba_mixer_prefill uses.  The
+ * result does not depend on chunk_len beyond floating-point rounding.  The
+ * workspace size for a given chunk_len comes from
+ * mamba_mixer_prefill_workspace_bytes_chunked.
+ */
+int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                const float* A_log, const float* D, const float* dt_bias,
+                                const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                                float* conv_state, float* ssm_state, void* y,
+                                int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                                int64_t chunk_len, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t mamba_mixer_prefill_workspace_bytes_chunked(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
+                                                   int64_t chunk_len);
+
+/* The chunk length mamba_mixer_prefill picks for these sizes (host only). */
+int64_t mamba_mixer_prefill_chunk_len(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
+
+/*
+ * mamba_mixer_decode -- one token for each of Bs independent rows; row r uses
+ * state slot r.  This is the TensorRT builder's single-token step with a batch
+ * dimension (same arithmetic as a prefill of Bs one-token sequences).
+ *
+ *   x, z, dt      [Bs, d]       io
+ *   B, C          [Bs, N]       io
+ *   A_log [d, N], D [d], dt_bias [d], conv_w [d, K], conv_b [d]   f32
+ *   conv_state    [Bs, d, K-1]  f32 in/out (drops its oldest entry, appends x)
+ *   ssm_state     [Bs, d, N]    f32 in/out
+ *   y             [Bs, d]       io  out
+ * Bs == 0 or d == 0 is a successful no-op.
+ */
+int mamba_mixer_decode(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                       const float* A_log, const float* D, const float* dt_bias,
+                       const float* conv_w, const float* conv_b,
+                       float* conv_state, float* ssm_state, void* y,
+                       int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype, void* stream);
+
+/* Static text for a status code (never NULL).  Host only. */
+const char* mamba_mixer_status_string(int status);
+
+/* Library version, e.g. "libmambamix 0.1 gfx950".  Host only. */
+const char* mamba_mixer_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBAMIX_H */

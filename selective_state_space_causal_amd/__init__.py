@@ -1,1 +1,178 @@
-"""libmambamix: the selective-SSM mixer core as a C-ABI HIP library for gfx950 (MI355X)."""
+"""libmambamix: the selective-SSM mixer core as a C-ABI HIP library for gfx950 (MI355X).
+
+This module is a thin ctypes binding of ``include/mambamix.h``.  It only checks
+shapes/dtypes, allocates outputs and workspace with torch (device memory and
+streams are all torch is used for) and passes raw device pointers to the C ABI;
+every step of the computation runs in the HIP kernels of ``libmambamix.so``.
+There is no CPU or PyTorch fallback: if the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmambamix.so")
+
+MM_OK = 0
+MM_IO_F32 = 0
+MM_IO_BF16 = 1
+MAX_N = 16
+CONV_K = 4
+
+_lib = None
+
+
+class MambaMixError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} (status {code})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libmambamix.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.mamba_mixer_prefill.argtypes = [P] * 14 + [i32, i64, i32, i32, i32, i32, P, sz, P]
+    lib.mamba_mixer_prefill.restype = ctypes.c_int
+    lib.mamba_mixer_prefill_chunked.argtypes = [P] * 14 + [i32, i64, i32, i32, i32, i32, i64, P, sz, P]
+    lib.mamba_mixer_prefill_chunked.restype = ctypes.c_int
+    lib.mamba_mixer_prefill_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.mamba_mixer_prefill_workspace_bytes.restype = sz
+    lib.mamba_mixer_prefill_workspace_bytes_chunked.argtypes = [i32, i64, i32, i32, i32, i64]
+    lib.mamba_mixer_prefill_workspace_bytes_chunked.restype = sz
+    lib.mamba_mixer_prefill_chunk_len.argtypes = [i32, i64, i32, i32, i32]
+    lib.mamba_mixer_prefill_chunk_len.restype = i64
+    lib.mamba_mixer_decode.argtypes = [P] * 13 + [i32, i32, i32, i32, i32, P]
+    lib.mamba_mixer_decode.restype = ctypes.c_int
+    lib.mamba_mixer_status_string.argtypes = [ctypes.c_int]
+    lib.mamba_mixer_status_string.restype = ctypes.c_char_p
+    lib.mamba_mixer_version.argtypes = []
+    lib.mamba_mixer_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().mamba_mixer_status_string(int(code)).decode()
+
+
+def version() -> str:
+    return load().mamba_mixer_version().decode()
+
+
+def workspace_bytes(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0) -> int:
+    return int(load().mamba_mixer_prefill_workspace_bytes_chunked(S, T, d, N, K, chunk_len))
+
+
+def chunk_len(S: int, T: int, d: int, N: int, K: int = CONV_K) -> int:
+    return int(load().mamba_mixer_prefill_chunk_len(S, T, d, N, K))
+
+
+def _io_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return MM_IO_F32
+    if t.dtype == torch.bfloat16:
+        return MM_IO_BF16
+    raise TypeError(f"io tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state,
+            y=None, workspace=None, chunk_len: int = 0, stream=None):
+    """Run the mixer over packed sequences; conv_state / ssm_state are updated in place.
+
+    x, z, dt [T, d] and B, C [T, N] share one io dtype (float32 or bfloat16); A_log [d, N],
+    D/dt_bias/conv_b [d], conv_w [d, 4], conv_state [S, d, 3], ssm_state [S, d, N] are float32;
+    cu_seqlens [S+1] int32.  Returns y [T, d] (io dtype).
+    """
+    import torch
+
+    T, d = x.shape
+    N = B.shape[1]
+    S = cu_seqlens.shape[0] - 1
+    io = x.dtype
+    for t, n in ((x, "x"), (z, "z"), (dt, "dt")):
+        _check(t, (T, d), io, n)
+    for t, n in ((B, "B"), (C, "C")):
+        _check(t, (T, N), io, n)
+    _check(A_log, (d, N), torch.float32, "A_log")
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (conv_b, "conv_b")):
+        _check(t, (d,), torch.float32, n)
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
+    if y is None:
+        y = torch.empty((T, d), dtype=io, device=x.device)
+    _check(y, (T, d), io, "y")
+    need = workspace_bytes(S, T, d, N, CONV_K, chunk_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().mamba_mixer_prefill_chunked(
+        _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(conv_w),
+        _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(ssm_state), _ptr(y),
+        S, T, d, N, CONV_K, _io_code(x), int(chunk_len), wptr, wbytes, _stream(stream))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_prefill")
+    return y
+
+
+def decode(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y=None, stream=None):
+    """One decode step for Bs rows (row r uses slot r); states are updated in place.  Returns y [Bs, d]."""
+    import torch
+
+    Bs, d = x.shape
+    N = B.shape[1]
+    io = x.dtype
+    for t, n in ((x, "x"), (z, "z"), (dt, "dt")):
+        _check(t, (Bs, d), io, n)
+    for t, n in ((B, "B"), (C, "C")):
+        _check(t, (Bs, N), io, n)
+    _check(A_log, (d, N), torch.float32, "A_log")
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (conv_b, "conv_b")):
+        _check(t, (d,), torch.float32, n)
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(conv_state, (Bs, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (Bs, d, N), torch.float32, "ssm_state")
+    if y is None:
+        y = torch.empty((Bs, d), dtype=io, device=x.device)
+    _check(y, (Bs, d), io, "y")
+    rc = load().mamba_mixer_decode(
+        _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(conv_w),
+        _ptr(conv_b), _ptr(conv_state), _ptr(ssm_state), _ptr(y), Bs, d, N, CONV_K, _io_code(x),
+        _stream(stream))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_decode")
+    return y

@@ -1,0 +1,148 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point,
+and rejects bad arguments on the host before anything is enqueued."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_causal_amd as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MM_ERR_NULL, MM_ERR_DIM, MM_ERR_UNSUPPORTED, MM_ERR_ALIGN, MM_ERR_WORKSPACE, MM_ERR_ALIAS = -1, -2, -3, -4, -5, -6
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(mamba_mixer_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mm.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert mm.version().startswith("libmambamix")
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 42):
+        s = mm.status_string(code)
+        assert isinstance(s, str) and s
+
+
+# fake, well-aligned device addresses: the calls below must fail validation before touching them
+A = 0x10000000
+STEP = 0x01000000
+
+
+def _ptrs(n, start=A):
+    return [ctypes.c_void_p(start + i * STEP) for i in range(n)]
+
+
+def _prefill(lib, ptrs, S=2, T=100, d=64, N=16, K=4, io=1, ws=None, wsb=0, chunk=0):
+    return lib.mamba_mixer_prefill_chunked(*ptrs, S, T, d, N, K, io, chunk, ws, wsb, None)
+
+
+def _decode(lib, ptrs, Bs=2, d=64, N=16, K=4, io=1):
+    return lib.mamba_mixer_decode(*ptrs, Bs, d, N, K, io, None)
+
+
+def test_prefill_validation(lib):
+    p = _ptrs(14)
+    ws_need = mm.workspace_bytes(2, 100, 64, 16)
+    assert ws_need > 0
+    ws = ctypes.c_void_p(0x70000000)
+    assert _prefill(lib, p, K=3, ws=ws, wsb=ws_need) == MM_ERR_UNSUPPORTED
+    assert _prefill(lib, p, N=17, ws=ws, wsb=ws_need) == MM_ERR_UNSUPPORTED
+    assert _prefill(lib, p, N=0, ws=ws, wsb=ws_need) == MM_ERR_UNSUPPORTED
+    assert _prefill(lib, p, io=7, ws=ws, wsb=ws_need) == MM_ERR_UNSUPPORTED
+    assert _prefill(lib, p, T=-1, ws=ws, wsb=ws_need) == MM_ERR_DIM
+    assert _prefill(lib, p, S=-1, ws=ws, wsb=ws_need) == MM_ERR_DIM
+    assert _prefill(lib, p, d=-5, ws=ws, wsb=ws_need) == MM_ERR_DIM
+    assert _prefill(lib, p, S=0, T=10, ws=ws, wsb=ws_need) == MM_ERR_DIM
+    assert _prefill(lib, p, T=2 ** 31, ws=ws, wsb=ws_need) == MM_ERR_DIM
+    for i in range(14):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert _prefill(lib, q, ws=ws, wsb=ws_need) == MM_ERR_NULL, i
+    # misaligned bf16 x and misaligned fp32 parameter
+    q = list(p)
+    q[0] = ctypes.c_void_p(A + 1)
+    assert _prefill(lib, q, ws=ws, wsb=ws_need) == MM_ERR_ALIGN
+    q = list(p)
+    q[6] = ctypes.c_void_p(p[6].value + 2)
+    assert _prefill(lib, q, ws=ws, wsb=ws_need) == MM_ERR_ALIGN
+    # bf16 io only needs 2-byte alignment
+    q = list(p)
+    q[0] = ctypes.c_void_p(A + 2)
+    assert _prefill(lib, q, ws=None, wsb=0) == MM_ERR_WORKSPACE
+    # workspace too small / missing / misaligned
+    assert _prefill(lib, p, ws=ws, wsb=ws_need - 1) == MM_ERR_WORKSPACE
+    assert _prefill(lib, p, ws=None, wsb=ws_need) == MM_ERR_WORKSPACE
+    assert _prefill(lib, p, ws=ctypes.c_void_p(0x70000010), wsb=ws_need) == MM_ERR_ALIGN
+    # y aliasing x, and conv_state overlapping ssm_state
+    q = list(p)
+    q[13] = q[0]
+    assert _prefill(lib, q, ws=ws, wsb=ws_need) == MM_ERR_ALIAS
+    q = list(p)
+    q[12] = ctypes.c_void_p(q[11].value + 64)
+    assert _prefill(lib, q, ws=ws, wsb=ws_need) == MM_ERR_ALIAS
+    # empty problems succeed without touching anything (null pointers allowed then)
+    z = [ctypes.c_void_p(0)] * 14
+    assert _prefill(lib, z, S=0, T=0) == 0
+    assert _prefill(lib, z, S=3, T=0) == 0
+    assert _prefill(lib, z, S=3, T=5, d=0) == 0
+
+
+def test_decode_validation(lib):
+    p = _ptrs(13)
+    assert _decode(lib, p, K=5) == MM_ERR_UNSUPPORTED
+    assert _decode(lib, p, N=32) == MM_ERR_UNSUPPORTED
+    assert _decode(lib, p, io=2) == MM_ERR_UNSUPPORTED
+    assert _decode(lib, p, Bs=-1) == MM_ERR_DIM
+    for i in range(13):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert _decode(lib, q) == MM_ERR_NULL, i
+    q = list(p)
+    q[3] = ctypes.c_void_p(A + 1)
+    assert _decode(lib, q) == MM_ERR_ALIGN
+    q = list(p)
+    q[12] = q[2]
+    assert _decode(lib, q) == MM_ERR_ALIAS
+    assert _decode(lib, [ctypes.c_void_p(0)] * 13, Bs=0) == 0
+
+
+def test_workspace_query_and_chunk_plan(lib):
+    assert mm.workspace_bytes(0, 0, 64, 16) == 0
+    assert mm.workspace_bytes(1, 64, 16, 4) > 0
+    # one chunk: only the packed B/C copy (T * 2 * NMAX floats, 256-byte aligned)
+    assert mm.workspace_bytes(1, 64, 16, 4, chunk_len=64) == 64 * 2 * 4 * 4
+    # more chunks need more workspace, and the size is a pure function of the arguments
+    w1 = mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=16384)
+    w2 = mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=256)
+    assert w2 > w1
+    assert mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=256) == w2
+    assert mm.workspace_bytes(8, 16384, 1536, 16) == mm.workspace_bytes(8, 16384, 1536, 16,
+                                                                        chunk_len=mm.chunk_len(8, 16384, 1536, 16))
+    # the automatic chunk length gives ~2048 waves of 64 channels, never below 64 tokens
+    for (S, T, d) in ((8, 16384, 1536), (8, 16384, 4096), (256, 131072, 8192), (1, 8192, 5120), (1, 64, 16)):
+        L = mm.chunk_len(S, T, d, 16)
+        assert 1 <= L <= T
+        assert L >= min(T, 64)
+        waves = -(-T // L) * -(-d // 64)
+        assert waves <= 2048 + -(-d // 64)
