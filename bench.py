@@ -1,0 +1,396 @@
+"""Benchmark of the selective-SSM mixer core on one MI355X.
+
+One step = one prefill call over the Mamba-130m-shaped layer workload (8 packed
+sequences of 2048 tokens, d_inner 1536, N 16, bf16 io, fp32 state): conv + SiLU,
+softplus, discretisation, the segmented selective scan, readout and gate, and the
+final-state write-back.  `value` is prefill tokens/s with all inputs resident in
+HBM.  The same JSON line also carries the batch-256 decode measurement (Falcon-
+Mamba-7B-shaped: d_inner 8192, N 16, state initialised by a 512-token prefill,
+then 128 single-token steps), the per-kernel times measured with HIP events on
+the launch stream, the roofline of the dominant kernel, and the fp64 CPU oracle
+timed on this host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + decode steps/s (B=256); achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# FP32 vector peak 157.3 TFLOP/s = 256 CUs x 2.4 GHz x 128 FMA lanes/clk x 2; one issue slot = one
+# plain fp32 op (an FMA counts 2 flops), a transcendental (exp2/log2/rcp) issues at a quarter of the
+# rate and counts 4 slots.
+ALU_PEAK_TFLOPS = 157.3
+TRANS_SLOTS = 4
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles created through libamdhip64 (recorded by the library on its launch stream)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev.append(h.value)
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        self.hip.hipEventSynchronize(ctypes.c_void_p(self.ev[b]))
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(self.ev[a]), ctypes.c_void_p(self.ev[b]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(f.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def dev(a):
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    if a.dtype == np.int32:
+        return torch.from_numpy(a).cuda()
+    return torch.from_numpy(a.astype(np.float32)).cuda()
+
+
+def prefill_alg_bytes(T, S, d, N, K, s_io):
+    """Bytes the method must move for one prefill: token io, shared B/C, parameters, cu_seqlens, states in+out."""
+    return T * d * 4 * s_io + 2 * T * N * s_io + d * (N + K + 3) * 4 + (S + 1) * 4 + 2 * S * d * (N + K - 1) * 4
+
+
+def decode_alg_bytes(Bs, d, N, K, s_io):
+    return Bs * d * 4 * s_io + 2 * Bs * N * s_io + d * (N + K + 3) * 4 + 2 * Bs * d * (N + K - 1) * 4
+
+
+def alu_slots_per_token_channel(N):
+    """Issue slots of the method's fp32 arithmetic per (token, channel), transcendentals weighted x4.
+
+    conv 4 FMA; SiLU(xc) = xc / (1 + exp(-xc)): add, mul + exp, rcp; softplus = log(1 + exp(v)):
+    2 adds + exp, log; delta*u 1; per state index: delta*A, delta*u*B, the state FMA, the readout FMA
+    (4) + 1 exp; D*u 1; SiLU(z) 2 + exp, rcp; gating multiply 1.
+    """
+    plain = 4 + 2 + 2 + 1 + 4 * N + 1 + 2 + 1
+    trans = 2 + 2 + N + 2
+    return plain + TRANS_SLOTS * trans, plain, trans
+
+
+def make_prefill_set(seed, lens, d, N, io):
+    from selective_state_space_causal_amd import inputs
+
+    T = int(sum(lens))
+    tok = inputs.prefill_inputs(seed, T, d, N, io)
+    p = inputs.params(seed, d, N, 4)
+    cs, ss = inputs.zero_states(len(lens), d, N, 4)
+    cu = inputs.cu_from_lengths(lens)
+    return tok, p, cs, ss, cu
+
+
+def bench_prefill(args):
+    import torch
+
+    import selective_state_space_causal_amd as mm
+
+    S, L, d, N, K, io = 8, 2048, 1536, 16, 4, "bf16"
+    T = S * L
+    lens = [L] * S
+    names = mm.kernel_names(S, T, d, N, K)
+    nk = len(names)
+    # two resident input sets, used alternately, so the 256 MB Infinity Cache cannot hold a whole step
+    sets = []
+    for seed in (0, 1):
+        tok, p, cs, ss, cu = make_prefill_set(seed, lens, d, N, io)
+        st = dict(x=dev(tok["x"]), z=dev(tok["z"]), dt=dev(tok["dt"]), B=dev(tok["B"]), C=dev(tok["C"]),
+                  A_log=dev(p["A_log"]), D=dev(p["D"]), dt_bias=dev(p["dt_bias"]), conv_w=dev(p["conv_w"]),
+                  conv_b=dev(p["conv_b"]), cu=dev(cu), cs=dev(cs), ss=dev(ss))
+        st["y"] = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        st["ws"] = torch.empty(mm.workspace_bytes(S, T, d, N), dtype=torch.uint8, device="cuda")
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    def step(i, events=None):
+        st = sets[i % 2]
+        mm.prefill(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"], st["dt_bias"],
+                   st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], y=st["y"], workspace=st["ws"],
+                   events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = HipEvents(args.steps * (nk + 1))
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev.ev[i * (nk + 1):(i + 1) * (nk + 1)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel = {n: [] for n in names}
+    for i in range(args.steps):
+        b = i * (nk + 1)
+        for k, n in enumerate(names):
+            per_kernel[n].append(ev.ms(b + k, b + k + 1))
+    ev.close()
+    kern_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    return dict(S=S, L=L, T=T, d=d, N=N, K=K, wall_s=wall, kern_ms=kern_ms, names=names,
+                chunk_len=mm.chunk_len(S, T, d, N))
+
+
+def bench_decode(args):
+    """Batch-256 decode: a 512-token prefill initialises the states, then 128 decode steps.
+
+    Three measurements of the same 128 steps:
+      * per-kernel time with the 256 MB Infinity Cache flushed before every step (a 1 GiB
+        buffer is rewritten; the kernel is timed alone with HIP events on the launch stream):
+        this is the HBM-roofline number;
+      * the 128 steps captured in one HIP graph and replayed back to back (the serving loop
+        without host launch overhead; the fp32 state may stay cache-resident between steps);
+      * the same steps launched eagerly from Python.
+    Every measurement starts from the prefilled states.
+    """
+    import torch
+
+    import selective_state_space_causal_amd as mm
+    from selective_state_space_causal_amd import inputs
+
+    Bs, Linit, steps, d, N, K, io = 256, 512, 128, 8192, 16, 4, "bf16"
+    T = Bs * Linit
+    t0 = time.perf_counter()
+    tok, p, cs, ss, cu = make_prefill_set(0, [Linit] * Bs, d, N, io)
+    log(f"[bench] decode init inputs generated in {time.perf_counter() - t0:.1f}s")
+    prm = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    csd, ssd = dev(cs), dev(ss)
+    xin = [dev(tok[k]) for k in ("x", "z", "dt", "B", "C")]
+    del tok
+    names = mm.kernel_names(Bs, T, d, N, K)
+    ev = HipEvents(len(names) + 1)
+    mm.prefill(*xin, *prm, dev(cu), csd, ssd, events=ev.ev)
+    init_kern = {n: ev.ms(k, k + 1) for k, n in enumerate(names)}
+    init_ms = ev.ms(0, len(names))
+    ev.close()
+    del xin
+    torch.cuda.empty_cache()
+    cs0, ss0 = csd.clone(), ssd.clone()
+    t0 = time.perf_counter()
+    dins = []
+    for s in range(steps):
+        dt_ = inputs.decode_inputs(0, s, Bs, d, N, io)
+        dins.append([dev(dt_[k]) for k in ("x", "z", "dt", "B", "C")])
+    log(f"[bench] decode step inputs generated in {time.perf_counter() - t0:.1f}s")
+    y = torch.empty((Bs, d), dtype=torch.bfloat16, device="cuda")
+
+    def restore():
+        csd.copy_(cs0)
+        ssd.copy_(ss0)
+
+    # warm-up (then the states are restored)
+    for s in range(min(args.warmup, steps)):
+        mm.decode(*dins[s], *prm, csd, ssd, y=y)
+    torch.cuda.synchronize()
+
+    # (1) flushed, per kernel
+    restore()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s in range(steps):
+        flush.fill_(float(s))
+        evs[s][0].record()
+        mm.decode(*dins[s], *prm, csd, ssd, y=y)
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    del flush
+    y_flushed_last = y.clone()
+
+    # (2) HIP graph of the 128 steps, replayed back to back
+    restore()
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gstream):
+        with torch.cuda.graph(g, stream=gstream):
+            for s in range(steps):
+                mm.decode(*dins[s], *prm, csd, ssd, y=y, stream=gstream)
+    torch.cuda.current_stream().wait_stream(gstream)
+    torch.cuda.synchronize()
+    g.replay()  # warm-up replay
+    torch.cuda.synchronize()
+    restore()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1)
+    same = bool(torch.equal(y, y_flushed_last))
+
+    # (3) eager Python loop
+    restore()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        mm.decode(*dins[s], *prm, csd, ssd, y=y)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t0
+    return dict(Bs=Bs, d=d, N=N, K=K, steps=steps, kern_ms=float(np.mean(kern_ms)),
+                kern_ms_min=float(np.min(kern_ms)), graph_ms=graph_ms, eager_s=eager_s,
+                graph_matches_eager=same, init_T=T, init_ms=init_ms, init_kern=init_kern)
+
+
+def cpu_baseline(lens, d, N, io):
+    """The fp64 oracle on this host: the whole bench prefill workload (all tokens, all channels)."""
+    import oracle
+
+    oracle.build(force=False)
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = oracle.threads(min(ncpu, 64))
+    tok, p, cs, ss, cu = make_prefill_set(0, lens, d, N, io)
+    t0 = time.perf_counter()
+    oracle.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"], p["D"], p["dt_bias"],
+                   p["conv_w"], p["conv_b"], cu, cs, ss)
+    el = time.perf_counter() - t0
+    T = int(sum(lens))
+    return dict(value=T / el, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"one full prefill of the bench workload ({len(lens)} x {lens[0]} tokens, d={d}, N={N}), "
+                       f"fp64, {el:.2f} s wall on {threads} threads (input widening to fp64 included)")
+
+
+def summarize_rocprof(path):
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    print(f"{'kernel':42s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total%':>7s}")
+    for r in rows:
+        name = r["Name"].replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+        print(f"{name[:42]:42s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+              f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):7.2f}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="decode measurement only (for profiling)")
+    ap.add_argument("--summarize-rocprof", metavar="STATS_CSV",
+                    help="print a per-kernel table of a rocprofv3 --stats kernel_stats.csv and exit")
+    args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the mixer core shards by channel or sequence with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import selective_state_space_causal_amd as mm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mm.load()
+    log(f"[bench] {mm.version()} on {torch.cuda.get_device_name(0)}")
+
+    if args.no_prefill:
+        args.no_cpu_baseline = True
+        out = dict(metric=METRIC, note="decode-only diagnostic run (--no-prefill); no headline value")
+    else:
+        out = prefill_result(args)
+    if not args.no_decode:
+        out["decode"] = decode_result(args)
+    if not args.no_cpu_baseline:
+        c = out["config"]
+        out["cpu_baseline"] = cpu_baseline([c["L"]] * c["S"], c["d_inner"], c["d_state"], "bf16")
+    print(json.dumps(out), flush=True)
+
+
+def prefill_result(args):
+    pf = bench_prefill(args)
+    T, d, N, K = pf["T"], pf["d"], pf["N"], pf["K"]
+    ms_per_step = pf["wall_s"] / args.steps * 1e3
+    tokens_per_s = T * args.steps / pf["wall_s"]
+    step_bytes = prefill_alg_bytes(T, pf["S"], d, N, K, 2)
+    dom = "k_prefill_final"
+    dom_ms = pf["kern_ms"][dom]
+    slots, plain, trans = alu_slots_per_token_channel(N)
+    achieved_tflops = T * d * slots * 2 / (dom_ms * 1e-3) / 1e12
+    roofline = dict(bound="alu", achieved=round(achieved_tflops, 2), peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved_tflops / ALU_PEAK_TFLOPS, 4), traffic=None,
+                    kernel=dom, kernel_ms=round(dom_ms, 4),
+                    per_unit=f"{slots} issue slots per (token, channel) = {plain} plain fp32 ops + "
+                             f"{trans} transcendentals x {TRANS_SLOTS}; FLOP = 2 x slots")
+    out = dict(metric=METRIC, value=round(tokens_per_s, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="f32", io_dtype="bf16", data="synthetic",
+               config=dict(workload="mamba-130m-shaped layer prefill: 8 packed sequences x 2048 tokens, "
+                                    "d_inner 1536, d_state 16, conv 4, bf16 io, fp32 state",
+                           S=pf["S"], L=pf["L"], T=T, d_inner=d, d_state=N, d_conv=K,
+                           chunk_len=pf["chunk_len"]),
+               roofline=roofline,
+               kernels_ms={k: round(v, 4) for k, v in pf["kern_ms"].items()},
+               hbm_view=dict(alg_bytes_per_step=step_bytes,
+                             achieved_GBs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                             peak_GBs=HBM_PEAK_GBS,
+                             frac=round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)))
+    return out
+
+
+def decode_result(args):
+    dc = bench_decode(args)
+    db = decode_alg_bytes(dc["Bs"], dc["d"], dc["N"], dc["K"], 2)
+    gbs = db / (dc["kern_ms"] * 1e-3) / 1e9
+    ib = prefill_alg_bytes(dc["init_T"], dc["Bs"], dc["d"], dc["N"], dc["K"], 2)
+    return dict(
+        workload="falcon-mamba-7b-shaped decode: batch 256, d_inner 8192, d_state 16, conv 4, bf16 io, "
+                 "states from a 512-token prefill, 128 single-token steps",
+        steps_per_s=round(dc["steps"] / (dc["graph_ms"] * 1e-3), 1),
+        steps_per_s_note="128 steps captured in one HIP graph and replayed back to back",
+        tokens_per_s=round(dc["Bs"] * dc["steps"] / (dc["graph_ms"] * 1e-3), 1),
+        steps_per_s_eager_python=round(dc["steps"] / dc["eager_s"], 1),
+        steps_per_s_kernel_flushed=round(1e3 / dc["kern_ms"], 1),
+        roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="k_decode_vec",
+                      kernel_ms=round(dc["kern_ms"], 4), kernel_ms_min=round(dc["kern_ms_min"], 4),
+                      alg_bytes_per_launch=db,
+                      note="kernel timed alone with HIP events, Infinity Cache flushed before each step"),
+        graph_replay_matches_flushed_run=dc["graph_matches_eager"],
+        init_prefill=dict(T=dc["init_T"], ms=round(dc["init_ms"], 3),
+                          tokens_per_s=round(dc["init_T"] / (dc["init_ms"] * 1e-3), 1),
+                          kernels_ms={k: round(v, 4) for k, v in dc["init_kern"].items()},
+                          hbm_GBs=round(ib / (dc["init_ms"] * 1e-3) / 1e9, 1)))
+
+
+if __name__ == "__main__":
+    main()

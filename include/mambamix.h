@@ -129,6 +129,30 @@ size_t mamba_mixer_prefill_workspace_bytes_chunked(int32_t S, int64_t T, int32_t
 int64_t mamba_mixer_prefill_chunk_len(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
 
 /*
+ * Per-kernel timing for measurement tools.  mamba_mixer_prefill_timed is
+ * mamba_mixer_prefill_chunked that, when `events` is not NULL, also records
+ * events[i] (a hipEvent_t the caller created) on `stream` just before the i-th
+ * kernel the call enqueues and events[n] just after the last one, where
+ * n = mamba_mixer_prefill_kernel_count(...) for the same sizes and chunk_len.
+ * n_events < n + 1 with events != NULL is MM_ERR_DIM.  The events are only
+ * recorded; the caller owns, waits on and destroys them.
+ * mamba_mixer_prefill_kernel_name gives the i-th kernel's name ("" if out of
+ * range).  Host only.
+ */
+int mamba_mixer_prefill_timed(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                              const float* A_log, const float* D, const float* dt_bias,
+                              const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                              float* conv_state, float* ssm_state, void* y,
+                              int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                              int64_t chunk_len, void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* events, int32_t n_events);
+
+int32_t mamba_mixer_prefill_kernel_count(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len);
+
+const char* mamba_mixer_prefill_kernel_name(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len,
+                                            int32_t i);
+
+/*
  * mamba_mixer_decode -- one token for each of Bs independent rows; row r uses
  * state slot r.  This is the TensorRT builder's single-token step with a batch
  * dimension (same arithmetic as a prefill of Bs one-token sequences).

@@ -49,6 +49,12 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_prefill_workspace_bytes_chunked.restype = sz
     lib.mamba_mixer_prefill_chunk_len.argtypes = [i32, i64, i32, i32, i32]
     lib.mamba_mixer_prefill_chunk_len.restype = i64
+    lib.mamba_mixer_prefill_timed.argtypes = [P] * 14 + [i32, i64, i32, i32, i32, i32, i64, P, sz, P, P, i32]
+    lib.mamba_mixer_prefill_timed.restype = ctypes.c_int
+    lib.mamba_mixer_prefill_kernel_count.argtypes = [i32, i64, i32, i32, i32, i64]
+    lib.mamba_mixer_prefill_kernel_count.restype = i32
+    lib.mamba_mixer_prefill_kernel_name.argtypes = [i32, i64, i32, i32, i32, i64, i32]
+    lib.mamba_mixer_prefill_kernel_name.restype = ctypes.c_char_p
     lib.mamba_mixer_decode.argtypes = [P] * 13 + [i32, i32, i32, i32, i32, P]
     lib.mamba_mixer_decode.restype = ctypes.c_int
     lib.mamba_mixer_status_string.argtypes = [ctypes.c_int]
@@ -73,6 +79,13 @@ def workspace_bytes(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: 
 
 def chunk_len(S: int, T: int, d: int, N: int, K: int = CONV_K) -> int:
     return int(load().mamba_mixer_prefill_chunk_len(S, T, d, N, K))
+
+
+def kernel_names(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0) -> list[str]:
+    """Names of the kernels one prefill call enqueues, in order."""
+    lib = load()
+    n = lib.mamba_mixer_prefill_kernel_count(S, T, d, N, K, chunk_len)
+    return [lib.mamba_mixer_prefill_kernel_name(S, T, d, N, K, chunk_len, i).decode() for i in range(n)]
 
 
 def _io_code(t) -> int:
@@ -108,7 +121,7 @@ def _check(t, shape, dtype, name):
 
 
 def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state,
-            y=None, workspace=None, chunk_len: int = 0, stream=None):
+            y=None, workspace=None, chunk_len: int = 0, stream=None, events=None):
     """Run the mixer over packed sequences; conv_state / ssm_state are updated in place.
 
     x, z, dt [T, d] and B, C [T, N] share one io dtype (float32 or bfloat16); A_log [d, N],
@@ -140,10 +153,15 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = load().mamba_mixer_prefill_chunked(
+    if events is None:
+        ev, nev = None, 0
+    else:  # raw hipEvent_t handles, recorded around each kernel of the call
+        ev = (ctypes.c_void_p * len(events))(*events)
+        nev = len(events)
+    rc = load().mamba_mixer_prefill_timed(
         _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(conv_w),
         _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(ssm_state), _ptr(y),
-        S, T, d, N, CONV_K, _io_code(x), int(chunk_len), wptr, wbytes, _stream(stream))
+        S, T, d, N, CONV_K, _io_code(x), int(chunk_len), wptr, wbytes, _stream(stream), ev, nev)
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_prefill")
     return y

@@ -140,49 +140,60 @@ __device__ __forceinline__ float mixer_token(const Chan<NMAX>& ch, float xv, flo
   return 0.0f;
 }
 
-// Scan tokens [g, g_end) of one sequence for channel c.  Loads are issued one
-// group of U tokens ahead of the arithmetic.
+// Scan tokens [g, g_end) of one sequence for channel c.  Full groups of U tokens
+// run as straight-line code (no per-token branch), so the scheduler can overlap
+// the independent per-token work (conv, softplus, decays) of the whole group
+// around the serial state updates; the next group's loads are issued before the
+// current group's arithmetic (their indices are clamped into the range, so the
+// last group's prefetch re-reads valid data instead of branching).  The < U
+// leftover tokens run one at a time.
 template <typename IO, int NMAX, bool READOUT>
 __device__ __forceinline__ void scan_range(const Chan<NMAX>& ch, int64_t g, int64_t g_end, int c, int d,
                                            const IO* __restrict__ x, const IO* __restrict__ z,
                                            const IO* __restrict__ dt, const float* __restrict__ bc,
                                            IO* __restrict__ y, float (&win)[kKS], float (&h)[NMAX], float& dsum) {
   constexpr int U = 8;
-  float xb[U], zb[U], db[U];
-#pragma unroll
-  for (int i = 0; i < U; ++i) {
-    const int64_t gi = g + i;
-    const bool ok = gi < g_end;
-    const int64_t off = gi * d + c;
-    xb[i] = ok ? ld_io(x, off) : 0.0f;
-    zb[i] = (ok && READOUT) ? ld_io(z, off) : 0.0f;
-    db[i] = ok ? ld_io(dt, off) : 0.0f;
-  }
-  for (; g < g_end; g += U) {
-    float xn[U], zn[U], dn[U];
+  const int64_t last = g_end - 1;
+  int64_t nfull = (g_end - g) / U;
+  if (nfull > 0) {
+    float xb[U], zb[U], db[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const int64_t gi = g + U + i;
-      const bool ok = gi < g_end;
-      const int64_t off = gi * d + c;
-      xn[i] = ok ? ld_io(x, off) : 0.0f;
-      zn[i] = (ok && READOUT) ? ld_io(z, off) : 0.0f;
-      dn[i] = ok ? ld_io(dt, off) : 0.0f;
+      const int64_t off = (g + i) * d + c;
+      xb[i] = ld_io(x, off);
+      if (READOUT) zb[i] = ld_io(z, off);
+      db[i] = ld_io(dt, off);
     }
+    for (; nfull > 0; --nfull, g += U) {
+      float xn[U], zn[U], dn[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int64_t gi = g + i;
-      if (gi < g_end) {
-        const float out = mixer_token<NMAX, READOUT>(ch, xb[i], zb[i], db[i], bc + gi * (2 * NMAX), win, h, dsum);
+      for (int i = 0; i < U; ++i) {
+        const int64_t gi = g + U + i;
+        const int64_t off = (gi < last ? gi : last) * d + c;
+        xn[i] = ld_io(x, off);
+        if (READOUT) zn[i] = ld_io(z, off);
+        dn[i] = ld_io(dt, off);
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int64_t gi = g + i;
+        const float out = mixer_token<NMAX, READOUT>(ch, xb[i], READOUT ? zb[i] : 0.0f, db[i],
+                                                     bc + gi * (2 * NMAX), win, h, dsum);
         if (READOUT) st_io(y, gi * d + c, out);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      xb[i] = xn[i];
-      zb[i] = zn[i];
-      db[i] = dn[i];
+      for (int i = 0; i < U; ++i) {
+        xb[i] = xn[i];
+        if (READOUT) zb[i] = zn[i];
+        db[i] = dn[i];
+      }
     }
+  }
+  for (; g < g_end; ++g) {
+    const int64_t off = g * d + c;
+    const float out = mixer_token<NMAX, READOUT>(ch, ld_io(x, off), READOUT ? ld_io(z, off) : 0.0f, ld_io(dt, off),
+                                                 bc + g * (2 * NMAX), win, h, dsum);
+    if (READOUT) st_io(y, off, out);
   }
 }
 
@@ -203,13 +214,15 @@ __global__ void __launch_bounds__(kBlock) k_pack_bc(const IO* __restrict__ B, co
 }
 
 struct ChunkWs {
-  float* a;        // [P][d][NMAX]  decay product of the chunk's last segment (0 after a sequence start)
+  float* a;        // [P][d]        sum of delta over the chunk's last segment, or -1 when that segment
+                   //               starts a sequence (its decay product is then 0: the segmented reset)
   float* b;        // [P][d][NMAX]  state at the chunk end from a zero (or slot) state
   float* hin;      // [P][d][NMAX]  carry-in state of chunks whose first token continues a sequence
   float* halo;     // [P][d][3]     raw inputs before the chunk start (same sequence / its conv state)
   float* stash_h;  // [P][d][NMAX]  initial ssm state of the sequence starting in the chunk and ending later
   float* stash_c;  // [P][d][3]     its initial conv state
-  int32_t* cont;   // [P]           1 if the chunk's first token continues a sequence
+  int32_t* flags;  // [P]           bit 0: the chunk's first token continues a sequence;
+                   //               bit 1: (a, b) of the chunk is needed (the next chunk continues)
 };
 
 // Pass 1: per chunk j and channel, (i) the halo of raw inputs before the chunk
@@ -230,7 +243,9 @@ __global__ void __launch_bounds__(kBlock) k_tail_aggregate(
   const int64_t g1 = (g0 + Lc < T) ? g0 + Lc : T;
   const int s0 = seq_of(cu, S, g0);
   const int64_t st0 = cu[s0];
-  if (c == 0) ws.cont[j] = (g0 > st0) ? 1 : 0;
+  // the next chunk continues a sequence of this one: then its carry-in needs (a, b) of this chunk
+  const bool next_cont = g1 < T && g1 > static_cast<int64_t>(cu[seq_of(cu, S, g1)]);
+  if (c == 0) ws.flags[j] = ((g0 > st0) ? 1 : 0) | (next_cont ? 2 : 0);
   if (c >= d) return;
   const int64_t pc = static_cast<int64_t>(j) * d + c;
 
@@ -244,77 +259,72 @@ __global__ void __launch_bounds__(kBlock) k_tail_aggregate(
       ws.halo[pc * kKS + k] = halo[k];
     }
   }
+  if (!next_cont) return;
 
+  const int s1 = seq_of(cu, S, g1);
+  const int64_t st1 = cu[s1];
+  const bool has_start = st1 >= g0;
   float h[NMAX];
+  float win[kKS];
+  if (has_start) {
+    const int64_t sc = static_cast<int64_t>(s1) * d + c;
 #pragma unroll
-  for (int n = 0; n < NMAX; ++n) h[n] = 0.0f;
-  float a_out[NMAX];
-#pragma unroll
-  for (int n = 0; n < NMAX; ++n) a_out[n] = 0.0f;
-
-  if (g1 < T) {
-    const int s1 = seq_of(cu, S, g1);
-    const int64_t st1 = cu[s1];
-    if (g1 > st1) {  // the next chunk continues sequence s1
-      const bool has_start = st1 >= g0;
-      float win[kKS];
-      if (has_start) {
-        const int64_t sc = static_cast<int64_t>(s1) * d + c;
-#pragma unroll
-        for (int k = 0; k < kKS; ++k) {
-          win[k] = conv_state[sc * kKS + k];
-          ws.stash_c[pc * kKS + k] = win[k];
-        }
-#pragma unroll
-        for (int n = 0; n < NMAX; ++n) {
-          h[n] = (n < N) ? ssm_state[sc * N + n] : 0.0f;
-          ws.stash_h[pc * NMAX + n] = h[n];
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < kKS; ++k) win[k] = halo[k];
-      }
-      Chan<NMAX> ch;
-      load_chan(ch, c, N, A_log, D, dt_bias, conv_w, conv_b);
-      float dsum = 0.0f;
-      scan_range<IO, NMAX, false>(ch, has_start ? st1 : g0, g1, c, d, x, x, dt, bc, nullptr, win, h, dsum);
-      if (!has_start) {
-#pragma unroll
-        for (int n = 0; n < NMAX; ++n) a_out[n] = exp2_hw(ch.A2[n] * dsum);
-      }
+    for (int k = 0; k < kKS; ++k) {
+      win[k] = conv_state[sc * kKS + k];
+      ws.stash_c[pc * kKS + k] = win[k];
     }
-  }
 #pragma unroll
-  for (int n = 0; n < NMAX; ++n) {
-    ws.a[pc * NMAX + n] = a_out[n];
-    ws.b[pc * NMAX + n] = h[n];
+    for (int n = 0; n < NMAX; ++n) {
+      h[n] = (n < N) ? ssm_state[sc * N + n] : 0.0f;
+      ws.stash_h[pc * NMAX + n] = h[n];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) win[k] = halo[k];
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) h[n] = 0.0f;
   }
+  Chan<NMAX> ch;
+  load_chan(ch, c, N, A_log, D, dt_bias, conv_w, conv_b);
+  float dsum = 0.0f;
+  scan_range<IO, NMAX, false>(ch, has_start ? st1 : g0, g1, c, d, x, x, dt, bc, nullptr, win, h, dsum);
+  ws.a[pc] = has_start ? -1.0f : dsum;
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n) ws.b[pc * NMAX + n] = h[n];
 }
 
-// Pass 2: fold the chunk pairs in order; carry-in of chunk j is the state at the
-// end of chunk j-1.  One thread per (channel, state index).
+// Pass 2: fold the chunk pairs in order; the carry-in of chunk j is the state at
+// the end of chunk j-1.  One thread per (channel, state index).  The per-chunk flags
+// are read U at a time (uniform scalar loads), the pair loads are unconditional
+// (entries of chunks whose pair is not needed hold stale data and are masked out),
+// so the loop has no memory round trip on its critical path.
 template <int NMAX>
-__global__ void __launch_bounds__(kBlock) k_carry(ChunkWs ws, int d, int P) {
+__global__ void __launch_bounds__(kBlock) k_carry(ChunkWs ws, const float* __restrict__ A_log, int d, int N,
+                                                  int P) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (q >= static_cast<int64_t>(d) * NMAX) return;
+  const int c = static_cast<int>(q / NMAX);
+  const int n = static_cast<int>(q % NMAX);
+  const float A2 = (n < N) ? -exp2_hw(A_log[static_cast<int64_t>(c) * N + n] * kLog2e) * kLog2e : 0.0f;
   const int64_t stride = static_cast<int64_t>(d) * NMAX;
   float cur = 0.0f;
-  constexpr int U = 16;
+  constexpr int U = 32;
   for (int j0 = 0; j0 < P; j0 += U) {
-    float av[U], bv[U];
+    int fl[U];
+    float sv[U], bv[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const bool ok = j0 + i < P;
-      av[i] = ok ? ws.a[(j0 + i) * stride + q] : 0.0f;
-      bv[i] = ok ? ws.b[(j0 + i) * stride + q] : 0.0f;
+      const int j = (j0 + i < P) ? j0 + i : P - 1;
+      fl[i] = (j0 + i < P) ? ws.flags[j] : 0;
+      sv[i] = ws.a[static_cast<int64_t>(j) * d + c];
+      bv[i] = ws.b[j * stride + q];
     }
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const int j = j0 + i;
-      if (j < P) {
-        if (ws.cont[j]) ws.hin[j * stride + q] = cur;
-        cur = __builtin_fmaf(av[i], cur, bv[i]);
-      }
+      if (fl[i] & 1) ws.hin[(j0 + i) * stride + q] = cur;
+      const bool need = (fl[i] & 2) != 0;
+      const float a = (need && sv[i] >= 0.0f) ? exp2_hw(A2 * sv[i]) : 0.0f;
+      cur = need ? __builtin_fmaf(a, cur, bv[i]) : 0.0f;
     }
   }
 }
@@ -420,16 +430,82 @@ __global__ void __launch_bounds__(kBlock) k_decode(
     if (n < N) ssm_state[rc * N + n] = h[n];
 }
 
+// Decode, streaming layout: G = NMAX/4 lanes per channel, each lane owning four
+// consecutive state entries as one float4, so that every load/store instruction of
+// a wave moves one contiguous 1 KiB run of ssm_state.  The per-channel work (conv,
+// SiLU, softplus, gate) is repeated by the G lanes of a channel (the kernel is bound
+// by HBM with ALU to spare) and the readout is summed across them with lane
+// exchanges.  Requires N == NMAX and 16-byte aligned ssm_state, A_log and conv_w.
+template <typename IO, int NMAX>
+__global__ void __launch_bounds__(kBlock) k_decode_vec(
+    const IO* __restrict__ x, const IO* __restrict__ z, const IO* __restrict__ dt, const IO* __restrict__ B,
+    const IO* __restrict__ C, const float* __restrict__ A_log, const float* __restrict__ D,
+    const float* __restrict__ dt_bias, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+    float* __restrict__ conv_state, float* __restrict__ ssm_state, IO* __restrict__ y, int d) {
+  constexpr int G = NMAX / 4;      // lanes per channel
+  constexpr int CPB = kBlock / G;  // channels per block
+  const int nb = (d + CPB - 1) / CPB;
+  const int r = static_cast<int>(blockIdx.x / nb);
+  const int q = static_cast<int>(threadIdx.x) % G;
+  const int c = static_cast<int>(blockIdx.x % nb) * CPB + static_cast<int>(threadIdx.x) / G;
+  if (c >= d) return;
+  const int64_t rc = static_cast<int64_t>(r) * d + c;
+  float4* srow = reinterpret_cast<float4*>(ssm_state + rc * NMAX);
+  const float4 hv = srow[q];
+  float h[4] = {hv.x, hv.y, hv.z, hv.w};
+  float win[kKS];
+#pragma unroll
+  for (int k = 0; k < kKS; ++k) win[k] = conv_state[rc * kKS + k];
+  const float xv = ld_io(x, rc), zv = ld_io(z, rc), dtv = ld_io(dt, rc);
+  float bq[4], cq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bq[i] = ld_io(B, static_cast<int64_t>(r) * NMAX + 4 * q + i);
+    cq[i] = ld_io(C, static_cast<int64_t>(r) * NMAX + 4 * q + i);
+  }
+  const float4 w = reinterpret_cast<const float4*>(conv_w)[c];
+  float xc = conv_b[c];
+  xc = __builtin_fmaf(w.x, win[0], xc);
+  xc = __builtin_fmaf(w.y, win[1], xc);
+  xc = __builtin_fmaf(w.z, win[2], xc);
+  xc = __builtin_fmaf(w.w, xv, xc);
+  const float u = silu(xc);
+  const float delta = softplus(dtv + dt_bias[c]);
+  const float du = delta * u;
+  const float4 al = reinterpret_cast<const float4*>(A_log + static_cast<int64_t>(c) * NMAX)[q];
+  const float alv[4] = {al.x, al.y, al.z, al.w};
+  float yp = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float A2 = -exp2_hw(alv[i] * kLog2e) * kLog2e;
+    const float a = exp2_hw(delta * A2);
+    h[i] = __builtin_fmaf(a, h[i], du * bq[i]);
+    yp = __builtin_fmaf(h[i], cq[i], yp);
+  }
+  if (G >= 2) yp += __shfl_xor(yp, 1);
+  if (G >= 4) yp += __shfl_xor(yp, 2);
+  srow[q] = make_float4(h[0], h[1], h[2], h[3]);
+  if (q == 0) st_io(y, rc, (yp + D[c] * u) * silu(zv));
+  // new conv state = [win1, win2, x]; entry k is written by lane k % G
+  const float nw[kKS] = {win[1], win[2], xv};
+#pragma unroll
+  for (int k = 0; k < kKS; ++k)
+    if (k % G == q) conv_state[rc * kKS + k] = nw[k];
+}
+
 // ---------------------------------------------------------------- host side
 
 struct Plan {
   int nmax;
   int64_t Lc, P;
-  size_t off_bc, off_a, off_b, off_hin, off_halo, off_stash_h, off_stash_c, off_cont, total;
+  size_t off_bc, off_a, off_b, off_hin, off_halo, off_stash_h, off_stash_c, off_flags, total;
 };
 
-constexpr int64_t kTargetWaves = 2048;  // two waves per SIMD on a 256-CU part
-constexpr int64_t kMinChunk = 64;
+// Enough chunks for ~32 waves per CU (short waves balance well), but never below
+// 128 tokens: below that the chunk-aggregate recompute and the carry fold cost more
+// than the extra parallelism returns.
+constexpr int64_t kTargetWaves = 32768;
+constexpr int64_t kMinChunk = 128;
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -439,7 +515,7 @@ int64_t auto_chunk(int64_t T, int d) {
   const int64_t nblk = (d + kWave - 1) / kWave;
   int64_t Lc = (T * nblk + kTargetWaves - 1) / kTargetWaves;
   if (Lc < kMinChunk) Lc = kMinChunk;
-  Lc = (Lc + 15) / 16 * 16;
+  Lc = (Lc + 63) / 64 * 64;
   if (Lc > T) Lc = T;
   return Lc;
 }
@@ -457,17 +533,19 @@ Plan make_plan(int64_t T, int d, int N, int64_t chunk_len) {
   if (p.P > 1) {
     const size_t pdn = static_cast<size_t>(p.P) * d * p.nmax * sizeof(float);
     const size_t pd3 = static_cast<size_t>(p.P) * d * kKS * sizeof(float);
-    p.off_a = off; off += align256(pdn);
+    p.off_a = off; off += align256(static_cast<size_t>(p.P) * d * sizeof(float));
     p.off_b = off; off += align256(pdn);
     p.off_hin = off; off += align256(pdn);
     p.off_stash_h = off; off += align256(pdn);
     p.off_halo = off; off += align256(pd3);
     p.off_stash_c = off; off += align256(pd3);
-    p.off_cont = off; off += align256(static_cast<size_t>(p.P) * sizeof(int32_t));
+    p.off_flags = off; off += align256(static_cast<size_t>(p.P) * sizeof(int32_t));
   }
   p.total = off;
   return p;
 }
+
+int prefill_kernel_count(const Plan& p) { return p.P > 1 ? 4 : 2; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -476,16 +554,29 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na > 0 && nb > 0 && a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Records events[k] (if given) on the stream before the k-th kernel and events[n]
+// after the last one.
+struct StageEvents {
+  void* const* ev;
+  int n;
+  int k;
+  void mark(hipStream_t st) {
+    if (ev != nullptr && k < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), st);
+    ++k;
+  }
+};
+
 template <typename IO, int NMAX>
 int launch_prefill(const Plan& p, const void* x, const void* z, const void* dt, const void* B, const void* C,
                    const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
                    const float* conv_b, const int32_t* cu, float* conv_state, float* ssm_state, void* y, int S,
-                   int64_t T, int d, int N, char* ws, hipStream_t st) {
+                   int64_t T, int d, int N, char* ws, hipStream_t st, StageEvents evs) {
   const IO* xi = static_cast<const IO*>(x);
   const IO* zi = static_cast<const IO*>(z);
   const IO* di = static_cast<const IO*>(dt);
   float* bc = reinterpret_cast<float*>(ws + p.off_bc);
   const int64_t nbc = T * 2 * NMAX;
+  evs.mark(st);
   hipLaunchKernelGGL((k_pack_bc<IO, NMAX>), dim3(static_cast<unsigned>((nbc + kBlock - 1) / kBlock)), dim3(kBlock),
                      0, st, static_cast<const IO*>(B), static_cast<const IO*>(C), bc, T, N);
   ChunkWs cw{};
@@ -496,18 +587,22 @@ int launch_prefill(const Plan& p, const void* x, const void* z, const void* dt, 
     cw.halo = reinterpret_cast<float*>(ws + p.off_halo);
     cw.stash_h = reinterpret_cast<float*>(ws + p.off_stash_h);
     cw.stash_c = reinterpret_cast<float*>(ws + p.off_stash_c);
-    cw.cont = reinterpret_cast<int32_t*>(ws + p.off_cont);
+    cw.flags = reinterpret_cast<int32_t*>(ws + p.off_flags);
   }
   const dim3 grid(static_cast<unsigned>(((d + kBlock - 1) / kBlock) * p.P));
   if (p.P > 1) {
+    evs.mark(st);
     hipLaunchKernelGGL((k_tail_aggregate<IO, NMAX>), grid, dim3(kBlock), 0, st, xi, di, bc, A_log, D, dt_bias,
                        conv_w, conv_b, cu, conv_state, ssm_state, cw, S, T, d, N, p.Lc);
     const int64_t q = static_cast<int64_t>(d) * NMAX;
+    evs.mark(st);
     hipLaunchKernelGGL((k_carry<NMAX>), dim3(static_cast<unsigned>((q + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                       st, cw, d, static_cast<int>(p.P));
+                       st, cw, A_log, d, N, static_cast<int>(p.P));
   }
+  evs.mark(st);
   hipLaunchKernelGGL((k_prefill_final<IO, NMAX>), grid, dim3(kBlock), 0, st, xi, zi, di, bc, A_log, D, dt_bias,
                      conv_w, conv_b, cu, conv_state, ssm_state, static_cast<IO*>(y), cw, S, T, d, N, p.Lc);
+  evs.mark(st);
   return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }
 
@@ -515,11 +610,21 @@ template <typename IO, int NMAX>
 int launch_decode(const void* x, const void* z, const void* dt, const void* B, const void* C, const float* A_log,
                   const float* D, const float* dt_bias, const float* conv_w, const float* conv_b,
                   float* conv_state, float* ssm_state, void* y, int Bs, int d, int N, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>((d + kBlock - 1) / kBlock) * Bs));
-  hipLaunchKernelGGL((k_decode<IO, NMAX>), grid, dim3(kBlock), 0, st, static_cast<const IO*>(x),
-                     static_cast<const IO*>(z), static_cast<const IO*>(dt), static_cast<const IO*>(B),
-                     static_cast<const IO*>(C), A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
-                     static_cast<IO*>(y), d, N);
+  const bool vec = N == NMAX && aligned(ssm_state, 16) && aligned(A_log, 16) && aligned(conv_w, 16);
+  if (vec) {
+    constexpr int CPB = kBlock / (NMAX / 4);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>((d + CPB - 1) / CPB) * Bs));
+    hipLaunchKernelGGL((k_decode_vec<IO, NMAX>), grid, dim3(kBlock), 0, st, static_cast<const IO*>(x),
+                       static_cast<const IO*>(z), static_cast<const IO*>(dt), static_cast<const IO*>(B),
+                       static_cast<const IO*>(C), A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
+                       static_cast<IO*>(y), d);
+  } else {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>((d + kBlock - 1) / kBlock) * Bs));
+    hipLaunchKernelGGL((k_decode<IO, NMAX>), grid, dim3(kBlock), 0, st, static_cast<const IO*>(x),
+                       static_cast<const IO*>(z), static_cast<const IO*>(dt), static_cast<const IO*>(B),
+                       static_cast<const IO*>(C), A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
+                       static_cast<IO*>(y), d, N);
+  }
   return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }
 
@@ -567,12 +672,13 @@ size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int3
   return mamba_mixer_prefill_workspace_bytes_chunked(S, T, d, N, K, 0);
 }
 
-int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, const void* B, const void* C,
-                                const float* A_log, const float* D, const float* dt_bias,
-                                const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
-                                float* conv_state, float* ssm_state, void* y,
-                                int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
-                                int64_t chunk_len, void* workspace, size_t workspace_bytes, void* stream) {
+int mamba_mixer_prefill_timed(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                              const float* A_log, const float* D, const float* dt_bias,
+                              const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                              float* conv_state, float* ssm_state, void* y,
+                              int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                              int64_t chunk_len, void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* events, int32_t n_events) {
   int rc = check_common(T, d, N, K, io_dtype);
   if (rc != MM_OK) return rc;
   if (S < 0 || T > INT32_MAX) return MM_ERR_DIM;
@@ -597,11 +703,13 @@ int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, co
   const Plan p = make_plan(T, d, N, chunk_len);
   if (p.total > 0 && (workspace == nullptr || workspace_bytes < p.total)) return MM_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MM_ERR_ALIGN;
+  if (events != nullptr && n_events < prefill_kernel_count(p) + 1) return MM_ERR_DIM;
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const StageEvents evs{events, n_events, 0};
 #define MM_PREFILL(IO, NM)                                                                                      \
   launch_prefill<IO, NM>(p, x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, \
-                         y, S, T, d, N, ws, st)
+                         y, S, T, d, N, ws, st, evs)
   if (io_dtype == MM_IO_BF16) {
     if (p.nmax == 4) return MM_PREFILL(uint16_t, 4);
     if (p.nmax == 8) return MM_PREFILL(uint16_t, 8);
@@ -611,6 +719,31 @@ int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, co
   if (p.nmax == 8) return MM_PREFILL(float, 8);
   return MM_PREFILL(float, 16);
 #undef MM_PREFILL
+}
+
+int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                const float* A_log, const float* D, const float* dt_bias,
+                                const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                                float* conv_state, float* ssm_state, void* y,
+                                int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                                int64_t chunk_len, void* workspace, size_t workspace_bytes, void* stream) {
+  return mamba_mixer_prefill_timed(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state,
+                                   ssm_state, y, S, T, d, N, K, io_dtype, chunk_len, workspace, workspace_bytes,
+                                   stream, nullptr, 0);
+}
+
+int32_t mamba_mixer_prefill_kernel_count(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len) {
+  if (check_common(T, d, N, K, MM_IO_F32) != MM_OK || S <= 0 || T == 0 || d == 0) return 0;
+  return prefill_kernel_count(make_plan(T, d, N, chunk_len));
+}
+
+const char* mamba_mixer_prefill_kernel_name(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len,
+                                            int32_t i) {
+  const int32_t n = mamba_mixer_prefill_kernel_count(S, T, d, N, K, chunk_len);
+  if (i < 0 || i >= n) return "";
+  static const char* const multi[] = {"k_pack_bc", "k_tail_aggregate", "k_carry", "k_prefill_final"};
+  static const char* const single[] = {"k_pack_bc", "k_prefill_final"};
+  return n == 4 ? multi[i] : single[i];
 }
 
 int mamba_mixer_prefill(const void* x, const void* z, const void* dt, const void* B, const void* C,

@@ -139,10 +139,12 @@ def test_workspace_query_and_chunk_plan(lib):
     assert mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=256) == w2
     assert mm.workspace_bytes(8, 16384, 1536, 16) == mm.workspace_bytes(8, 16384, 1536, 16,
                                                                         chunk_len=mm.chunk_len(8, 16384, 1536, 16))
-    # the automatic chunk length gives ~2048 waves of 64 channels, never below 64 tokens
+    # the automatic chunk length targets ~32768 waves of 64 channels, never below 128 tokens
     for (S, T, d) in ((8, 16384, 1536), (8, 16384, 4096), (256, 131072, 8192), (1, 8192, 5120), (1, 64, 16)):
         L = mm.chunk_len(S, T, d, 16)
         assert 1 <= L <= T
-        assert L >= min(T, 64)
+        assert L >= min(T, 128)
         waves = -(-T // L) * -(-d // 64)
-        assert waves <= 2048 + -(-d // 64)
+        assert waves <= 32768 + -(-d // 64)
+    assert mm.chunk_len(256, 131072, 8192, 16) == 512
+    assert mm.chunk_len(8, 16384, 1536, 16) == 128
