@@ -70,6 +70,30 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_causal_amd", "csrc", "mambamix.hip")
+PROFILE_PREFILL = os.path.join(ROOT, "profiles", "k_prefill_final__m130_prefill_8x2048_d1536_N16_bf16.txt")
+PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d8192_N16_bf16.txt")
+
+
+def counted_traffic(profile_path):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None when the summary is
+    missing or was taken on a different kernel source than the one built now."""
+    import hashlib
+
+    try:
+        text = open(profile_path).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    sha = traffic = None
+    for line in text.splitlines():
+        if line.startswith("kernel source sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        if line.startswith("traffic_bytes_per_launch:"):
+            traffic = int(float(line.split(":", 1)[1]))
+    return traffic if sha == src else None
+
+
 def dev(a):
     import torch
 
@@ -284,13 +308,39 @@ def cpu_baseline(lens, d, N, io):
                        f"fp64, {el:.2f} s wall on {threads} threads (input widening to fp64 included)")
 
 
+def copy_calibration():
+    """A plain copy of a known size: 1 GiB read + 1 GiB written per launch (torch's copy kernel)."""
+    import torch
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_calibration=True, bytes_read_per_launch=1 << 30, bytes_written_per_launch=1 << 30,
+                          launches=3)), flush=True)
+
+
+def _short_kernel_name(name):
+    return name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+
+
 def summarize_rocprof(path):
     import csv
 
     rows = list(csv.DictReader(open(path)))
+    if rows and "Counter_Name" in rows[0]:
+        agg = {}
+        for r in rows:
+            key = (_short_kernel_name(r["Kernel_Name"]), r["Counter_Name"])
+            agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        print(f"{'kernel':46s} {'counter':12s} {'dispatches':>10s} {'avg_per_dispatch':>18s} {'min':>14s} {'max':>14s}")
+        for (k, c), v in sorted(agg.items()):
+            print(f"{k[:46]:46s} {c:12s} {len(v):10d} {np.mean(v):18.1f} {np.min(v):14.1f} {np.max(v):14.1f}")
+        return
     print(f"{'kernel':42s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total%':>7s}")
     for r in rows:
-        name = r["Name"].replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+        name = _short_kernel_name(r["Name"])
         print(f"{name[:42]:42s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
               f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):7.2f}")
 
@@ -303,11 +353,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode measurement only (for profiling)")
-    ap.add_argument("--summarize-rocprof", metavar="STATS_CSV",
-                    help="print a per-kernel table of a rocprofv3 --stats kernel_stats.csv and exit")
+    ap.add_argument("--summarize-rocprof", metavar="CSV",
+                    help="print a per-kernel table of a rocprofv3 kernel_stats.csv or counter_collection.csv "
+                         "and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy three times (to scale HBM byte counters)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.copy_calibration:
+        copy_calibration()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -347,7 +403,7 @@ def prefill_result(args):
     slots, plain, trans = alu_slots_per_token_channel(N)
     achieved_tflops = T * d * slots * 2 / (dom_ms * 1e-3) / 1e12
     roofline = dict(bound="alu", achieved=round(achieved_tflops, 2), peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved_tflops / ALU_PEAK_TFLOPS, 4), traffic=None,
+                    frac=round(achieved_tflops / ALU_PEAK_TFLOPS, 4), traffic=counted_traffic(PROFILE_PREFILL),
                     kernel=dom, kernel_ms=round(dom_ms, 4),
                     per_unit=f"{slots} issue slots per (token, channel) = {plain} plain fp32 ops + "
                              f"{trans} transcendentals x {TRANS_SLOTS}; FLOP = 2 x slots")
@@ -381,7 +437,8 @@ def decode_result(args):
         steps_per_s_eager_python=round(dc["steps"] / dc["eager_s"], 1),
         steps_per_s_kernel_flushed=round(1e3 / dc["kern_ms"], 1),
         roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="k_decode_vec",
+                      frac=round(gbs / HBM_PEAK_GBS, 4), traffic=counted_traffic(PROFILE_DECODE),
+                      kernel="k_decode_vec",
                       kernel_ms=round(dc["kern_ms"], 4), kernel_ms_min=round(dc["kern_ms_min"], 4),
                       alg_bytes_per_launch=db,
                       note="kernel timed alone with HIP events, Infinity Cache flushed before each step"),

@@ -431,11 +431,31 @@ __global__ void __launch_bounds__(kBlock) k_decode(
 }
 
 // Decode, streaming layout: G = NMAX/4 lanes per channel, each lane owning four
-// consecutive state entries as one float4, so that every load/store instruction of
-// a wave moves one contiguous 1 KiB run of ssm_state.  The per-channel work (conv,
-// SiLU, softplus, gate) is repeated by the G lanes of a channel (the kernel is bound
-// by HBM with ALU to spare) and the readout is summed across them with lane
-// exchanges.  Requires N == NMAX and 16-byte aligned ssm_state, A_log and conv_w.
+// consecutive state entries, so every state load/store instruction of a wave moves
+// one contiguous 1 KiB run.  The fp32 state is touched exactly once in each
+// direction, with nontemporal loads/stores (it is not reused by this kernel and
+// should not displace other data from the caches).  The three conv-state values of
+// a channel are loaded by three different lanes of its group (one dword each, one
+// contiguous run per wave) and shared within the group by lane shuffles.  The
+// per-channel work (conv, SiLU, softplus, gate) is repeated by the G lanes of a
+// channel (the kernel is bound by HBM with ALU to spare) and the readout is summed
+// across them with lane exchanges.  Requires N == NMAX, 16-byte aligned ssm_state,
+// A_log and conv_w, and B/C rows aligned for 4-element vector loads.
+template <typename T>
+__device__ __forceinline__ T nt_load(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void nt_store(T v, T* p) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ void ld4_io(const float* p, float (&o)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void ld4_io(const uint16_t* p, float (&o)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+
 template <typename IO, int NMAX>
 __global__ void __launch_bounds__(kBlock) k_decode_vec(
     const IO* __restrict__ x, const IO* __restrict__ z, const IO* __restrict__ dt, const IO* __restrict__ B,
@@ -444,25 +464,35 @@ __global__ void __launch_bounds__(kBlock) k_decode_vec(
     float* __restrict__ conv_state, float* __restrict__ ssm_state, IO* __restrict__ y, int d) {
   constexpr int G = NMAX / 4;      // lanes per channel
   constexpr int CPB = kBlock / G;  // channels per block
+  constexpr int KPL = (kKS + G - 1) / G;  // conv-state entries loaded per lane
   const int nb = (d + CPB - 1) / CPB;
   const int r = static_cast<int>(blockIdx.x / nb);
   const int q = static_cast<int>(threadIdx.x) % G;
   const int c = static_cast<int>(blockIdx.x % nb) * CPB + static_cast<int>(threadIdx.x) / G;
   if (c >= d) return;
   const int64_t rc = static_cast<int64_t>(r) * d + c;
-  float4* srow = reinterpret_cast<float4*>(ssm_state + rc * NMAX);
-  const float4 hv = srow[q];
-  float h[4] = {hv.x, hv.y, hv.z, hv.w};
-  float win[kKS];
+  float* srow = ssm_state + rc * NMAX + 4 * q;
+  float h[4] = {nt_load(srow), nt_load(srow + 1), nt_load(srow + 2), nt_load(srow + 3)};
+  // conv state entry k is loaded by lane k % G of the channel's group
+  float cv[KPL];
 #pragma unroll
-  for (int k = 0; k < kKS; ++k) win[k] = conv_state[rc * kKS + k];
+  for (int m = 0; m < KPL; ++m) {
+    const int k = m * G + q;
+    cv[m] = (k < kKS) ? nt_load(conv_state + rc * kKS + k) : 0.0f;
+  }
+  float win[kKS];
+  if constexpr (G == 1) {
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) win[k] = cv[k];
+  } else {
+    const int base = (static_cast<int>(threadIdx.x) & (kWave - 1)) - q;
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) win[k] = __shfl(cv[k / G], base + k % G, kWave);
+  }
   const float xv = ld_io(x, rc), zv = ld_io(z, rc), dtv = ld_io(dt, rc);
   float bq[4], cq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bq[i] = ld_io(B, static_cast<int64_t>(r) * NMAX + 4 * q + i);
-    cq[i] = ld_io(C, static_cast<int64_t>(r) * NMAX + 4 * q + i);
-  }
+  ld4_io(B + static_cast<int64_t>(r) * NMAX + 4 * q, bq);
+  ld4_io(C + static_cast<int64_t>(r) * NMAX + 4 * q, cq);
   const float4 w = reinterpret_cast<const float4*>(conv_w)[c];
   float xc = conv_b[c];
   xc = __builtin_fmaf(w.x, win[0], xc);
@@ -484,13 +514,16 @@ __global__ void __launch_bounds__(kBlock) k_decode_vec(
   }
   if (G >= 2) yp += __shfl_xor(yp, 1);
   if (G >= 4) yp += __shfl_xor(yp, 2);
-  srow[q] = make_float4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nt_store(h[i], srow + i);
   if (q == 0) st_io(y, rc, (yp + D[c] * u) * silu(zv));
   // new conv state = [win1, win2, x]; entry k is written by lane k % G
   const float nw[kKS] = {win[1], win[2], xv};
 #pragma unroll
-  for (int k = 0; k < kKS; ++k)
-    if (k % G == q) conv_state[rc * kKS + k] = nw[k];
+  for (int m = 0; m < KPL; ++m) {
+    const int k = m * G + q;
+    if (k < kKS) nt_store(nw[k], conv_state + rc * kKS + k);
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -610,7 +643,9 @@ template <typename IO, int NMAX>
 int launch_decode(const void* x, const void* z, const void* dt, const void* B, const void* C, const float* A_log,
                   const float* D, const float* dt_bias, const float* conv_w, const float* conv_b,
                   float* conv_state, float* ssm_state, void* y, int Bs, int d, int N, hipStream_t st) {
-  const bool vec = N == NMAX && aligned(ssm_state, 16) && aligned(A_log, 16) && aligned(conv_w, 16);
+  const size_t bca = 4 * sizeof(IO);  // B/C rows are read four elements at a time
+  const bool vec = N == NMAX && aligned(ssm_state, 16) && aligned(A_log, 16) && aligned(conv_w, 16) &&
+                   aligned(B, bca) && aligned(C, bca);
   if (vec) {
     constexpr int CPB = kBlock / (NMAX / 4);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>((d + CPB - 1) / CPB) * Bs));

@@ -114,7 +114,7 @@ def _decode_case(seed, Bs, d, N, io):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("Bs,d,N", [(1, 16, 4), (5, 200, 16), (3, 64, 7), (256, 512, 16)])
+@pytest.mark.parametrize("Bs,d,N", [(1, 16, 4), (5, 200, 16), (3, 64, 7), (256, 512, 16), (9, 136, 8), (2, 72, 12)])
 def test_decode_vs_oracle(io, Bs, d, N):
     log(f"[decode] Bs={Bs} d={d} N={N} io={io}")
     tok, p, cs, ss = _decode_case(Bs + d + N, Bs, d, N, io)
@@ -129,6 +129,8 @@ def test_decode_vs_oracle(io, Bs, d, N):
 
 
 def test_decode_equals_prefill_one_token_sequences():
+    """Decode equals a prefill of Bs one-token sequences: the states bit for bit (same per-element
+    arithmetic); y within tolerance (the decode kernel sums the readout over four lane groups)."""
     Bs, d, N = 37, 130, 16
     tok, p, cs, ss = _decode_case(99, Bs, d, N, "bf16")
     args = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
@@ -137,7 +139,7 @@ def test_decode_equals_prefill_one_token_sequences():
     cs2, ss2 = dev(cs), dev(ss)
     yp = mm.prefill(dev(tok["x"]), dev(tok["z"]), dev(tok["dt"]), dev(tok["B"]), dev(tok["C"]), *args,
                     dev(np.arange(Bs + 1, dtype=np.int32)), cs2, ss2)
-    assert np.array_equal(host(yd), host(yp))
+    assert_within(host(yd), host(yp), "bf16", "decode vs one-token prefill")
     assert np.array_equal(host(ss1), host(ss2)) and np.array_equal(host(cs1), host(cs2))
 
 
