@@ -71,7 +71,7 @@ class HipEvents:
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_causal_amd", "csrc", "mambamix.hip")
-PROFILE_PREFILL = os.path.join(ROOT, "profiles", "k_prefill_final__m130_prefill_8x2048_d1536_N16_bf16.txt")
+PREFILL_PROFILE_SUFFIX = "__m130_prefill_8x2048_d1536_N16_bf16.txt"  # profiles/<final kernel><suffix>
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d8192_N16_bf16.txt")
 
 
@@ -181,8 +181,9 @@ def bench_prefill(args):
             per_kernel[n].append(ev.ms(b + k, b + k + 1))
     ev.close()
     kern_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    plan = mm.plan(S, T, d, N, K)
     return dict(S=S, L=L, T=T, d=d, N=N, K=K, wall_s=wall, kern_ms=kern_ms, names=names,
-                chunk_len=mm.chunk_len(S, T, d, N))
+                chunk_len=plan["chunk_len"], engine=plan["engine_name"])
 
 
 def bench_decode(args):
@@ -398,12 +399,12 @@ def prefill_result(args):
     ms_per_step = pf["wall_s"] / args.steps * 1e3
     tokens_per_s = T * args.steps / pf["wall_s"]
     step_bytes = prefill_alg_bytes(T, pf["S"], d, N, K, 2)
-    dom = "k_prefill_final"
+    dom = pf["names"][-1]  # the final pass: the dominant kernel
     dom_ms = pf["kern_ms"][dom]
     slots, plain, trans = alu_slots_per_token_channel(N)
     achieved_tflops = T * d * slots * 2 / (dom_ms * 1e-3) / 1e12
     roofline = dict(bound="alu", achieved=round(achieved_tflops, 2), peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved_tflops / ALU_PEAK_TFLOPS, 4), traffic=counted_traffic(PROFILE_PREFILL),
+                    frac=round(achieved_tflops / ALU_PEAK_TFLOPS, 4), traffic=counted_traffic(os.path.join(ROOT, "profiles", dom + PREFILL_PROFILE_SUFFIX)),
                     kernel=dom, kernel_ms=round(dom_ms, 4),
                     per_unit=f"{slots} issue slots per (token, channel) = {plain} plain fp32 ops + "
                              f"{trans} transcendentals x {TRANS_SLOTS}; FLOP = 2 x slots")
@@ -413,7 +414,7 @@ def prefill_result(args):
                config=dict(workload="mamba-130m-shaped layer prefill: 8 packed sequences x 2048 tokens, "
                                     "d_inner 1536, d_state 16, conv 4, bf16 io, fp32 state",
                            S=pf["S"], L=pf["L"], T=T, d_inner=d, d_state=N, d_conv=K,
-                           chunk_len=pf["chunk_len"]),
+                           chunk_len=pf["chunk_len"], engine=pf["engine"]),
                roofline=roofline,
                kernels_ms={k: round(v, 4) for k, v in pf["kern_ms"].items()},
                hbm_view=dict(alg_bytes_per_step=step_bytes,

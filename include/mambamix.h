@@ -60,8 +60,8 @@ extern "C" {
 /* status codes */
 #define MM_OK               0
 #define MM_ERR_NULL        -1  /* a required pointer is NULL                                  */
-#define MM_ERR_DIM         -2  /* a negative size, T > INT32_MAX, or S == 0 with T > 0          */
-#define MM_ERR_UNSUPPORTED -3  /* K != 4, N outside 1..16, or unknown io dtype                  */
+#define MM_ERR_DIM         -2  /* a negative size, T > INT32_MAX, S == 0 with T > 0, too few events */
+#define MM_ERR_UNSUPPORTED -3  /* K != 4, N outside 1..16, unknown io dtype or engine            */
 #define MM_ERR_ALIGN       -4  /* a pointer not aligned to its element size                    */
 #define MM_ERR_WORKSPACE   -5  /* workspace smaller than the size query returns (or NULL)      */
 #define MM_ERR_ALIAS       -6  /* y overlaps an input, or conv_state overlaps ssm_state         */
@@ -106,13 +106,20 @@ int mamba_mixer_prefill(const void* x, const void* z, const void* dt, const void
 /* Workspace bytes mamba_mixer_prefill needs for these sizes (0 is possible).  Host only. */
 size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
 
+/* Prefill engines (see mamba_mixer_prefill_ex). */
+#define MM_ENGINE_AUTO   0  /* the library picks from S, T and d                                   */
+#define MM_ENGINE_LANE   1  /* one lane per channel, all N state entries of it in registers        */
+#define MM_ENGINE_SPLIT1 2  /* state entries split across the waves of a workgroup, 1 per wave     */
+#define MM_ENGINE_SPLIT2 3  /* ... 2 state entries per wave                                        */
+#define MM_ENGINE_SPLIT4 4  /* ... 4 state entries per wave                                        */
+
 /*
  * mamba_mixer_prefill_chunked -- mamba_mixer_prefill with an explicit time-chunk
- * length.  The token stream is cut into chunks of `chunk_len` tokens that are
- * processed in parallel and stitched with the associative combine of the
- * recurrence; chunk_len <= 0 picks the length mamba_mixer_prefill uses.  The
- * result does not depend on chunk_len beyond floating-point rounding.  The
- * workspace size for a given chunk_len comes from
+ * length.  Each sequence is cut into chunks of `chunk_len` tokens (the last one
+ * shorter) that are processed in parallel and stitched with the associative
+ * combine of the recurrence; chunk_len <= 0 picks the length mamba_mixer_prefill
+ * uses.  The result does not depend on chunk_len beyond floating-point rounding.
+ * The workspace size for a given chunk_len comes from
  * mamba_mixer_prefill_workspace_bytes_chunked.
  */
 int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, const void* B, const void* C,
@@ -125,32 +132,38 @@ int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, co
 size_t mamba_mixer_prefill_workspace_bytes_chunked(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
                                                    int64_t chunk_len);
 
-/* The chunk length mamba_mixer_prefill picks for these sizes (host only). */
-int64_t mamba_mixer_prefill_chunk_len(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
+/*
+ * mamba_mixer_prefill_ex -- the full-control prefill: explicit chunk length
+ * (<= 0: automatic), explicit engine (MM_ENGINE_*), and optional per-kernel timing
+ * for measurement tools.  When `events` is not NULL the call also records
+ * events[i] (a hipEvent_t the caller created) on `stream` just before the i-th
+ * kernel it enqueues and events[n] just after the last one, where n is the kernel
+ * count mamba_mixer_prefill_plan reports; n_events < n + 1 with events != NULL is
+ * MM_ERR_DIM.  The events are only recorded; the caller owns and destroys them.
+ * An unknown engine is MM_ERR_UNSUPPORTED.  The workspace size comes from
+ * mamba_mixer_prefill_plan with the same chunk_len and engine.
+ */
+int mamba_mixer_prefill_ex(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                           const float* A_log, const float* D, const float* dt_bias,
+                           const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                           float* conv_state, float* ssm_state, void* y,
+                           int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                           int64_t chunk_len, int32_t engine, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events, int32_t n_events);
 
 /*
- * Per-kernel timing for measurement tools.  mamba_mixer_prefill_timed is
- * mamba_mixer_prefill_chunked that, when `events` is not NULL, also records
- * events[i] (a hipEvent_t the caller created) on `stream` just before the i-th
- * kernel the call enqueues and events[n] just after the last one, where
- * n = mamba_mixer_prefill_kernel_count(...) for the same sizes and chunk_len.
- * n_events < n + 1 with events != NULL is MM_ERR_DIM.  The events are only
- * recorded; the caller owns, waits on and destroys them.
- * mamba_mixer_prefill_kernel_name gives the i-th kernel's name ("" if out of
- * range).  Host only.
+ * mamba_mixer_prefill_plan -- what a prefill call with these sizes, chunk_len and
+ * engine will do (host only; each output pointer may be NULL): the chunk length,
+ * the engine, the workspace bytes it needs and the number of kernels it enqueues.
+ * Returns MM_OK or the argument error the call itself would return.
  */
-int mamba_mixer_prefill_timed(const void* x, const void* z, const void* dt, const void* B, const void* C,
-                              const float* A_log, const float* D, const float* dt_bias,
-                              const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
-                              float* conv_state, float* ssm_state, void* y,
-                              int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
-                              int64_t chunk_len, void* workspace, size_t workspace_bytes, void* stream,
-                              void* const* events, int32_t n_events);
+int mamba_mixer_prefill_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len,
+                             int32_t engine, int64_t* chunk_len_out, int32_t* engine_out, size_t* workspace_out,
+                             int32_t* kernels_out);
 
-int32_t mamba_mixer_prefill_kernel_count(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len);
-
+/* Name of the i-th kernel such a call enqueues ("" if out of range).  Host only. */
 const char* mamba_mixer_prefill_kernel_name(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len,
-                                            int32_t i);
+                                            int32_t engine, int32_t i);
 
 /*
  * mamba_mixer_decode -- one token for each of Bs independent rows; row r uses

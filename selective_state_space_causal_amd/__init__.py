@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(HERE, "libmambamix.so")
 MM_OK = 0
 MM_IO_F32 = 0
 MM_IO_BF16 = 1
+ENGINE_AUTO, ENGINE_LANE, ENGINE_SPLIT1, ENGINE_SPLIT2, ENGINE_SPLIT4 = 0, 1, 2, 3, 4
+ENGINE_NAMES = {1: "lane", 2: "split1", 3: "split2", 4: "split4"}
 MAX_N = 16
 CONV_K = 4
 
@@ -47,13 +49,12 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_prefill_workspace_bytes.restype = sz
     lib.mamba_mixer_prefill_workspace_bytes_chunked.argtypes = [i32, i64, i32, i32, i32, i64]
     lib.mamba_mixer_prefill_workspace_bytes_chunked.restype = sz
-    lib.mamba_mixer_prefill_chunk_len.argtypes = [i32, i64, i32, i32, i32]
-    lib.mamba_mixer_prefill_chunk_len.restype = i64
-    lib.mamba_mixer_prefill_timed.argtypes = [P] * 14 + [i32, i64, i32, i32, i32, i32, i64, P, sz, P, P, i32]
-    lib.mamba_mixer_prefill_timed.restype = ctypes.c_int
-    lib.mamba_mixer_prefill_kernel_count.argtypes = [i32, i64, i32, i32, i32, i64]
-    lib.mamba_mixer_prefill_kernel_count.restype = i32
-    lib.mamba_mixer_prefill_kernel_name.argtypes = [i32, i64, i32, i32, i32, i64, i32]
+    lib.mamba_mixer_prefill_ex.argtypes = [P] * 14 + [i32, i64, i32, i32, i32, i32, i64, i32, P, sz, P, P, i32]
+    lib.mamba_mixer_prefill_ex.restype = ctypes.c_int
+    lib.mamba_mixer_prefill_plan.argtypes = [i32, i64, i32, i32, i32, i64, i32, ctypes.POINTER(i64),
+                                             ctypes.POINTER(i32), ctypes.POINTER(sz), ctypes.POINTER(i32)]
+    lib.mamba_mixer_prefill_plan.restype = ctypes.c_int
+    lib.mamba_mixer_prefill_kernel_name.argtypes = [i32, i64, i32, i32, i32, i64, i32, i32]
     lib.mamba_mixer_prefill_kernel_name.restype = ctypes.c_char_p
     lib.mamba_mixer_decode.argtypes = [P] * 13 + [i32, i32, i32, i32, i32, P]
     lib.mamba_mixer_decode.restype = ctypes.c_int
@@ -73,19 +74,33 @@ def version() -> str:
     return load().mamba_mixer_version().decode()
 
 
-def workspace_bytes(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0) -> int:
-    return int(load().mamba_mixer_prefill_workspace_bytes_chunked(S, T, d, N, K, chunk_len))
-
-
-def chunk_len(S: int, T: int, d: int, N: int, K: int = CONV_K) -> int:
-    return int(load().mamba_mixer_prefill_chunk_len(S, T, d, N, K))
-
-
-def kernel_names(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0) -> list[str]:
-    """Names of the kernels one prefill call enqueues, in order."""
+def plan(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0, engine: int = ENGINE_AUTO) -> dict:
+    """What a prefill call with these sizes does: chunk length, engine, workspace bytes, kernel names."""
     lib = load()
-    n = lib.mamba_mixer_prefill_kernel_count(S, T, d, N, K, chunk_len)
-    return [lib.mamba_mixer_prefill_kernel_name(S, T, d, N, K, chunk_len, i).decode() for i in range(n)]
+    L, e, w, k = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_size_t(), ctypes.c_int32()
+    rc = lib.mamba_mixer_prefill_plan(S, T, d, N, K, chunk_len, engine, ctypes.byref(L), ctypes.byref(e),
+                                      ctypes.byref(w), ctypes.byref(k))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_prefill_plan")
+    names = [lib.mamba_mixer_prefill_kernel_name(S, T, d, N, K, chunk_len, engine, i).decode()
+             for i in range(k.value)]
+    return dict(chunk_len=L.value, engine=e.value, engine_name=ENGINE_NAMES.get(e.value, "none"),
+                workspace_bytes=w.value, kernels=names)
+
+
+def workspace_bytes(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0,
+                    engine: int = ENGINE_AUTO) -> int:
+    return plan(S, T, d, N, K, chunk_len, engine)["workspace_bytes"]
+
+
+def chunk_len(S: int, T: int, d: int, N: int, K: int = CONV_K, engine: int = ENGINE_AUTO) -> int:
+    return plan(S, T, d, N, K, 0, engine)["chunk_len"]
+
+
+def kernel_names(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0,
+                 engine: int = ENGINE_AUTO) -> list[str]:
+    """Names of the kernels one prefill call enqueues, in order."""
+    return plan(S, T, d, N, K, chunk_len, engine)["kernels"]
 
 
 def _io_code(t) -> int:
@@ -121,7 +136,7 @@ def _check(t, shape, dtype, name):
 
 
 def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state,
-            y=None, workspace=None, chunk_len: int = 0, stream=None, events=None):
+            y=None, workspace=None, chunk_len: int = 0, stream=None, events=None, engine: int = ENGINE_AUTO):
     """Run the mixer over packed sequences; conv_state / ssm_state are updated in place.
 
     x, z, dt [T, d] and B, C [T, N] share one io dtype (float32 or bfloat16); A_log [d, N],
@@ -148,7 +163,7 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
     if y is None:
         y = torch.empty((T, d), dtype=io, device=x.device)
     _check(y, (T, d), io, "y")
-    need = workspace_bytes(S, T, d, N, CONV_K, chunk_len)
+    need = workspace_bytes(S, T, d, N, CONV_K, chunk_len, engine) if T > 0 and d > 0 and S > 0 else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
@@ -158,10 +173,10 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
     else:  # raw hipEvent_t handles, recorded around each kernel of the call
         ev = (ctypes.c_void_p * len(events))(*events)
         nev = len(events)
-    rc = load().mamba_mixer_prefill_timed(
+    rc = load().mamba_mixer_prefill_ex(
         _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(conv_w),
         _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(ssm_state), _ptr(y),
-        S, T, d, N, CONV_K, _io_code(x), int(chunk_len), wptr, wbytes, _stream(stream), ev, nev)
+        S, T, d, N, CONV_K, _io_code(x), int(chunk_len), int(engine), wptr, wbytes, _stream(stream), ev, nev)
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_prefill")
     return y

@@ -86,7 +86,7 @@ def make_prefill(seed, lens, d, N, io, nonzero_state=True, extra_slots=0):
     return dict(cu=inputs.cu_from_lengths(lens), T=T, S=S, d=d, N=N, io=io, cs=cs, ss=ss, **tok, **p)
 
 
-def run_gpu_prefill(case, chunk_len=0, slots=None):
+def run_gpu_prefill(case, chunk_len=0, slots=None, engine=0):
     """Run the HIP prefill on a case; returns (y, conv_state, ssm_state) as float64 numpy."""
     import selective_state_space_causal_amd as mm
 
@@ -95,7 +95,7 @@ def run_gpu_prefill(case, chunk_len=0, slots=None):
     ss = dev(case["ss"][:S] if slots is None else case["ss"])
     y = mm.prefill(dev(case["x"]), dev(case["z"]), dev(case["dt"]), dev(case["B"]), dev(case["C"]),
                    dev(case["A_log"]), dev(case["D"]), dev(case["dt_bias"]), dev(case["conv_w"]),
-                   dev(case["conv_b"]), dev(case["cu"]), cs, ss, chunk_len=chunk_len)
+                   dev(case["conv_b"]), dev(case["cu"]), cs, ss, chunk_len=chunk_len, engine=engine)
     torch.cuda.synchronize()
     return host(y), host(cs), host(ss)
 

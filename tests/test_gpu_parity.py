@@ -22,49 +22,60 @@ def _gpu():
     oracle.build(force=False)
 
 
-def _check_prefill(case, chunk_len, what):
-    log(f"[prefill] {what}: T={case['T']} S={case['S']} d={case['d']} N={case['N']} io={case['io']} chunk={chunk_len}")
-    y, cs, ss = run_gpu_prefill(case, chunk_len)
+ENGINES = [mm.ENGINE_LANE, mm.ENGINE_SPLIT1, mm.ENGINE_SPLIT2, mm.ENGINE_SPLIT4]
+
+
+def _check_prefill(case, chunk_len, what, engine=0):
+    log(f"[prefill] {what}: T={case['T']} S={case['S']} d={case['d']} N={case['N']} io={case['io']} "
+        f"chunk={chunk_len} engine={engine}")
+    y, cs, ss = run_gpu_prefill(case, chunk_len, engine=engine)
     yr, csr, ssr = run_oracle_prefill(case)
     assert_within(y, yr, case["io"], f"{what} y")
     assert_within(ss, ssr, case["io"], f"{what} ssm_state")
     assert np.array_equal(cs, csr), f"{what}: conv_state not bit-exact"
 
 
-def test_tiny_f32_workload():
+@pytest.mark.parametrize("engine", [0] + ENGINES)
+def test_tiny_f32_workload(engine):
     """B=1, L=64, d=16, N=4, fp32 io, seed 0, zero initial states (the small workload)."""
     case = make_prefill(0, [64], 16, 4, "f32", nonzero_state=False)
     for ch in (0, 64, 16, 7):
-        _check_prefill(case, ch, "tiny_f32")
+        _check_prefill(case, ch, "tiny_f32", engine)
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("chunk", [0, 64, 100, 1000])
-def test_ragged_packed(io, chunk):
+def test_ragged_packed(io, chunk, engine):
     """Several tiles, ragged channel block (d=200), empty and < K-1 sequences, nonzero slots."""
     case = make_prefill(3, [300, 1, 0, 2, 517, 64, 3], 200, 16, io)
-    _check_prefill(case, chunk, f"ragged io={io}")
+    _check_prefill(case, chunk, f"ragged io={io}", engine)
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 9, 16])
-def test_state_sizes(N):
+def test_state_sizes(N, engine):
     case = make_prefill(10 + N, [70, 130, 33], 72, N, "f32")
-    _check_prefill(case, 48, f"N={N}")
+    _check_prefill(case, 48, f"N={N}", engine)
 
 
-def test_sequences_ending_on_chunk_boundaries():
-    lens = [64, 64, 128, 1, 63, 64, 1]
+@pytest.mark.parametrize("engine", ENGINES)
+def test_sequences_ending_on_chunk_boundaries(engine):
+    lens = [64, 64, 128, 1, 63, 64, 1, 16, 17, 15]
     case = make_prefill(5, lens, 64, 16, "bf16")
-    for ch in (64, 32, 65):
-        _check_prefill(case, ch, "boundaries")
+    for ch in (64, 32, 16, 65):
+        _check_prefill(case, ch, "boundaries", engine)
 
 
-def test_packed_equals_separate_gpu():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_packed_equals_separate_gpu(engine):
+    """Chunks never cross a sequence boundary, so with the same chunk length and engine a packed run
+    and per-sequence runs do the same arithmetic: bit-identical."""
     lens = [257, 3, 0, 900, 128, 2]
     case = make_prefill(7, lens, 128, 16, "bf16")
     T = case["T"]
-    y, cs, ss = run_gpu_prefill(case, chunk_len=T)  # one chunk: same arithmetic order as separate runs
-    yc, csc, ssc = run_gpu_prefill(case, chunk_len=96)
+    y, cs, ss = run_gpu_prefill(case, chunk_len=T, engine=engine)
+    yc, csc, ssc = run_gpu_prefill(case, chunk_len=96, engine=engine)
     cu = case["cu"]
     for s in range(len(lens)):
         g0, g1 = int(cu[s]), int(cu[s + 1])
@@ -75,10 +86,13 @@ def test_packed_equals_separate_gpu():
                    ss=case["ss"][s:s + 1])
         if g1 == g0:
             continue
-        ys, css, sss = run_gpu_prefill(sub, chunk_len=g1 - g0)
+        ys, css, sss = run_gpu_prefill(sub, chunk_len=T, engine=engine)
         assert np.array_equal(ys, y[g0:g1]), f"seq {s}: packed != separate (single chunk)"
         assert np.array_equal(sss[0], ss[s]) and np.array_equal(css[0], cs[s])
-        assert_within(yc[g0:g1], ys, "bf16", f"seq {s} multi-chunk vs separate")
+        ysc, cssc, sssc = run_gpu_prefill(sub, chunk_len=96, engine=engine)
+        assert np.array_equal(ysc, yc[g0:g1]), f"seq {s}: packed != separate (96-token chunks)"
+        assert np.array_equal(sssc[0], ssc[s]) and np.array_equal(cssc[0], csc[s])
+        assert_within(yc[g0:g1], ys, "bf16", f"seq {s} multi-chunk vs single chunk")
     # the empty sequence's slot is unchanged
     assert np.array_equal(cs[2], case["cs"][2]) and np.array_equal(ss[2], case["ss"][2])
 
@@ -168,25 +182,25 @@ def test_isolation_and_guards():
     G = 64  # guard elements
     args = [dev(case[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
 
-    def run(xarr, chunk):
+    def run(xarr, chunk, engine):
         csf = dev(case["cs"])  # S + 2 slots
         ssf = dev(case["ss"])
         ybuf = torch.full((T * d + 2 * G,), float("nan"), dtype=torch.bfloat16, device="cuda")
         y = ybuf[G:G + T * d].view(T, d)
         mm.prefill(dev(xarr), dev(case["z"]), dev(case["dt"]), dev(case["B"]), dev(case["C"]), *args,
-                   dev(case["cu"]), csf[:S], ssf[:S], y=y, chunk_len=chunk)
+                   dev(case["cu"]), csf[:S], ssf[:S], y=y, chunk_len=chunk, engine=engine)
         torch.cuda.synchronize()
         return host(ybuf), host(csf), host(ssf)
 
-    for chunk in (0, 40):
-        yb, csf, ssf = run(case["x"], chunk)
+    for chunk, engine in ((0, 0), (40, mm.ENGINE_LANE), (40, mm.ENGINE_SPLIT1), (24, mm.ENGINE_SPLIT2)):
+        yb, csf, ssf = run(case["x"], chunk, engine)
         assert np.all(np.isnan(yb[:G])) and np.all(np.isnan(yb[G + T * d:])), "guard region written"
         assert np.all(np.isfinite(yb[G:G + T * d])), "a y element was not written"
         assert np.array_equal(csf[S:], case["cs"][S:]) and np.array_equal(ssf[S:], case["ss"][S:])
         x2 = case["x"].copy()
         cu = case["cu"]
         x2[cu[1]:cu[2]] ^= np.uint16(0x0040)  # perturb sequence 1 only
-        yb2, csf2, ssf2 = run(x2, chunk)
+        yb2, csf2, ssf2 = run(x2, chunk, engine)
         y1 = yb[G:G + T * d].reshape(T, d)
         y2 = yb2[G:G + T * d].reshape(T, d)
         for s in (0, 2, 4):

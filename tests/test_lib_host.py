@@ -127,24 +127,37 @@ def test_decode_validation(lib):
     assert _decode(lib, [ctypes.c_void_p(0)] * 13, Bs=0) == 0
 
 
-def test_workspace_query_and_chunk_plan(lib):
+def test_workspace_query_and_plan(lib):
     assert mm.workspace_bytes(0, 0, 64, 16) == 0
     assert mm.workspace_bytes(1, 64, 16, 4) > 0
-    # one chunk: only the packed B/C copy (T * 2 * NMAX floats, 256-byte aligned)
-    assert mm.workspace_bytes(1, 64, 16, 4, chunk_len=64) == 64 * 2 * 4 * 4
-    # more chunks need more workspace, and the size is a pure function of the arguments
+    # the size is a pure function of the arguments, and grows with the number of carry slots
     w1 = mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=16384)
     w2 = mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=256)
     assert w2 > w1
     assert mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=256) == w2
-    assert mm.workspace_bytes(8, 16384, 1536, 16) == mm.workspace_bytes(8, 16384, 1536, 16,
-                                                                        chunk_len=mm.chunk_len(8, 16384, 1536, 16))
-    # the automatic chunk length targets ~32768 waves of 64 channels, never below 128 tokens
-    for (S, T, d) in ((8, 16384, 1536), (8, 16384, 4096), (256, 131072, 8192), (1, 8192, 5120), (1, 64, 16)):
-        L = mm.chunk_len(S, T, d, 16)
-        assert 1 <= L <= T
-        assert L >= min(T, 128)
-        waves = -(-T // L) * -(-d // 64)
-        assert waves <= 32768 + -(-d // 64)
-    assert mm.chunk_len(256, 131072, 8192, 16) == 512
-    assert mm.chunk_len(8, 16384, 1536, 16) == 128
+    p = mm.plan(8, 16384, 1536, 16)
+    assert mm.workspace_bytes(8, 16384, 1536, 16) == p["workspace_bytes"]
+    # few (sequence, channel-block) pairs -> the split engine, whole sequences per chunk
+    assert p["engine_name"] == "split1" and p["chunk_len"] == 2048
+    assert p["kernels"][0] == "k_chunk_plan" and p["kernels"][-1] == "k_split_final"
+    # many sequences -> the lane engine; sequences of the mean length are not split
+    q = mm.plan(256, 131072, 8192, 16)
+    assert q["engine_name"] == "lane" and q["chunk_len"] >= 512 and q["kernels"][-1] == "k_lane_final"
+    # a single long sequence is split into chunks to fill the GPU
+    r = mm.plan(1, 131072, 5120, 16)
+    assert r["engine_name"] == "split1" and r["chunk_len"] < 131072 and "k_carry" in r["kernels"]
+    # explicit engines and chunk lengths are honoured (chunk lengths round up to 16)
+    for e, name in ((1, "lane"), (2, "split1"), (3, "split2"), (4, "split4")):
+        pe = mm.plan(3, 500, 100, 16, chunk_len=40, engine=e)
+        assert pe["engine_name"] == name and pe["chunk_len"] == 48
+    # unknown engine
+    with pytest.raises(mm.MambaMixError):
+        mm.plan(3, 500, 100, 16, engine=9)
+    p = _ptrs(14)
+    ws = ctypes.c_void_p(0x70000000)
+    rc = lib.mamba_mixer_prefill_ex(*p, 2, 100, 64, 16, 4, 1, 0, 9, ws, 1 << 30, None, None, 0)
+    assert rc == MM_ERR_UNSUPPORTED
+    # too few events for the kernels of the call
+    evs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    rc = lib.mamba_mixer_prefill_ex(*p, 2, 100, 64, 16, 4, 1, 0, 0, ws, 1 << 30, None, evs, 2)
+    assert rc == MM_ERR_DIM
