@@ -112,6 +112,7 @@ size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int3
 #define MM_ENGINE_SPLIT1 2  /* state entries split across the waves of a workgroup, 1 per wave     */
 #define MM_ENGINE_SPLIT2 3  /* ... 2 state entries per wave                                        */
 #define MM_ENGINE_SPLIT4 4  /* ... 4 state entries per wave                                        */
+#define MM_ENGINE_ROW    5  /* one channel per 16-lane row, one state entry per lane (DPP exchange) */
 
 /*
  * mamba_mixer_prefill_chunked -- mamba_mixer_prefill with an explicit time-chunk

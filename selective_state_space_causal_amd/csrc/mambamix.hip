@@ -22,6 +22,7 @@
 #include "mm_decode.h"
 #include "mm_device.h"
 #include "mm_prefill.h"
+#include "mm_row.h"
 
 namespace mm {
 namespace {
@@ -29,7 +30,7 @@ namespace {
 // ---------------------------------------------------------------- prefill plan
 
 // The lane engine needs this many (chunk, 64-channel block) waves to keep the
-// GPU busy without splitting sequences; below it the split engine takes over.
+// GPU busy without splitting sequences; below it the row engine takes over.
 constexpr int64_t kLaneMinWaves = 4096;
 constexpr int64_t kCUs = 256;
 
@@ -38,7 +39,7 @@ inline int nmax_for(int N) { return N <= 4 ? 4 : (N <= 8 ? 8 : 16); }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
-  int engine;  // MM_ENGINE_LANE or MM_ENGINE_SPLIT1/2/4
+  int engine;  // MM_ENGINE_LANE, MM_ENGINE_ROW or MM_ENGINE_SPLIT1/2/4
   int npw;     // split engine: state entries per wave
   int nmax;
   int64_t Lc;    // chunk length
@@ -47,6 +48,7 @@ struct Plan {
   int64_t Tpad;  // B/C rows incl. zero padding past T
   size_t off_off, off_moff, off_bc, off_a, off_b, off_stash, total;
   int kernels;   // kernels one call enqueues
+  bool whole;    // row engine with one chunk per sequence: no plan, no carries
 };
 
 int npw_of(int engine) { return engine == MM_ENGINE_SPLIT4 ? 4 : (engine == MM_ENGINE_SPLIT2 ? 2 : 1); }
@@ -60,20 +62,45 @@ double split_cost(int64_t S, int64_t nblk, int64_t P) {
   return (1.0 + 0.85 * (P - 1) / P) / util;
 }
 
+// Relative time of the row engine with P chunks per (average) sequence: pass 1
+// costs about half of pass 2 per token, and the GPU is full at about three
+// workgroups (12 waves) per CU.
+double row_cost(int64_t S, int d, int64_t P) {
+  const double wgs = static_cast<double>(S) * P * cdiv(d, kRowChans);
+  const double full = 3.0 * kCUs;
+  const double util = wgs >= full ? 1.0 : wgs / full;
+  return (1.0 + 0.55 * (P - 1) / P) / util;
+}
+
+// workgroups of a row-engine launch: (chunk, channel-group) items, 8 per 32 workgroups
+int64_t row_grid(int64_t chunks, int d) {
+  const int64_t items = chunks * cdiv(cdiv(d, kRowChans), kRowGroup);
+  return cdiv(items, kXcds) * kXcds * kRowGroup;
+}
+
 int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, int engine) {
   p = Plan{};
   p.nmax = nmax_for(N);
   const int64_t nblk = cdiv(d, kWave);
   const int64_t avg = cdiv(T, S > 0 ? S : 1);
-  if (engine == MM_ENGINE_AUTO) engine = (S * nblk >= kLaneMinWaves) ? MM_ENGINE_LANE : MM_ENGINE_SPLIT1;
-  if (engine != MM_ENGINE_LANE && engine != MM_ENGINE_SPLIT1 && engine != MM_ENGINE_SPLIT2 &&
-      engine != MM_ENGINE_SPLIT4)
+  if (engine == MM_ENGINE_AUTO) engine = (S * nblk >= kLaneMinWaves) ? MM_ENGINE_LANE : MM_ENGINE_ROW;
+  if (engine != MM_ENGINE_LANE && engine != MM_ENGINE_ROW && engine != MM_ENGINE_SPLIT1 &&
+      engine != MM_ENGINE_SPLIT2 && engine != MM_ENGINE_SPLIT4)
     return MM_ERR_UNSUPPORTED;
   p.engine = engine;
-  p.npw = engine == MM_ENGINE_LANE ? 0 : npw_of(engine);
+  if (engine == MM_ENGINE_ROW) p.nmax = kRow;  // one state entry per lane of a 16-lane row
+  p.npw = (engine == MM_ENGINE_LANE || engine == MM_ENGINE_ROW) ? 0 : npw_of(engine);
   if (p.npw > p.nmax) p.npw = p.nmax;
   if (chunk_len > 0) {
     p.Lc = chunk_len;
+  } else if (engine == MM_ENGINE_ROW) {
+    // chunks shorter than ~256 tokens are not worth their carries
+    const int64_t pmax = avg / 256 < 16 ? avg / 256 : 16;
+    int64_t best = 1;
+    for (int64_t P = 2; P <= pmax; ++P)
+      if (row_cost(S, d, P) < row_cost(S, d, best)) best = P;
+    // one chunk per sequence: a chunk longer than the whole stream leaves no carries
+    p.Lc = best == 1 ? T + 1 : cdiv(avg, best);
   } else if (engine == MM_ENGINE_LANE) {
     // sequences up to 4x the mean length stay whole; longer ones are split for balance
     p.Lc = 4 * avg;
@@ -88,12 +115,16 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   p.Lc = (p.Lc + 15) / 16 * 16;
   p.Pmax = cdiv(T, p.Lc) + S;
   p.Mmax = T / p.Lc;
-  const int tile = p.engine == MM_ENGINE_LANE ? 0 : p.nmax / p.npw;
+  const int tile = p.npw == 0 ? 0 : p.nmax / p.npw;
   p.Tpad = T + (tile > 16 ? tile : 16);
+  // packed B/C rows (the row engine stages B/C itself)
+  const size_t nbc = engine == MM_ENGINE_ROW ? 0 : static_cast<size_t>(p.Tpad) * 2 * p.nmax;
+  p.whole = engine == MM_ENGINE_ROW && p.Lc > T;
   size_t off = 0;
   p.off_off = off; off += align256(static_cast<size_t>(S + 1) * sizeof(int32_t));
   p.off_moff = off; off += align256(static_cast<size_t>(S + 1) * sizeof(int32_t));
-  p.off_bc = off; off += align256(static_cast<size_t>(p.Tpad) * 2 * p.nmax * sizeof(float));
+  p.off_bc = off; off += align256(nbc * sizeof(float));
+  if (p.whole) off = 0;  // nothing in the workspace is used
   if (p.Mmax > 0) {
     p.off_a = off; off += align256(static_cast<size_t>(p.Mmax) * d * sizeof(float));
     p.off_b = off; off += align256(static_cast<size_t>(p.Mmax) * d * p.nmax * sizeof(float));
@@ -101,21 +132,30 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   }
   p.total = off;
   p.kernels = p.Mmax > 0 ? 5 : 3;
-  const int64_t wg_rows = engine == MM_ENGINE_LANE ? cdiv(d, kBlock) : nblk;
-  if (p.Pmax * wg_rows > INT32_MAX || p.Pmax > INT32_MAX) return MM_ERR_DIM;
+  if (engine == MM_ENGINE_ROW) p.kernels = p.whole ? 1 : (p.Mmax > 0 ? 4 : 2);
+  const int64_t wgs = engine == MM_ENGINE_LANE ? p.Pmax * cdiv(d, kBlock)
+                      : engine == MM_ENGINE_ROW ? row_grid(p.whole ? S : p.Pmax, d) : p.Pmax * nblk;
+  if (wgs > INT32_MAX || p.Pmax > INT32_MAX) return MM_ERR_DIM;
   return MM_OK;
 }
 
 const char* kernel_name(const Plan& p, int i) {
-  const bool lane = p.engine == MM_ENGINE_LANE;
+  const char* agg = p.engine == MM_ENGINE_LANE ? "k_lane_agg" : (p.engine == MM_ENGINE_ROW ? "k_row_agg" : "k_split_agg");
+  const char* fin =
+      p.engine == MM_ENGINE_LANE ? "k_lane_final" : (p.engine == MM_ENGINE_ROW ? "k_row_final" : "k_split_final");
+  if (p.engine == MM_ENGINE_ROW) {  // stages B/C itself: no packing kernel
+    if (p.whole) return i == 0 ? fin : "";
+    const char* names[4] = {"k_chunk_plan", p.Mmax > 0 ? agg : fin, "k_carry", fin};
+    return i < p.kernels ? names[i] : "";
+  }
   if (i == 0) return "k_chunk_plan";
   if (i == 1) return "k_pack_bc";
   if (p.Mmax > 0) {
-    if (i == 2) return lane ? "k_lane_agg" : "k_split_agg";
+    if (i == 2) return agg;
     if (i == 3) return "k_carry";
-    if (i == 4) return lane ? "k_lane_final" : "k_split_final";
+    if (i == 4) return fin;
   } else if (i == 2) {
-    return lane ? "k_lane_final" : "k_split_final";
+    return fin;
   }
   return "";
 }
@@ -174,6 +214,36 @@ void launch_split(const Plan& p, const PrefillArgs& a, CarryWs cw, const float* 
                      static_cast<IO*>(a.y), cw, a.S, a.d, a.N, p.Lc);
 }
 
+template <typename IO>
+void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st, StageEvents& evs) {
+  const IO* xi = static_cast<const IO*>(a.x);
+  const IO* zi = static_cast<const IO*>(a.z);
+  const IO* di = static_cast<const IO*>(a.dt);
+  const IO* Bi = static_cast<const IO*>(a.B);
+  const IO* Ci = static_cast<const IO*>(a.C);
+  const dim3 grid(static_cast<unsigned>(row_grid(p.whole ? a.S : p.Pmax, a.d)));
+  const dim3 block(kRowThreads);
+  const int whole = p.whole ? 1 : 0;
+  if (!p.whole) {
+    evs.mark(st);
+    hipLaunchKernelGGL(k_chunk_plan, dim3(1), dim3(kPlanThreads), 0, st, a.cu, a.S, p.Lc, cw.off, cw.moff);
+  }
+  if (p.Mmax > 0) {
+    evs.mark(st);
+    hipLaunchKernelGGL((k_row<IO, false>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias,
+                       a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d,
+                       a.N, p.Lc, whole);
+    evs.mark(st);
+    const int64_t q = static_cast<int64_t>(a.d) * kRow;
+    hipLaunchKernelGGL((k_carry<kRow>), dim3(static_cast<unsigned>(cdiv(q, kBlock))), dim3(kBlock), 0, st, cw,
+                       a.A_log, a.S, a.d, a.N);
+  }
+  evs.mark(st);
+  hipLaunchKernelGGL((k_row<IO, true>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w,
+                     a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d, a.N, p.Lc,
+                     whole);
+}
+
 template <typename IO, int NMAX>
 int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st, StageEvents evs) {
   CarryWs cw{};
@@ -183,6 +253,11 @@ int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st
     cw.a = reinterpret_cast<float*>(ws + p.off_a);
     cw.b = reinterpret_cast<float*>(ws + p.off_b);
     cw.stash = reinterpret_cast<float*>(ws + p.off_stash);
+  }
+  if (p.engine == MM_ENGINE_ROW) {
+    if constexpr (NMAX == kRow) launch_row<IO>(p, a, cw, st, evs);
+    evs.mark(st);
+    return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
   }
   float* bc = reinterpret_cast<float*>(ws + p.off_bc);
   evs.mark(st);
@@ -284,7 +359,7 @@ const char* mamba_mixer_status_string(int status) {
   }
 }
 
-const char* mamba_mixer_version(void) { return "libmambamix 0.2 gfx950"; }
+const char* mamba_mixer_version(void) { return "libmambamix 0.3 gfx950"; }
 
 int mamba_mixer_prefill_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len,
                              int32_t engine, int64_t* chunk_len_out, int32_t* engine_out, size_t* workspace_out,

@@ -53,7 +53,8 @@ def _ptrs(n, start=A):
     return [ctypes.c_void_p(start + i * STEP) for i in range(n)]
 
 
-def _prefill(lib, ptrs, S=2, T=100, d=64, N=16, K=4, io=1, ws=None, wsb=0, chunk=0):
+def _prefill(lib, ptrs, S=2, T=100, d=64, N=16, K=4, io=1, ws=None, wsb=0, chunk=32):
+    # 32-token chunks: a plan that needs workspace (whole sequences need none)
     return lib.mamba_mixer_prefill_chunked(*ptrs, S, T, d, N, K, io, chunk, ws, wsb, None)
 
 
@@ -63,8 +64,8 @@ def _decode(lib, ptrs, Bs=2, d=64, N=16, K=4, io=1):
 
 def test_prefill_validation(lib):
     p = _ptrs(14)
-    ws_need = mm.workspace_bytes(2, 100, 64, 16)
-    assert ws_need > 0
+    ws_need = mm.workspace_bytes(2, 100, 64, 16, chunk_len=32)
+    assert ws_need > 0 and mm.workspace_bytes(2, 100, 64, 16) == 0
     ws = ctypes.c_void_p(0x70000000)
     assert _prefill(lib, p, K=3, ws=ws, wsb=ws_need) == MM_ERR_UNSUPPORTED
     assert _prefill(lib, p, N=17, ws=ws, wsb=ws_need) == MM_ERR_UNSUPPORTED
@@ -129,7 +130,8 @@ def test_decode_validation(lib):
 
 def test_workspace_query_and_plan(lib):
     assert mm.workspace_bytes(0, 0, 64, 16) == 0
-    assert mm.workspace_bytes(1, 64, 16, 4) > 0
+    assert mm.workspace_bytes(1, 64, 16, 4) == 0  # one sequence, one chunk: the row engine needs none
+    assert mm.workspace_bytes(1, 64, 16, 4, engine=mm.ENGINE_LANE) > 0
     # the size is a pure function of the arguments, and grows with the number of carry slots
     w1 = mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=16384)
     w2 = mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=256)
@@ -137,17 +139,18 @@ def test_workspace_query_and_plan(lib):
     assert mm.workspace_bytes(8, 16384, 1536, 16, chunk_len=256) == w2
     p = mm.plan(8, 16384, 1536, 16)
     assert mm.workspace_bytes(8, 16384, 1536, 16) == p["workspace_bytes"]
-    # few (sequence, channel-block) pairs -> the split engine, whole sequences per chunk
-    assert p["engine_name"] == "split1" and p["chunk_len"] == 2048
-    assert p["kernels"][0] == "k_chunk_plan" and p["kernels"][-1] == "k_split_final"
+    # few (sequence, channel-block) pairs -> the row engine, whole sequences per chunk
+    assert p["engine_name"] == "row" and p["chunk_len"] > 16384
+    assert p["kernels"] == ["k_row_final"] and p["workspace_bytes"] == 0
     # many sequences -> the lane engine; sequences of the mean length are not split
     q = mm.plan(256, 131072, 8192, 16)
     assert q["engine_name"] == "lane" and q["chunk_len"] >= 512 and q["kernels"][-1] == "k_lane_final"
     # a single long sequence is split into chunks to fill the GPU
     r = mm.plan(1, 131072, 5120, 16)
-    assert r["engine_name"] == "split1" and r["chunk_len"] < 131072 and "k_carry" in r["kernels"]
+    assert r["engine_name"] == "row" and r["chunk_len"] < 131072
+    assert r["kernels"] == ["k_chunk_plan", "k_row_agg", "k_carry", "k_row_final"]
     # explicit engines and chunk lengths are honoured (chunk lengths round up to 16)
-    for e, name in ((1, "lane"), (2, "split1"), (3, "split2"), (4, "split4")):
+    for e, name in ((1, "lane"), (2, "split1"), (3, "split2"), (4, "split4"), (5, "row")):
         pe = mm.plan(3, 500, 100, 16, chunk_len=40, engine=e)
         assert pe["engine_name"] == name and pe["chunk_len"] == 48
     # unknown engine
@@ -159,5 +162,5 @@ def test_workspace_query_and_plan(lib):
     assert rc == MM_ERR_UNSUPPORTED
     # too few events for the kernels of the call
     evs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
-    rc = lib.mamba_mixer_prefill_ex(*p, 2, 100, 64, 16, 4, 1, 0, 0, ws, 1 << 30, None, evs, 2)
+    rc = lib.mamba_mixer_prefill_ex(*p, 2, 100, 64, 16, 4, 1, 32, 0, ws, 1 << 30, None, evs, 2)
     assert rc == MM_ERR_DIM
