@@ -70,7 +70,20 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_causal_amd", "csrc", "mambamix.hip")
+KERNEL_DIR = os.path.join(ROOT, "selective_state_space_causal_amd", "csrc")
+
+
+def kernel_source_sha256():
+    """sha256 over the HIP sources (every file of csrc/, in name order), to tie a counter summary to them."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
 PREFILL_PROFILE_SUFFIX = "__m130_prefill_8x2048_d1536_N16_bf16.txt"  # profiles/<final kernel><suffix>
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d8192_N16_bf16.txt")
 
@@ -78,11 +91,9 @@ PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d
 def counted_traffic(profile_path):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None when the summary is
     missing or was taken on a different kernel source than the one built now."""
-    import hashlib
-
     try:
         text = open(profile_path).read()
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        src = kernel_source_sha256()
     except OSError:
         return None
     sha = traffic = None
@@ -289,7 +300,8 @@ def bench_decode(args):
 
 
 def cpu_baseline(lens, d, N, io):
-    """The fp64 oracle on this host: the whole bench prefill workload (all tokens, all channels)."""
+    """The fp64 oracle on this host's cores: full prefills of the bench workload (all tokens, all
+    channels), repeated until about 12 s of CPU time have been spent (at most 8 runs)."""
     import oracle
 
     oracle.build(force=False)
@@ -299,14 +311,17 @@ def cpu_baseline(lens, d, N, io):
         ncpu = os.cpu_count() or 1
     threads = oracle.threads(min(ncpu, 64))
     tok, p, cs, ss, cu = make_prefill_set(0, lens, d, N, io)
-    t0 = time.perf_counter()
-    oracle.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"], p["D"], p["dt_bias"],
-                   p["conv_w"], p["conv_b"], cu, cs, ss)
-    el = time.perf_counter() - t0
     T = int(sum(lens))
-    return dict(value=T / el, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"one full prefill of the bench workload ({len(lens)} x {lens[0]} tokens, d={d}, N={N}), "
-                       f"fp64, {el:.2f} s wall on {threads} threads (input widening to fp64 included)")
+    runs, c0, t0 = 0, time.process_time(), time.perf_counter()
+    while runs < 8 and (runs == 0 or time.process_time() - c0 < 12.0):
+        oracle.prefill(tok["x"], tok["z"], tok["dt"], tok["B"], tok["C"], p["A_log"], p["D"], p["dt_bias"],
+                       p["conv_w"], p["conv_b"], cu, cs, ss)
+        runs += 1
+    el = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return dict(value=round(runs * T / el, 1), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{runs} full prefills of the bench workload ({len(lens)} x {lens[0]} tokens, d={d}, N={N}), "
+                       f"fp64, {el:.2f} s wall, {cpu:.1f} s CPU on {threads} threads (input widening to fp64 included)")
 
 
 def copy_calibration():
@@ -357,6 +372,7 @@ def main():
     ap.add_argument("--summarize-rocprof", metavar="CSV",
                     help="print a per-kernel table of a rocprofv3 kernel_stats.csv or counter_collection.csv "
                          "and exit")
+    ap.add_argument("--source-sha", action="store_true", help="print the HIP source hash and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy three times (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -365,6 +381,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.source_sha:
+        print(kernel_source_sha256())
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -107,12 +107,9 @@ int mamba_mixer_prefill(const void* x, const void* z, const void* dt, const void
 size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
 
 /* Prefill engines (see mamba_mixer_prefill_ex). */
-#define MM_ENGINE_AUTO   0  /* the library picks from S, T and d                                   */
-#define MM_ENGINE_LANE   1  /* one lane per channel, all N state entries of it in registers        */
-#define MM_ENGINE_SPLIT1 2  /* state entries split across the waves of a workgroup, 1 per wave     */
-#define MM_ENGINE_SPLIT2 3  /* ... 2 state entries per wave                                        */
-#define MM_ENGINE_SPLIT4 4  /* ... 4 state entries per wave                                        */
-#define MM_ENGINE_ROW    5  /* one channel per 16-lane row, one state entry per lane (DPP exchange) */
+#define MM_ENGINE_AUTO 0  /* the library picks from S, T and d                                        */
+#define MM_ENGINE_LANE 1  /* one lane per channel, all N state entries of it in registers             */
+#define MM_ENGINE_ROW  2  /* one channel per 16-lane row, one state entry per lane (for few sequences) */
 
 /*
  * mamba_mixer_prefill_chunked -- mamba_mixer_prefill with an explicit time-chunk

@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(HERE, "libmambamix.so")
 MM_OK = 0
 MM_IO_F32 = 0
 MM_IO_BF16 = 1
-ENGINE_AUTO, ENGINE_LANE, ENGINE_SPLIT1, ENGINE_SPLIT2, ENGINE_SPLIT4, ENGINE_ROW = 0, 1, 2, 3, 4, 5
-ENGINE_NAMES = {1: "lane", 2: "split1", 3: "split2", 4: "split4", 5: "row"}
+ENGINE_AUTO, ENGINE_LANE, ENGINE_ROW = 0, 1, 2
+ENGINE_NAMES = {1: "lane", 2: "row"}
 MAX_N = 16
 CONV_K = 4
 

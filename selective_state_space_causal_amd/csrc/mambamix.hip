@@ -18,6 +18,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <cmath>
+
 #include "mambamix.h"
 #include "mm_decode.h"
 #include "mm_device.h"
@@ -39,8 +41,7 @@ inline int nmax_for(int N) { return N <= 4 ? 4 : (N <= 8 ? 8 : 16); }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
-  int engine;  // MM_ENGINE_LANE, MM_ENGINE_ROW or MM_ENGINE_SPLIT1/2/4
-  int npw;     // split engine: state entries per wave
+  int engine;  // MM_ENGINE_LANE or MM_ENGINE_ROW
   int nmax;
   int64_t Lc;    // chunk length
   int64_t Pmax;  // chunk grid bound: ceil(T / Lc) + S
@@ -51,25 +52,25 @@ struct Plan {
   bool whole;    // row engine with one chunk per sequence: no plan, no carries
 };
 
-int npw_of(int engine) { return engine == MM_ENGINE_SPLIT4 ? 4 : (engine == MM_ENGINE_SPLIT2 ? 2 : 1); }
-
-// Relative time of the split engine with P chunks per (average) sequence: the
-// aggregate pass recomputes (P-1)/P of the tokens at ~0.85 of the final pass's cost,
-// and fewer than one workgroup per CU leaves CUs idle.
-double split_cost(int64_t S, int64_t nblk, int64_t P) {
-  const double wgs = static_cast<double>(S) * P * nblk;
-  const double util = wgs >= kCUs ? 1.0 : wgs / kCUs;
-  return (1.0 + 0.85 * (P - 1) / P) / util;
+// Modelled time (microseconds) of the row engine with P chunks per (average)
+// sequence, fitted to measurements on MI355X.  A pass is as slow as its busiest
+// CU: with g = workgroups / 256, some CU runs ceil(g) workgroups of W / wgs
+// (token, channel) pairs each, at a per-CU rate of ~575 M pairs/s with >= 4
+// workgroups (16 waves) on the CU, ~500 M/s with 2-3 and less with 1.  Pass 1
+// runs ~1.33x faster (no readout); chunking adds the plan and carry kernels
+// (~13 us).
+double row_pass_us(double W, double wgs, double speed) {
+  if (wgs <= 0) return 0.0;
+  const double g = std::ceil(wgs / kCUs);
+  const double rate = 575.0 * (g >= 4 ? 1.0 : (g >= 2 ? 0.88 : 0.6)) * speed;  // pairs per us per CU
+  return g * (W / wgs) / rate;
 }
-
-// Relative time of the row engine with P chunks per (average) sequence: pass 1
-// costs about half of pass 2 per token, and the GPU is full at about three
-// workgroups (12 waves) per CU.
-double row_cost(int64_t S, int d, int64_t P) {
-  const double wgs = static_cast<double>(S) * P * cdiv(d, kRowChans);
-  const double full = 3.0 * kCUs;
-  const double util = wgs >= full ? 1.0 : wgs / full;
-  return (1.0 + 0.55 * (P - 1) / P) / util;
+double row_cost(int64_t S, int64_t T, int d, int64_t P) {
+  const double W = static_cast<double>(T) * d;
+  const double wgs = static_cast<double>(S) * cdiv(d, kRowChans);
+  double t = row_pass_us(W, wgs * P, 1.0);
+  if (P > 1) t += row_pass_us(W * (P - 1) / P, wgs * (P - 1), 1.33) + 13.0;
+  return t;
 }
 
 // workgroups of a row-engine launch: (chunk, channel-group) items, 8 per 32 workgroups
@@ -84,13 +85,9 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   const int64_t nblk = cdiv(d, kWave);
   const int64_t avg = cdiv(T, S > 0 ? S : 1);
   if (engine == MM_ENGINE_AUTO) engine = (S * nblk >= kLaneMinWaves) ? MM_ENGINE_LANE : MM_ENGINE_ROW;
-  if (engine != MM_ENGINE_LANE && engine != MM_ENGINE_ROW && engine != MM_ENGINE_SPLIT1 &&
-      engine != MM_ENGINE_SPLIT2 && engine != MM_ENGINE_SPLIT4)
-    return MM_ERR_UNSUPPORTED;
+  if (engine != MM_ENGINE_LANE && engine != MM_ENGINE_ROW) return MM_ERR_UNSUPPORTED;
   p.engine = engine;
   if (engine == MM_ENGINE_ROW) p.nmax = kRow;  // one state entry per lane of a 16-lane row
-  p.npw = (engine == MM_ENGINE_LANE || engine == MM_ENGINE_ROW) ? 0 : npw_of(engine);
-  if (p.npw > p.nmax) p.npw = p.nmax;
   if (chunk_len > 0) {
     p.Lc = chunk_len;
   } else if (engine == MM_ENGINE_ROW) {
@@ -98,25 +95,19 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
     const int64_t pmax = avg / 256 < 16 ? avg / 256 : 16;
     int64_t best = 1;
     for (int64_t P = 2; P <= pmax; ++P)
-      if (row_cost(S, d, P) < row_cost(S, d, best)) best = P;
+      if (row_cost(S, T, d, P) < row_cost(S, T, d, best)) best = P;
     // one chunk per sequence: a chunk longer than the whole stream leaves no carries
     p.Lc = best == 1 ? T + 1 : cdiv(avg, best);
-  } else if (engine == MM_ENGINE_LANE) {
-    // sequences up to 4x the mean length stay whole; longer ones are split for balance
+  } else {
+    // lane engine: sequences up to 4x the mean length stay whole; longer ones are split for balance
     p.Lc = 4 * avg;
     if (p.Lc < 512) p.Lc = 512;
-  } else {
-    int64_t best = 1;
-    for (int64_t P = 2; P <= 16; ++P)
-      if (split_cost(S, nblk, P) < split_cost(S, nblk, best)) best = P;
-    p.Lc = cdiv(avg, best);
   }
   if (p.Lc < 16) p.Lc = 16;  // >= 3 keeps a continuing chunk's conv window inside its sequence
   p.Lc = (p.Lc + 15) / 16 * 16;
   p.Pmax = cdiv(T, p.Lc) + S;
   p.Mmax = T / p.Lc;
-  const int tile = p.npw == 0 ? 0 : p.nmax / p.npw;
-  p.Tpad = T + (tile > 16 ? tile : 16);
+  p.Tpad = T + 16;
   // packed B/C rows (the row engine stages B/C itself)
   const size_t nbc = engine == MM_ENGINE_ROW ? 0 : static_cast<size_t>(p.Tpad) * 2 * p.nmax;
   p.whole = engine == MM_ENGINE_ROW && p.Lc > T;
@@ -133,16 +124,14 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   p.total = off;
   p.kernels = p.Mmax > 0 ? 5 : 3;
   if (engine == MM_ENGINE_ROW) p.kernels = p.whole ? 1 : (p.Mmax > 0 ? 4 : 2);
-  const int64_t wgs = engine == MM_ENGINE_LANE ? p.Pmax * cdiv(d, kBlock)
-                      : engine == MM_ENGINE_ROW ? row_grid(p.whole ? S : p.Pmax, d) : p.Pmax * nblk;
+  const int64_t wgs = engine == MM_ENGINE_LANE ? p.Pmax * cdiv(d, kBlock) : row_grid(p.whole ? S : p.Pmax, d);
   if (wgs > INT32_MAX || p.Pmax > INT32_MAX) return MM_ERR_DIM;
   return MM_OK;
 }
 
 const char* kernel_name(const Plan& p, int i) {
-  const char* agg = p.engine == MM_ENGINE_LANE ? "k_lane_agg" : (p.engine == MM_ENGINE_ROW ? "k_row_agg" : "k_split_agg");
-  const char* fin =
-      p.engine == MM_ENGINE_LANE ? "k_lane_final" : (p.engine == MM_ENGINE_ROW ? "k_row_final" : "k_split_final");
+  const char* agg = p.engine == MM_ENGINE_LANE ? "k_lane_agg" : "k_row_agg";
+  const char* fin = p.engine == MM_ENGINE_LANE ? "k_lane_final" : "k_row_final";
   if (p.engine == MM_ENGINE_ROW) {  // stages B/C itself: no packing kernel
     if (p.whole) return i == 0 ? fin : "";
     const char* names[4] = {"k_chunk_plan", p.Mmax > 0 ? agg : fin, "k_carry", fin};
@@ -189,30 +178,6 @@ struct PrefillArgs {
   int64_t T;
   int d, N;
 };
-
-template <typename IO, int NMAX, int NPW>
-void launch_split(const Plan& p, const PrefillArgs& a, CarryWs cw, const float* bct, hipStream_t st,
-                  StageEvents& evs) {
-  constexpr int NW = NMAX / NPW;
-  const IO* xi = static_cast<const IO*>(a.x);
-  const IO* zi = static_cast<const IO*>(a.z);
-  const IO* di = static_cast<const IO*>(a.dt);
-  const dim3 grid(static_cast<unsigned>(p.Pmax * cdiv(a.d, kWave)));
-  if (p.Mmax > 0) {
-    evs.mark(st);
-    hipLaunchKernelGGL((k_split<IO, NMAX, NPW, false>), grid, dim3(kWave * NW), 0, st, xi, zi, di, bct, p.Tpad,
-                       a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state,
-                       static_cast<IO*>(a.y), cw, a.S, a.d, a.N, p.Lc);
-    evs.mark(st);
-    const int64_t q = static_cast<int64_t>(a.d) * NMAX;
-    hipLaunchKernelGGL((k_carry<NMAX>), dim3(static_cast<unsigned>(cdiv(q, kBlock))), dim3(kBlock), 0, st, cw,
-                       a.A_log, a.S, a.d, a.N);
-  }
-  evs.mark(st);
-  hipLaunchKernelGGL((k_split<IO, NMAX, NPW, true>), grid, dim3(kWave * NW), 0, st, xi, zi, di, bct, p.Tpad,
-                     a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state,
-                     static_cast<IO*>(a.y), cw, a.S, a.d, a.N, p.Lc);
-}
 
 template <typename IO>
 void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st, StageEvents& evs) {
@@ -267,7 +232,7 @@ int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st
   const dim3 gbc(static_cast<unsigned>(cdiv(nbc, kBlock)));
   const IO* Bi = static_cast<const IO*>(a.B);
   const IO* Ci = static_cast<const IO*>(a.C);
-  if (p.engine == MM_ENGINE_LANE) {
+  {
     hipLaunchKernelGGL((k_pack_bc_rows<IO, NMAX>), gbc, dim3(kBlock), 0, st, Bi, Ci, bc, a.T, p.Tpad, a.N);
     const IO* xi = static_cast<const IO*>(a.x);
     const IO* zi = static_cast<const IO*>(a.z);
@@ -286,11 +251,6 @@ int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st
     hipLaunchKernelGGL((k_lane_final<IO, NMAX>), grid, dim3(kBlock), 0, st, xi, zi, di, bc, a.A_log, a.D,
                        a.dt_bias, a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw,
                        a.S, a.d, a.N, p.Lc);
-  } else {
-    hipLaunchKernelGGL((k_pack_bc_cols<IO, NMAX>), gbc, dim3(kBlock), 0, st, Bi, Ci, bc, a.T, p.Tpad, a.N);
-    if (p.npw == 1) launch_split<IO, NMAX, 1>(p, a, cw, bc, st, evs);
-    else if (p.npw == 2) launch_split<IO, NMAX, (NMAX >= 2 ? 2 : 1)>(p, a, cw, bc, st, evs);
-    else launch_split<IO, NMAX, (NMAX >= 4 ? 4 : 1)>(p, a, cw, bc, st, evs);
   }
   evs.mark(st);
   return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;

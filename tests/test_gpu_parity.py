@@ -22,7 +22,7 @@ def _gpu():
     oracle.build(force=False)
 
 
-ENGINES = [mm.ENGINE_LANE, mm.ENGINE_ROW, mm.ENGINE_SPLIT1, mm.ENGINE_SPLIT2, mm.ENGINE_SPLIT4]
+ENGINES = [mm.ENGINE_LANE, mm.ENGINE_ROW]
 
 
 def _check_prefill(case, chunk_len, what, engine=0):
@@ -192,7 +192,7 @@ def test_isolation_and_guards():
         torch.cuda.synchronize()
         return host(ybuf), host(csf), host(ssf)
 
-    for chunk, engine in ((0, 0), (40, mm.ENGINE_LANE), (40, mm.ENGINE_ROW), (40, mm.ENGINE_SPLIT1), (24, mm.ENGINE_SPLIT2)):
+    for chunk, engine in ((0, 0), (40, mm.ENGINE_LANE), (40, mm.ENGINE_ROW), (24, mm.ENGINE_ROW)):
         yb, csf, ssf = run(case["x"], chunk, engine)
         assert np.all(np.isnan(yb[:G])) and np.all(np.isnan(yb[G + T * d:])), "guard region written"
         assert np.all(np.isfinite(yb[G:G + T * d])), "a y element was not written"
