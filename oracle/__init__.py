@@ -113,3 +113,27 @@ def decode(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_st
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return y, cs, ss
+
+
+def decode_replay(x_ring, dt_ring, B_ring, k, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
+                  nthreads: int = 0):
+    """Decode step k of a replay window ("ReplaySSM: Cache SSM Inputs, Not State", abstract).
+
+    The recurrent state is kept as a checkpoint (``conv_state``, ``ssm_state``: the state before
+    window step 0) plus a buffer of the recent steps' inputs (``x_ring``, ``dt_ring`` [W, Bs, d]
+    and ``B_ring`` [W, Bs, N]; slot s holds window step s).  The output of step k comes from
+    replaying the buffered steps 0..k-1 from the checkpoint and then taking step k with its own
+    z and C: the plain sequential definition, one ``decode`` step after another.  The outputs of
+    the replayed steps were emitted by earlier calls; only their effect on the state matters here.
+
+    Returns (y_k, conv_state, ssm_state) with the states after step k (float64).
+    """
+    Bs, d = np.asarray(z).shape
+    N = np.asarray(C).shape[1]
+    cs, ss = conv_state, ssm_state
+    zero_z = np.zeros((Bs, d))
+    zero_c = np.zeros((Bs, N))
+    for s in range(k):
+        _, cs, ss = decode(x_ring[s], zero_z, dt_ring[s], B_ring[s], zero_c, A_log, D, dt_bias, conv_w, conv_b,
+                           cs, ss, nthreads)
+    return decode(x_ring[k], z, dt_ring[k], B_ring[k], C, A_log, D, dt_bias, conv_w, conv_b, cs, ss, nthreads)

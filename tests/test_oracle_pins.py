@@ -295,6 +295,30 @@ def test_oracle_decode_steps_equal_scan(oracle_lib):
     assert np.array_equal(yp, yd) and np.array_equal(csp, csd) and np.array_equal(ssp, ssd)
 
 
+def test_oracle_replay_equals_scan(oracle_lib):
+    """Replay decode (checkpoint + buffered inputs) equals the prefill routine run over the same
+    tokens from the checkpoint: y of the last token and both final states, bit for bit.  Replaying
+    one step too few or too many, or dropping a buffered B, fails this."""
+    Bs, W, d, N = 3, 4, 5, 16
+    tok, p, _, _ = _rand_case(43, Bs * W, d, N)
+    rng = np.random.default_rng(6)
+    conv0 = rng.standard_normal((Bs, d, 3))
+    h0 = rng.standard_normal((Bs, d, N))
+    args = (p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"])
+    # token t of row r is window step t: ring slot t holds rows (r*W + t)
+    ring = {k: np.stack([tok[k][[r * W + t for r in range(Bs)]] for t in range(W)]) for k in ("x", "dt", "B")}
+    for k in range(W):
+        rows = [r * W + k for r in range(Bs)]
+        y, cs, ss = oracle_lib.decode_replay(ring["x"], ring["dt"], ring["B"], k, tok["z"][rows], tok["C"][rows],
+                                             *args, conv0, h0)
+        sel = [r * W + t for r in range(Bs) for t in range(k + 1)]
+        yp, csp, ssp = oracle_lib.prefill(tok["x"][sel], tok["z"][sel], tok["dt"][sel], tok["B"][sel],
+                                          tok["C"][sel], *args, inputs.cu_from_lengths([k + 1] * Bs), conv0, h0)
+        last = [r * (k + 1) + k for r in range(Bs)]
+        assert np.array_equal(y, yp[last]), k
+        assert np.array_equal(cs, csp) and np.array_equal(ss, ssp), k
+
+
 def test_oracle_isolation_and_channel_subset(oracle_lib):
     lens = [9, 30, 4]
     d, N = 12, 4
