@@ -86,6 +86,7 @@ def kernel_source_sha256():
 
 PREFILL_PROFILE_SUFFIX = "__m130_prefill_8x2048_d1536_N16_bf16.txt"  # profiles/<final kernel><suffix>
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d8192_N16_bf16.txt")
+PROFILE_REPLAY = os.path.join(ROOT, "profiles", "k_decode_replay__m7b_decode_b256_d8192_N16_W4_bf16.txt")
 
 
 def counted_traffic(profile_path):
@@ -123,6 +124,22 @@ def prefill_alg_bytes(T, S, d, N, K, s_io):
 
 def decode_alg_bytes(Bs, d, N, K, s_io):
     return Bs * d * 4 * s_io + 2 * Bs * N * s_io + d * (N + K + 3) * 4 + 2 * Bs * d * (N + K - 1) * 4
+
+
+def replay_alg_bytes(Bs, d, N, K, s_io, W):
+    """Mean bytes per replay-decode step over a window of W steps: every step reads the checkpoint
+    (ssm + conv state), the buffered x, dt of steps 0..k and B of steps 0..k, this step's z and C,
+    the parameters, and writes y; the last step of the window also writes the checkpoint."""
+    total = 0
+    for k in range(W):
+        b = Bs * d * (N + K - 1) * 4                      # checkpoint read
+        b += Bs * d * 2 * (k + 1) * s_io + Bs * N * (k + 1) * s_io  # buffered x, dt and B
+        b += Bs * d * 2 * s_io + Bs * N * s_io            # z in, y out; C
+        b += d * (N + K + 3) * 4                          # parameters
+        if k == W - 1:
+            b += Bs * d * (N + K - 1) * 4                 # checkpoint write
+        total += b
+    return total / W
 
 
 def alu_slots_per_token_channel(N):
@@ -200,13 +217,15 @@ def bench_prefill(args):
 def bench_decode(args):
     """Batch-256 decode: a 512-token prefill initialises the states, then 128 decode steps.
 
-    Three measurements of the same 128 steps:
+    Measurements of the same 128 steps:
       * per-kernel time with the 256 MB Infinity Cache flushed before every step (a 1 GiB
-        buffer is rewritten; the kernel is timed alone with HIP events on the launch stream):
+        buffer is read; the kernel is timed alone with HIP events on the launch stream):
         this is the HBM-roofline number;
       * the 128 steps captured in one HIP graph and replayed back to back (the serving loop
         without host launch overhead; the fp32 state may stay cache-resident between steps);
-      * the same steps launched eagerly from Python.
+      * the same steps launched eagerly from Python;
+      * the replay decode (checkpoint + ring of the window's inputs) over the same steps,
+        flushed per kernel and as a HIP graph; its last output must equal the eager one.
     Every measurement starts from the prefilled states.
     """
     import torch
@@ -233,10 +252,14 @@ def bench_decode(args):
     torch.cuda.empty_cache()
     cs0, ss0 = csd.clone(), ssd.clone()
     t0 = time.perf_counter()
-    dins = []
+    # the steps' inputs stacked [steps, Bs, ...]: four consecutive steps are also a replay window's ring
+    stk = {k: [] for k in ("x", "z", "dt", "B", "C")}
     for s in range(steps):
         dt_ = inputs.decode_inputs(0, s, Bs, d, N, io)
-        dins.append([dev(dt_[k]) for k in ("x", "z", "dt", "B", "C")])
+        for k in stk:
+            stk[k].append(dev(dt_[k]))
+    stk = {k: torch.stack(v) for k, v in stk.items()}
+    dins = [[stk[k][s] for k in ("x", "z", "dt", "B", "C")] for s in range(steps)]
     log(f"[bench] decode step inputs generated in {time.perf_counter() - t0:.1f}s")
     y = torch.empty((Bs, d), dtype=torch.bfloat16, device="cuda")
 
@@ -249,12 +272,14 @@ def bench_decode(args):
         mm.decode(*dins[s], *prm, csd, ssd, y=y)
     torch.cuda.synchronize()
 
-    # (1) flushed, per kernel
+    # (1) flushed, per kernel: before each step a 1 GiB buffer is read (not written), so the
+    # Infinity Cache holds clean lines of that buffer and no write-back of earlier steps'
+    # dirty lines lands inside the timed kernel
     restore()
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for s in range(steps):
-        flush.fill_(float(s))
+        flush.sum()
         evs[s][0].record()
         mm.decode(*dins[s], *prm, csd, ssd, y=y)
         evs[s][1].record()
@@ -294,9 +319,53 @@ def bench_decode(args):
         mm.decode(*dins[s], *prm, csd, ssd, y=y)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
+    y_eager_last = y.clone()
+
+    # (4) replay decode over the same steps: windows of W steps, each window's ring is a
+    # view of four consecutive stacked steps; flushed per-kernel timing, then a HIP graph
+    W = 4
+
+    def replay(s, stream=None):
+        w0 = (s // W) * W
+        return mm.decode_replay(stk["x"][w0:w0 + W], stk["dt"][w0:w0 + W], stk["B"][w0:w0 + W], stk["z"][s],
+                                stk["C"][s], *prm, csd, ssd, s - w0, y=y, stream=stream)
+
+    restore()
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s in range(steps):
+        flush.sum()
+        rev[s][0].record()
+        replay(s)
+        rev[s][1].record()
+    torch.cuda.synchronize()
+    rkern = [a.elapsed_time(b) for a, b in rev]
+    del flush
+    replay_matches = bool(torch.equal(y, y_eager_last))
+    restore()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gstream):
+        with torch.cuda.graph(g2, stream=gstream):
+            for s in range(steps):
+                replay(s, stream=gstream)
+    torch.cuda.current_stream().wait_stream(gstream)
+    torch.cuda.synchronize()
+    g2.replay()
+    torch.cuda.synchronize()
+    restore()
+    torch.cuda.synchronize()
+    e0.record()
+    g2.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    rgraph_ms = e0.elapsed_time(e1)
+    replay_graph_matches = bool(torch.equal(y, y_eager_last))
     return dict(Bs=Bs, d=d, N=N, K=K, steps=steps, kern_ms=float(np.mean(kern_ms)),
                 kern_ms_min=float(np.min(kern_ms)), graph_ms=graph_ms, eager_s=eager_s,
-                graph_matches_eager=same, init_T=T, init_ms=init_ms, init_kern=init_kern)
+                graph_matches_eager=same, init_T=T, init_ms=init_ms, init_kern=init_kern,
+                replay=dict(W=W, kern_ms=float(np.mean(rkern)), kern_ms_min=float(np.min(rkern)),
+                            kern_ms_by_k=[float(np.mean(rkern[k::W])) for k in range(W)], graph_ms=rgraph_ms,
+                            matches_eager=replay_matches and replay_graph_matches))
 
 
 def cpu_baseline(lens, d, N, io):
@@ -443,6 +512,26 @@ def prefill_result(args):
     return out
 
 
+def replay_result(dc):
+    rp = dc["replay"]
+    rb = replay_alg_bytes(dc["Bs"], dc["d"], dc["N"], dc["K"], 2, rp["W"])
+    gbs = rb / (rp["kern_ms"] * 1e-3) / 1e9
+    return dict(
+        what="replay decode (checkpoint + ring of the last W steps' x, dt, B; the state is written once "
+             "per window), same 128 steps",
+        W=rp["W"],
+        steps_per_s=round(dc["steps"] / (rp["graph_ms"] * 1e-3), 1),
+        steps_per_s_note="128 steps captured in one HIP graph and replayed back to back",
+        steps_per_s_kernel_flushed=round(1e3 / rp["kern_ms"], 1),
+        kernel_ms_by_window_step=[round(v, 4) for v in rp["kern_ms_by_k"]],
+        roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(gbs / HBM_PEAK_GBS, 4), traffic=counted_traffic(PROFILE_REPLAY),
+                      kernel="k_decode_replay",
+                      kernel_ms=round(rp["kern_ms"], 4), alg_bytes_per_launch_mean=round(rb),
+                      note="mean over the window; kernel timed alone, Infinity Cache flushed before each step"),
+        y_matches_eager_decode=rp["matches_eager"])
+
+
 def decode_result(args):
     dc = bench_decode(args)
     db = decode_alg_bytes(dc["Bs"], dc["d"], dc["N"], dc["K"], 2)
@@ -463,6 +552,7 @@ def decode_result(args):
                       alg_bytes_per_launch=db,
                       note="kernel timed alone with HIP events, Infinity Cache flushed before each step"),
         graph_replay_matches_flushed_run=dc["graph_matches_eager"],
+        replay=replay_result(dc),
         init_prefill=dict(T=dc["init_T"], ms=round(dc["init_ms"], 3),
                           tokens_per_s=round(dc["init_T"] / (dc["init_ms"] * 1e-3), 1),
                           kernels_ms={k: round(v, 4) for k, v in dc["init_kern"].items()},

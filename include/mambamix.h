@@ -182,6 +182,37 @@ int mamba_mixer_decode(const void* x, const void* z, const void* dt, const void*
                        float* conv_state, float* ssm_state, void* y,
                        int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype, void* stream);
 
+/*
+ * mamba_mixer_decode_replay -- one decode token for each of Bs rows with the state
+ * kept as a checkpoint plus the inputs of the recent steps ("ReplaySSM: Cache SSM
+ * Inputs, Not State", abstract: the state is represented as a checkpoint and a
+ * buffer of recent inputs, and the checkpoint is updated only periodically, so most
+ * steps read the state but do not write it).
+ *
+ * A window has W steps (1 <= W <= 4); this call is step k of it (0 <= k < W).
+ *   x_ring, dt_ring [W, Bs, d]  io   raw x and dt of window steps 0..k; the caller writes
+ *                                    step k's x and dt into slot k before the call
+ *   B_ring          [W, Bs, N]  io   B of window steps 0..k, slot k likewise
+ *   z [Bs, d], C [Bs, N]        io   gate input and readout vector of step k
+ *   A_log [d, N], D [d], dt_bias [d], conv_w [d, K], conv_b [d]   f32
+ *   conv_state [Bs, d, K-1], ssm_state [Bs, d, N]   f32  the checkpoint: the state before
+ *                                    window step 0.  Read every call; overwritten with the
+ *                                    state after step k when the call commits
+ *   y [Bs, d]                   io   out: step k's output
+ * The call commits when commit != 0 or k == W - 1; after a committing call the next
+ * window starts at k = 0 (the ring slots are free again).  Step k's output and the
+ * committed state equal, bit for bit, those of k + 1 mamba_mixer_decode calls from the
+ * checkpoint (the same operations in the same order).
+ * Limits: N == 16 (else MM_ERR_UNSUPPORTED); W outside 1..4 or k outside 0..W-1 is
+ * MM_ERR_DIM; A_log, conv_w and ssm_state must be 16-byte aligned and B_ring, C aligned
+ * to 4 elements (MM_ERR_ALIGN).  Bs == 0 or d == 0 is a successful no-op.
+ */
+int mamba_mixer_decode_replay(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z,
+                              const void* C, const float* A_log, const float* D, const float* dt_bias,
+                              const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
+                              void* y, int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype, int32_t W,
+                              int32_t k, int32_t commit, void* stream);
+
 /* Static text for a status code (never NULL).  Host only. */
 const char* mamba_mixer_status_string(int status);
 

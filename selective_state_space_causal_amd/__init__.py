@@ -58,6 +58,8 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_prefill_kernel_name.restype = ctypes.c_char_p
     lib.mamba_mixer_decode.argtypes = [P] * 13 + [i32, i32, i32, i32, i32, P]
     lib.mamba_mixer_decode.restype = ctypes.c_int
+    lib.mamba_mixer_decode_replay.argtypes = [P] * 13 + [i32, i32, i32, i32, i32, i32, i32, i32, P]
+    lib.mamba_mixer_decode_replay.restype = ctypes.c_int
     lib.mamba_mixer_status_string.argtypes = [ctypes.c_int]
     lib.mamba_mixer_status_string.restype = ctypes.c_char_p
     lib.mamba_mixer_version.argtypes = []
@@ -208,4 +210,41 @@ def decode(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_st
         _stream(stream))
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_decode")
+    return y
+
+
+def decode_replay(x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, k: int,
+                  commit: bool = False, y=None, stream=None):
+    """Step k of a replay window (see ``mamba_mixer_decode_replay``).
+
+    x_ring, dt_ring [W, Bs, d] and B_ring [W, Bs, N] hold the raw inputs of window steps 0..k
+    (slot k is this step's); z [Bs, d] and C [Bs, N] are this step's.  conv_state / ssm_state
+    are the checkpoint (the state before window step 0); they are overwritten with the state
+    after step k when the call commits (commit=True or k == W - 1).  Returns y [Bs, d].
+    """
+    import torch
+
+    W, Bs, d = x_ring.shape
+    N = B_ring.shape[2]
+    io = x_ring.dtype
+    _check(x_ring, (W, Bs, d), io, "x_ring")
+    _check(dt_ring, (W, Bs, d), io, "dt_ring")
+    _check(B_ring, (W, Bs, N), io, "B_ring")
+    _check(z, (Bs, d), io, "z")
+    _check(C, (Bs, N), io, "C")
+    _check(A_log, (d, N), torch.float32, "A_log")
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (conv_b, "conv_b")):
+        _check(t, (d,), torch.float32, n)
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(conv_state, (Bs, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (Bs, d, N), torch.float32, "ssm_state")
+    if y is None:
+        y = torch.empty((Bs, d), dtype=io, device=x_ring.device)
+    _check(y, (Bs, d), io, "y")
+    rc = load().mamba_mixer_decode_replay(
+        _ptr(x_ring), _ptr(dt_ring), _ptr(B_ring), _ptr(z), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias),
+        _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(ssm_state), _ptr(y), Bs, d, N, CONV_K, _io_code(x_ring),
+        W, int(k), 1 if commit else 0, _stream(stream))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_decode_replay")
     return y

@@ -35,6 +35,9 @@ namespace {
 // GPU busy without splitting sequences; below it the row engine takes over.
 constexpr int64_t kLaneMinWaves = 4096;
 constexpr int64_t kCUs = 256;
+// replay decode: N = 16 (4 lanes x 4 state entries per channel), windows of at most 4 steps
+constexpr int kReplayN = 16;
+constexpr int kReplayMaxW = 4;
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 inline int nmax_for(int N) { return N <= 4 ? 4 : (N <= 8 ? 8 : 16); }
@@ -267,11 +270,11 @@ int launch_decode(const void* x, const void* z, const void* dt, const void* B, c
                    aligned(B, bca) && aligned(C, bca);
   if (vec) {
     constexpr int CPB = kBlock / (NMAX / 4);
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>((d + CPB - 1) / CPB) * Bs));
+    const dim3 grid(static_cast<unsigned>(cdiv(d, CPB) * cdiv(Bs, NMAX / 4)));
     hipLaunchKernelGGL((k_decode_vec<IO, NMAX>), grid, dim3(kBlock), 0, st, static_cast<const IO*>(x),
                        static_cast<const IO*>(z), static_cast<const IO*>(dt), static_cast<const IO*>(B),
                        static_cast<const IO*>(C), A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
-                       static_cast<IO*>(y), d);
+                       static_cast<IO*>(y), Bs, d);
   } else {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>((d + kBlock - 1) / kBlock) * Bs));
     hipLaunchKernelGGL((k_decode<IO, NMAX>), grid, dim3(kBlock), 0, st, static_cast<const IO*>(x),
@@ -463,6 +466,57 @@ int mamba_mixer_decode(const void* x, const void* z, const void* dt, const void*
   if (nm == 8) return MM_DECODE(float, 8);
   return MM_DECODE(float, 16);
 #undef MM_DECODE
+}
+
+int mamba_mixer_decode_replay(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z,
+                              const void* C, const float* A_log, const float* D, const float* dt_bias,
+                              const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
+                              void* y, int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype, int32_t W,
+                              int32_t k, int32_t commit, void* stream) {
+  int rc = check_common(Bs, d, N, K, io_dtype);
+  if (rc != MM_OK) return rc;
+  if (N != kReplayN) return MM_ERR_UNSUPPORTED;
+  if (W < 1 || W > kReplayMaxW || k < 0 || k >= W) return MM_ERR_DIM;
+  if (Bs == 0 || d == 0) return MM_OK;
+  const void* req[] = {x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y};
+  for (const void* p : req)
+    if (p == nullptr) return MM_ERR_NULL;
+  const size_t es = io_dtype == MM_IO_BF16 ? 2 : 4;
+  const void* iop[] = {x_ring, dt_ring, z, y};
+  for (const void* p : iop)
+    if (!aligned(p, es)) return MM_ERR_ALIGN;
+  const void* vec[] = {B_ring, C};  // rows are read four elements at a time
+  for (const void* p : vec)
+    if (!aligned(p, 4 * es)) return MM_ERR_ALIGN;
+  const void* fp[] = {D, dt_bias, conv_b, conv_state};
+  for (const void* p : fp)
+    if (!aligned(p, 4)) return MM_ERR_ALIGN;
+  const void* f16[] = {A_log, conv_w, ssm_state};
+  for (const void* p : f16)
+    if (!aligned(p, 16)) return MM_ERR_ALIGN;
+  const size_t ny = static_cast<size_t>(Bs) * d * es, nring = static_cast<size_t>(W) * ny;
+  const size_t nbr = static_cast<size_t>(W) * Bs * N * es, nc = static_cast<size_t>(Bs) * N * es;
+  if (overlap(y, ny, x_ring, nring) || overlap(y, ny, dt_ring, nring) || overlap(y, ny, B_ring, nbr) ||
+      overlap(y, ny, z, ny) || overlap(y, ny, C, nc))
+    return MM_ERR_ALIAS;
+  if (overlap(conv_state, static_cast<size_t>(Bs) * d * kKS * 4, ssm_state, static_cast<size_t>(Bs) * d * N * 4))
+    return MM_ERR_ALIAS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(cdiv(d, kBlock) * Bs));
+  const int cm = (commit != 0 || k == W - 1) ? 1 : 0;
+  if (io_dtype == MM_IO_BF16) {
+    hipLaunchKernelGGL((k_decode_replay<uint16_t>), grid, dim3(kBlock), 0, st,
+                       static_cast<const uint16_t*>(x_ring), static_cast<const uint16_t*>(dt_ring),
+                       static_cast<const uint16_t*>(B_ring), static_cast<const uint16_t*>(z),
+                       static_cast<const uint16_t*>(C), A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
+                       static_cast<uint16_t*>(y), Bs, d, k, cm);
+  } else {
+    hipLaunchKernelGGL((k_decode_replay<float>), grid, dim3(kBlock), 0, st, static_cast<const float*>(x_ring),
+                       static_cast<const float*>(dt_ring), static_cast<const float*>(B_ring),
+                       static_cast<const float*>(z), static_cast<const float*>(C), A_log, D, dt_bias, conv_w,
+                       conv_b, conv_state, ssm_state, static_cast<float*>(y), Bs, d, k, cm);
+  }
+  return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }
 
 }  // extern "C"

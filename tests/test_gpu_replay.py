@@ -1,0 +1,113 @@
+"""Replay decode (checkpoint + buffered inputs) on the GPU: bit-identical to the eager decode
+step by step, and within tolerance of the oracle's replay."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_causal_amd as mm
+from selective_state_space_causal_amd import inputs
+from tests.gpu_util import assert_within, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _stream(seed, steps, Bs, d, N, io):
+    toks = [inputs.decode_inputs(seed, s, Bs, d, N, io) for s in range(steps)]
+    p = inputs.params(seed, d, N, 4)
+    rng = np.random.default_rng(seed)
+    cs = rng.standard_normal((Bs, d, 3)).astype(np.float32)
+    if io == "bf16":  # the conv state holds raw inputs; keep them bf16-representable
+        cs = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(cs)).reshape(cs.shape)
+    ss = (0.5 * rng.standard_normal((Bs, d, N))).astype(np.float32)
+    return toks, p, cs, ss
+
+
+def _run_replay(toks, p, cs, ss, W, commit_at=()):
+    """Feed the steps through the replay path; returns per-step y and the checkpoint after each
+    committing step."""
+    steps = len(toks)
+    Bs, d = toks[0]["x"].shape
+    N = toks[0]["B"].shape[1]
+    io = torch.bfloat16 if toks[0]["x"].dtype == np.uint16 else torch.float32
+    prm = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    csd, ssd = dev(cs), dev(ss)
+    xr = torch.zeros((W, Bs, d), dtype=io, device="cuda")
+    dr = torch.zeros((W, Bs, d), dtype=io, device="cuda")
+    br = torch.zeros((W, Bs, N), dtype=io, device="cuda")
+    ys, ckpts = [], {}
+    k = 0
+    for s in range(steps):
+        xr[k].copy_(dev(toks[s]["x"]))
+        dr[k].copy_(dev(toks[s]["dt"]))
+        br[k].copy_(dev(toks[s]["B"]))
+        commit = s in commit_at
+        y = mm.decode_replay(xr, dr, br, dev(toks[s]["z"]), dev(toks[s]["C"]), *prm, csd, ssd, k, commit=commit)
+        ys.append(host(y))
+        if commit or k == W - 1:
+            ckpts[s] = (host(csd), host(ssd))
+            k = 0
+        else:
+            k += 1
+    return ys, ckpts
+
+
+def _run_eager(toks, p, cs, ss, keep):
+    """Eager decode of the same steps; returns per-step y and the states after the steps in keep."""
+    prm = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    csd, ssd = dev(cs), dev(ss)
+    ys, states = [], {}
+    for s, t in enumerate(toks):
+        y = mm.decode(dev(t["x"]), dev(t["z"]), dev(t["dt"]), dev(t["B"]), dev(t["C"]), *prm, csd, ssd)
+        ys.append(host(y))
+        if s in keep:
+            states[s] = (host(csd), host(ssd))
+    return ys, states
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_replay_equals_eager_decode(io, W):
+    """Every step's y and every committed checkpoint equal the eager decode bit for bit (the replay
+    performs the eager step's operations in the same order), including an early commit."""
+    Bs, d, N = 5, 200, 16
+    steps = 3 * W + 2
+    log(f"[replay] W={W} io={io} Bs={Bs} d={d} steps={steps}")
+    toks, p, cs, ss = _stream(70 + W, steps, Bs, d, N, io)
+    commit_at = {W + 1} if W > 2 else set()  # an explicit commit in the middle of the second window
+    yr, ck = _run_replay(toks, p, cs, ss, W, commit_at)
+    ye, st = _run_eager(toks, p, cs, ss, set(ck))
+    for s in range(steps):
+        assert np.array_equal(yr[s], ye[s]), f"step {s}: y differs from the eager decode"
+    assert ck, "no checkpoint was committed"
+    for s, (c1, s1) in ck.items():
+        assert np.array_equal(c1, st[s][0]) and np.array_equal(s1, st[s][1]), f"checkpoint after step {s}"
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_replay_vs_oracle(io):
+    W, Bs, d, N = 4, 7, 136, 16
+    toks, p, cs, ss = _stream(91, W, Bs, d, N, io)
+    yr, ck = _run_replay(toks, p, cs, ss, W)
+    ring = {k: np.stack([t[k] for t in toks]) for k in ("x", "dt", "B")}
+    for k in range(W):
+        y, csr, ssr = oracle.decode_replay(ring["x"], ring["dt"], ring["B"], k, toks[k]["z"], toks[k]["C"],
+                                           p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"], cs, ss)
+        assert_within(yr[k], y, io, f"replay step {k} y")
+    c1, s1 = ck[W - 1]
+    assert np.array_equal(c1, csr)
+    assert_within(s1, ssr, io, "replay checkpoint")
+
+
+def test_replay_7b_shape_window():
+    """The 7B-shaped decode (batch 256, d 8192) over one full window and a bit more."""
+    W, Bs, d, N = 4, 256, 8192, 16
+    steps = W + 1
+    toks, p, cs, ss = _stream(5, steps, Bs, d, N, "bf16")
+    yr, ck = _run_replay(toks, p, cs, ss, W)
+    ye, st = _run_eager(toks, p, cs, ss, {W - 1})
+    for s in range(steps):
+        assert np.array_equal(yr[s], ye[s]), s
+    assert np.array_equal(ck[W - 1][1], st[W - 1][1])

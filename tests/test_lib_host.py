@@ -164,3 +164,35 @@ def test_workspace_query_and_plan(lib):
     evs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     rc = lib.mamba_mixer_prefill_ex(*p, 2, 100, 64, 16, 4, 1, 32, 0, ws, 1 << 30, None, evs, 2)
     assert rc == MM_ERR_DIM
+
+
+def _replay(lib, ptrs, Bs=2, d=64, N=16, K=4, io=1, W=4, k=0, commit=0):
+    return lib.mamba_mixer_decode_replay(*ptrs, Bs, d, N, K, io, W, k, commit, None)
+
+
+def test_decode_replay_validation(lib):
+    p = _ptrs(13)
+    assert _replay(lib, p, N=8) == MM_ERR_UNSUPPORTED  # 4 lanes x 4 state entries per channel: N must be 16
+    assert _replay(lib, p, K=3) == MM_ERR_UNSUPPORTED
+    assert _replay(lib, p, W=5) == MM_ERR_DIM
+    assert _replay(lib, p, W=0) == MM_ERR_DIM
+    assert _replay(lib, p, k=4) == MM_ERR_DIM
+    assert _replay(lib, p, k=-1) == MM_ERR_DIM
+    assert _replay(lib, p, W=2, k=2) == MM_ERR_DIM
+    for i in range(13):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert _replay(lib, q) == MM_ERR_NULL, i
+    q = list(p)
+    q[2] = ctypes.c_void_p(A + 2)  # B_ring rows are read 4 bf16 at a time
+    assert _replay(lib, q) == MM_ERR_ALIGN
+    q = list(p)
+    q[11] = ctypes.c_void_p(p[11].value + 4)  # ssm_state needs 16 bytes
+    assert _replay(lib, q) == MM_ERR_ALIGN
+    q = list(p)
+    q[12] = q[3]  # y aliases z
+    assert _replay(lib, q) == MM_ERR_ALIAS
+    q = list(p)
+    q[11] = q[10]  # ssm_state overlaps conv_state
+    assert _replay(lib, q) == MM_ERR_ALIAS
+    assert _replay(lib, [ctypes.c_void_p(0)] * 13, Bs=0) == 0
