@@ -288,6 +288,31 @@ def bench_decode(args):
     del flush
     y_flushed_last = y.clone()
 
+    # (1b) replay decode over the same steps: windows of W steps, each window's ring is a
+    # view of four consecutive stacked steps; flushed per-kernel timing (graph below)
+    W = 4
+
+    def replay(s, stream=None):
+        w0 = (s // W) * W
+        return mm.decode_replay(stk["x"][w0:w0 + W], stk["dt"][w0:w0 + W], stk["B"][w0:w0 + W], stk["z"][s],
+                                stk["C"][s], *prm, csd, ssd, s - w0, y=y, stream=stream)
+
+    restore()
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s in range(steps):
+        flush.sum()
+        rev[s][0].record()
+        replay(s)
+        rev[s][1].record()
+    torch.cuda.synchronize()
+    rkern = [a.elapsed_time(b) for a, b in rev]
+    del flush
+    y_replay_flushed_last = y.clone()
+    if args.decode_flushed_only:  # profiling runs: only the flushed dispatches
+        return dict(Bs=Bs, d=d, N=N, K=K, steps=steps, kern_ms=float(np.mean(kern_ms)),
+                    replay_kern_ms=float(np.mean(rkern)))
+
     # (2) HIP graph of the 128 steps, replayed back to back
     restore()
     gstream = torch.cuda.Stream()
@@ -321,27 +346,7 @@ def bench_decode(args):
     eager_s = time.perf_counter() - t0
     y_eager_last = y.clone()
 
-    # (4) replay decode over the same steps: windows of W steps, each window's ring is a
-    # view of four consecutive stacked steps; flushed per-kernel timing, then a HIP graph
-    W = 4
-
-    def replay(s, stream=None):
-        w0 = (s // W) * W
-        return mm.decode_replay(stk["x"][w0:w0 + W], stk["dt"][w0:w0 + W], stk["B"][w0:w0 + W], stk["z"][s],
-                                stk["C"][s], *prm, csd, ssd, s - w0, y=y, stream=stream)
-
-    restore()
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for s in range(steps):
-        flush.sum()
-        rev[s][0].record()
-        replay(s)
-        rev[s][1].record()
-    torch.cuda.synchronize()
-    rkern = [a.elapsed_time(b) for a, b in rev]
-    del flush
-    replay_matches = bool(torch.equal(y, y_eager_last))
+    replay_matches = bool(torch.equal(y_replay_flushed_last, y_eager_last))
     restore()
     g2 = torch.cuda.CUDAGraph()
     with torch.cuda.stream(gstream):
@@ -438,6 +443,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode measurement only (for profiling)")
+    ap.add_argument("--decode-flushed-only", action="store_true",
+                    help="with --no-prefill: only the flushed-cache eager and replay decode dispatches "
+                         "(the kernel-trace and counter runs of the profiles)")
     ap.add_argument("--summarize-rocprof", metavar="CSV",
                     help="print a per-kernel table of a rocprofv3 kernel_stats.csv or counter_collection.csv "
                          "and exit")
@@ -474,7 +482,7 @@ def main():
     else:
         out = prefill_result(args)
     if not args.no_decode:
-        out["decode"] = decode_result(args)
+        out["decode"] = decode_result(args) if not args.decode_flushed_only else bench_decode(args)
     if not args.no_cpu_baseline:
         c = out["config"]
         out["cpu_baseline"] = cpu_baseline([c["L"]] * c["S"], c["d_inner"], c["d_state"], "bf16")
