@@ -213,6 +213,30 @@ int mamba_mixer_decode_replay(const void* x_ring, const void* dt_ring, const voi
                               void* y, int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype, int32_t W,
                               int32_t k, int32_t commit, void* stream);
 
+/*
+ * mamba_mixer_decode_replay_multi -- several steps of a replay window in one call, for
+ * speculative decoding (the ReplaySSM page, abstract: with the recent inputs kept,
+ * rolling back a speculation is a buffer-pointer move, and outputs of draft tokens can be
+ * checked without materialising intermediate states).
+ *
+ * Window steps 0..k1 are taken from the checkpoint; steps k0..k1 (0 <= k0 <= k1 < W <= 4)
+ * write their outputs; no state is written unless 0 <= commit_step <= k1, in which case the
+ * state after window step commit_step becomes the checkpoint (the accepted prefix of a
+ * draft; the caller then starts the next window at slot 0, with the rejected drafts
+ * dropped).  commit_step == -1 commits nothing.
+ *   x_ring, dt_ring, z_ring, y_ring [W, Bs, d] io   (y_ring out, slots k0..k1 written)
+ *   B_ring, C_ring                  [W, Bs, N] io
+ * Everything else, the alignment rules and the limits are those of
+ * mamba_mixer_decode_replay; the outputs and the committed state equal, bit for bit, those
+ * of the corresponding single-step calls.  k0 > k1, k1 >= W or commit_step outside -1..k1
+ * is MM_ERR_DIM.
+ */
+int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z_ring,
+                                    const void* C_ring, const float* A_log, const float* D, const float* dt_bias,
+                                    const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
+                                    void* y_ring, int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                                    int32_t W, int32_t k0, int32_t k1, int32_t commit_step, void* stream);
+
 /* Static text for a status code (never NULL).  Host only. */
 const char* mamba_mixer_status_string(int status);
 

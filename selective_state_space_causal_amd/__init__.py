@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_decode.restype = ctypes.c_int
     lib.mamba_mixer_decode_replay.argtypes = [P] * 13 + [i32, i32, i32, i32, i32, i32, i32, i32, P]
     lib.mamba_mixer_decode_replay.restype = ctypes.c_int
+    lib.mamba_mixer_decode_replay_multi.argtypes = [P] * 13 + [i32] * 9 + [P]
+    lib.mamba_mixer_decode_replay_multi.restype = ctypes.c_int
     lib.mamba_mixer_status_string.argtypes = [ctypes.c_int]
     lib.mamba_mixer_status_string.restype = ctypes.c_char_p
     lib.mamba_mixer_version.argtypes = []
@@ -248,3 +250,34 @@ def decode_replay(x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_decode_replay")
     return y
+
+
+def decode_replay_multi(x_ring, dt_ring, B_ring, z_ring, C_ring, A_log, D, dt_bias, conv_w, conv_b, conv_state,
+                        ssm_state, k0: int, k1: int, commit_step: int = -1, y_ring=None, stream=None):
+    """Window steps k0..k1 in one call (see ``mamba_mixer_decode_replay_multi``): outputs into
+    y_ring slots k0..k1, no state written unless commit_step >= 0.  Returns y_ring [W, Bs, d]."""
+    import torch
+
+    W, Bs, d = x_ring.shape
+    N = B_ring.shape[2]
+    io = x_ring.dtype
+    for t, n in ((x_ring, "x_ring"), (dt_ring, "dt_ring"), (z_ring, "z_ring")):
+        _check(t, (W, Bs, d), io, n)
+    _check(B_ring, (W, Bs, N), io, "B_ring")
+    _check(C_ring, (W, Bs, N), io, "C_ring")
+    _check(A_log, (d, N), torch.float32, "A_log")
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (conv_b, "conv_b")):
+        _check(t, (d,), torch.float32, n)
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(conv_state, (Bs, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (Bs, d, N), torch.float32, "ssm_state")
+    if y_ring is None:
+        y_ring = torch.empty((W, Bs, d), dtype=io, device=x_ring.device)
+    _check(y_ring, (W, Bs, d), io, "y_ring")
+    rc = load().mamba_mixer_decode_replay_multi(
+        _ptr(x_ring), _ptr(dt_ring), _ptr(B_ring), _ptr(z_ring), _ptr(C_ring), _ptr(A_log), _ptr(D), _ptr(dt_bias),
+        _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(ssm_state), _ptr(y_ring), Bs, d, N, CONV_K,
+        _io_code(x_ring), W, int(k0), int(k1), int(commit_step), _stream(stream))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_decode_replay_multi")
+    return y_ring

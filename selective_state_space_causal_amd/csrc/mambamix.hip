@@ -301,6 +301,65 @@ int check_prefill_sizes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, i
   return MM_OK;
 }
 
+// Validation and launch shared by the two replay entry points.  multi: z, C and y are
+// rings [W][Bs][...] indexed by window step; otherwise they are this step's [Bs][...].
+int replay_launch(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z, const void* C,
+                  const float* A_log, const float* D, const float* dt_bias, const float* conv_w, const float* conv_b,
+                  float* conv_state, float* ssm_state, void* y, int32_t Bs, int32_t d, int32_t N, int32_t K,
+                  int32_t io_dtype, int32_t W, int32_t k0, int32_t k1, int32_t cstep, bool multi, void* stream) {
+  int rc = check_common(Bs, d, N, K, io_dtype);
+  if (rc != MM_OK) return rc;
+  if (N != kReplayN) return MM_ERR_UNSUPPORTED;
+  if (W < 1 || W > kReplayMaxW || k0 < 0 || k0 > k1 || k1 >= W || cstep < -1 || cstep > k1) return MM_ERR_DIM;
+  if (Bs == 0 || d == 0) return MM_OK;
+  const void* req[] = {x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y};
+  for (const void* p : req)
+    if (p == nullptr) return MM_ERR_NULL;
+  const size_t es = io_dtype == MM_IO_BF16 ? 2 : 4;
+  const void* iop[] = {x_ring, dt_ring, z, y};
+  for (const void* p : iop)
+    if (!aligned(p, es)) return MM_ERR_ALIGN;
+  const void* vec[] = {B_ring, C};  // rows are read four elements at a time
+  for (const void* p : vec)
+    if (!aligned(p, 4 * es)) return MM_ERR_ALIGN;
+  const void* fp[] = {D, dt_bias, conv_b, conv_state};
+  for (const void* p : fp)
+    if (!aligned(p, 4)) return MM_ERR_ALIGN;
+  const void* f16[] = {A_log, conv_w, ssm_state};
+  for (const void* p : f16)
+    if (!aligned(p, 16)) return MM_ERR_ALIGN;
+  const size_t slot_d = static_cast<size_t>(Bs) * d * es, slot_n = static_cast<size_t>(Bs) * N * es;
+  const size_t nring = static_cast<size_t>(W) * slot_d, nbr = static_cast<size_t>(W) * slot_n;
+  const size_t ny = multi ? nring : slot_d, nz = multi ? nring : slot_d, nc = multi ? nbr : slot_n;
+  if (overlap(y, ny, x_ring, nring) || overlap(y, ny, dt_ring, nring) || overlap(y, ny, B_ring, nbr) ||
+      overlap(y, ny, z, nz) || overlap(y, ny, C, nc))
+    return MM_ERR_ALIAS;
+  if (overlap(conv_state, static_cast<size_t>(Bs) * d * kKS * 4, ssm_state, static_cast<size_t>(Bs) * d * N * 4))
+    return MM_ERR_ALIAS;
+  // z/C/y of step t sit at slot t - k0 of the pointers passed to the kernel
+  const int64_t zs = multi ? static_cast<int64_t>(Bs) * d : 0, cs = multi ? static_cast<int64_t>(Bs) * N : 0;
+  const int64_t off_d = multi ? static_cast<int64_t>(k0) * Bs * d : 0;
+  const int64_t off_n = multi ? static_cast<int64_t>(k0) * Bs * N : 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(cdiv(d, kBlock) * Bs));
+  if (io_dtype == MM_IO_BF16) {
+    using T = uint16_t;
+    hipLaunchKernelGGL((k_decode_replay<T>), grid, dim3(kBlock), 0, st, static_cast<const T*>(x_ring),
+                       static_cast<const T*>(dt_ring), static_cast<const T*>(B_ring),
+                       static_cast<const T*>(z) + off_d, static_cast<const T*>(C) + off_n, A_log, D, dt_bias,
+                       conv_w, conv_b, conv_state, ssm_state, static_cast<T*>(y) + off_d, Bs, d, k0, k1, cstep, zs,
+                       cs, zs);
+  } else {
+    using T = float;
+    hipLaunchKernelGGL((k_decode_replay<T>), grid, dim3(kBlock), 0, st, static_cast<const T*>(x_ring),
+                       static_cast<const T*>(dt_ring), static_cast<const T*>(B_ring),
+                       static_cast<const T*>(z) + off_d, static_cast<const T*>(C) + off_n, A_log, D, dt_bias,
+                       conv_w, conv_b, conv_state, ssm_state, static_cast<T*>(y) + off_d, Bs, d, k0, k1, cstep, zs,
+                       cs, zs);
+  }
+  return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace mm
 
@@ -473,50 +532,18 @@ int mamba_mixer_decode_replay(const void* x_ring, const void* dt_ring, const voi
                               const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
                               void* y, int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype, int32_t W,
                               int32_t k, int32_t commit, void* stream) {
-  int rc = check_common(Bs, d, N, K, io_dtype);
-  if (rc != MM_OK) return rc;
-  if (N != kReplayN) return MM_ERR_UNSUPPORTED;
-  if (W < 1 || W > kReplayMaxW || k < 0 || k >= W) return MM_ERR_DIM;
-  if (Bs == 0 || d == 0) return MM_OK;
-  const void* req[] = {x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y};
-  for (const void* p : req)
-    if (p == nullptr) return MM_ERR_NULL;
-  const size_t es = io_dtype == MM_IO_BF16 ? 2 : 4;
-  const void* iop[] = {x_ring, dt_ring, z, y};
-  for (const void* p : iop)
-    if (!aligned(p, es)) return MM_ERR_ALIGN;
-  const void* vec[] = {B_ring, C};  // rows are read four elements at a time
-  for (const void* p : vec)
-    if (!aligned(p, 4 * es)) return MM_ERR_ALIGN;
-  const void* fp[] = {D, dt_bias, conv_b, conv_state};
-  for (const void* p : fp)
-    if (!aligned(p, 4)) return MM_ERR_ALIGN;
-  const void* f16[] = {A_log, conv_w, ssm_state};
-  for (const void* p : f16)
-    if (!aligned(p, 16)) return MM_ERR_ALIGN;
-  const size_t ny = static_cast<size_t>(Bs) * d * es, nring = static_cast<size_t>(W) * ny;
-  const size_t nbr = static_cast<size_t>(W) * Bs * N * es, nc = static_cast<size_t>(Bs) * N * es;
-  if (overlap(y, ny, x_ring, nring) || overlap(y, ny, dt_ring, nring) || overlap(y, ny, B_ring, nbr) ||
-      overlap(y, ny, z, ny) || overlap(y, ny, C, nc))
-    return MM_ERR_ALIAS;
-  if (overlap(conv_state, static_cast<size_t>(Bs) * d * kKS * 4, ssm_state, static_cast<size_t>(Bs) * d * N * 4))
-    return MM_ERR_ALIAS;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(cdiv(d, kBlock) * Bs));
-  const int cm = (commit != 0 || k == W - 1) ? 1 : 0;
-  if (io_dtype == MM_IO_BF16) {
-    hipLaunchKernelGGL((k_decode_replay<uint16_t>), grid, dim3(kBlock), 0, st,
-                       static_cast<const uint16_t*>(x_ring), static_cast<const uint16_t*>(dt_ring),
-                       static_cast<const uint16_t*>(B_ring), static_cast<const uint16_t*>(z),
-                       static_cast<const uint16_t*>(C), A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
-                       static_cast<uint16_t*>(y), Bs, d, k, cm);
-  } else {
-    hipLaunchKernelGGL((k_decode_replay<float>), grid, dim3(kBlock), 0, st, static_cast<const float*>(x_ring),
-                       static_cast<const float*>(dt_ring), static_cast<const float*>(B_ring),
-                       static_cast<const float*>(z), static_cast<const float*>(C), A_log, D, dt_bias, conv_w,
-                       conv_b, conv_state, ssm_state, static_cast<float*>(y), Bs, d, k, cm);
-  }
-  return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
+  const int cstep = (commit != 0 || k == W - 1) ? k : -1;
+  return replay_launch(x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y,
+                       Bs, d, N, K, io_dtype, W, k, k, cstep, false, stream);
+}
+
+int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z_ring,
+                                    const void* C_ring, const float* A_log, const float* D, const float* dt_bias,
+                                    const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
+                                    void* y_ring, int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                                    int32_t W, int32_t k0, int32_t k1, int32_t commit_step, void* stream) {
+  return replay_launch(x_ring, dt_ring, B_ring, z_ring, C_ring, A_log, D, dt_bias, conv_w, conv_b, conv_state,
+                       ssm_state, y_ring, Bs, d, N, K, io_dtype, W, k0, k1, commit_step, true, stream);
 }
 
 }  // extern "C"

@@ -167,48 +167,58 @@ __global__ void __launch_bounds__(kBlock) k_decode_vec(
 // order, including the grouping of the readout sum), so a replayed step reproduces
 // the eager step bit for bit.
 //
+// The same kernel also serves speculative decoding: one call can emit the outputs of
+// several window steps (draft tokens) without writing any state, and commit the state
+// after any of them (the accepted prefix); a rejected draft is dropped by moving the
+// caller's ring position back.
+//
 // Layout: one lane per channel with its 16 state entries in registers, 256 channels
 // of one row per block.  x and dt of every window step are one coalesced load per
 // row; B and C of a row are the same for every lane, so they come through the
 // scalar unit; the state moves as four 16-byte loads per lane.  Few, wide vector
 // loads per (row, channel) keep this kernel on the HBM roofline where a
 // lanes-per-channel layout spent its time issuing small loads.  W <= 4, N = 16.
+// Window steps 0..k1 are taken from the checkpoint; steps k0..k1 write their output
+// (z, C and y of step t at slot t - k0 of the z/C/y arrays, slot strides zs, cs_, ys);
+// if 0 <= cstep <= k1 the state after step cstep becomes the checkpoint.
 template <typename IO>
 __global__ void __launch_bounds__(kBlock) k_decode_replay(
     const IO* __restrict__ x_ring, const IO* __restrict__ dt_ring, const IO* __restrict__ B_ring,
     const IO* __restrict__ z, const IO* __restrict__ C, const float* __restrict__ A_log,
     const float* __restrict__ D, const float* __restrict__ dt_bias, const float* __restrict__ conv_w,
     const float* __restrict__ conv_b, float* __restrict__ conv_state, float* __restrict__ ssm_state,
-    IO* __restrict__ y, int Bs, int d, int k, int commit) {
+    IO* __restrict__ y, int Bs, int d, int k0, int k1, int cstep, int64_t zs, int64_t cst, int64_t ys) {
   constexpr int NMAX = 16;
   constexpr int W = 4;  // ring slots read at most
   const int nb = (d + kBlock - 1) / kBlock;
   const int r = static_cast<int>(blockIdx.x / nb);
   const int c = static_cast<int>(blockIdx.x % nb) * kBlock + static_cast<int>(threadIdx.x);
-  // B of the window steps and C of step k: the same for every lane of the block (scalar
-  // loads, all issued before any store)
+  // B of the window steps and C of the output steps: the same for every lane of the
+  // block (scalar loads, all issued before any store)
   const int64_t bslot = static_cast<int64_t>(Bs) * NMAX;  // ring slot stride of B
-  float bv[W][NMAX], cvv[NMAX];
+  float bv[W][NMAX], cvv[W][NMAX];
 #pragma unroll
   for (int t = 0; t < W; ++t) {
-    const IO* bt = B_ring + (t <= k ? t : k) * bslot + static_cast<int64_t>(r) * NMAX;
+    const int tb = t <= k1 ? t : k1;
+    const int tc = (t >= k0 ? t : k0) - k0;
+    const IO* bt = B_ring + tb * bslot + static_cast<int64_t>(r) * NMAX;
+    const IO* ct = C + (tc <= k1 - k0 ? tc : k1 - k0) * cst + static_cast<int64_t>(r) * NMAX;
 #pragma unroll
     for (int v = 0; v < NMAX / 4; ++v) {
-      float o[4];
+      float o[4], oc[4];
       ld4_io(bt + 4 * v, o);  // rows are aligned to four elements
-      bv[t][4 * v] = o[0]; bv[t][4 * v + 1] = o[1]; bv[t][4 * v + 2] = o[2]; bv[t][4 * v + 3] = o[3];
-    }
-  }
+      ld4_io(ct + 4 * v, oc);
 #pragma unroll
-  for (int v = 0; v < NMAX / 4; ++v) {
-    float o[4];
-    ld4_io(C + static_cast<int64_t>(r) * NMAX + 4 * v, o);
-    cvv[4 * v] = o[0]; cvv[4 * v + 1] = o[1]; cvv[4 * v + 2] = o[2]; cvv[4 * v + 3] = o[3];
+      for (int e = 0; e < 4; ++e) {
+        bv[t][4 * v + e] = o[e];
+        cvv[t][4 * v + e] = oc[e];
+      }
+    }
   }
   if (c >= d) return;
   const int64_t slot = static_cast<int64_t>(Bs) * d;  // ring slot stride of x and dt
   const int64_t rc = static_cast<int64_t>(r) * d + c;
-  float h[NMAX], cs[kKS], xs[W], ds[W];
+  float h[NMAX], cs[kKS], xs[W], ds[W], zv[W];
   const float4* srow = reinterpret_cast<const float4*>(ssm_state + rc * NMAX);
 #pragma unroll
   for (int v = 0; v < NMAX / 4; ++v) {
@@ -218,11 +228,11 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
 #pragma unroll
   for (int m = 0; m < kKS; ++m) cs[m] = conv_state[rc * kKS + m];
 #pragma unroll
-  for (int t = 0; t < W; ++t) {  // slots past k are not read
-    xs[t] = (t <= k) ? ld_io(x_ring, t * slot + rc) : 0.0f;
-    ds[t] = (t <= k) ? ld_io(dt_ring, t * slot + rc) : 0.0f;
+  for (int t = 0; t < W; ++t) {  // slots past k1 are not read
+    xs[t] = (t <= k1) ? ld_io(x_ring, t * slot + rc) : 0.0f;
+    ds[t] = (t <= k1) ? ld_io(dt_ring, t * slot + rc) : 0.0f;
+    zv[t] = (t >= k0 && t <= k1) ? ld_io(z, (t - k0) * zs + rc) : 0.0f;
   }
-  const float zv = ld_io(z, rc);
   const float4 w = reinterpret_cast<const float4*>(conv_w)[c];
   const float cb = conv_b[c], dtb = dt_bias[c], Dc = D[c];
   float A2[NMAX];
@@ -236,16 +246,15 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
   }
   // X(m) = x of window step m (m >= 0) or checkpoint conv entry 3+m (m < 0)
   auto X = [&](int m) -> float { return m >= 0 ? xs[m] : cs[kKS + m]; };
-  float u = 0.0f;
 #pragma unroll
   for (int t = 0; t < W; ++t) {
-    if (t > k) break;  // k is uniform
+    if (t > k1) break;  // k0, k1 and cstep are uniform
     float xc = cb;
     xc = __builtin_fmaf(w.x, X(t - 3), xc);
     xc = __builtin_fmaf(w.y, X(t - 2), xc);
     xc = __builtin_fmaf(w.z, X(t - 1), xc);
     xc = __builtin_fmaf(w.w, xs[t], xc);
-    u = silu(xc);
+    const float u = silu(xc);
     const float delta = softplus(ds[t] + dtb);
     const float du = delta * u;
 #pragma unroll
@@ -253,30 +262,25 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
       const float a = exp2_hw(delta * A2[n]);
       h[n] = __builtin_fmaf(a, h[n], du * bv[t][n]);
     }
-  }
-  // readout of step k, summed as the four-lane decode sums it: per group of four
-  // entries in order, then (g0 + g1) + (g2 + g3)
-  float g[4];
+    if (t >= k0) {
+      // readout, summed as the four-lane decode sums it: per group of four entries in
+      // order, then (g0 + g1) + (g2 + g3)
+      float g[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    g[v] = 0.0f;
+      for (int v = 0; v < 4; ++v) {
+        g[v] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) g[v] = __builtin_fmaf(h[4 * v + e], cvv[4 * v + e], g[v]);
-  }
-  const float yp = (g[0] + g[1]) + (g[2] + g[3]);
-  st_io(y, rc, __builtin_fmaf(Dc, u, yp) * silu(zv));
-  if (commit) {  // the state after step k becomes the checkpoint
-    float* so = ssm_state + rc * NMAX;
+        for (int e = 0; e < 4; ++e) g[v] = __builtin_fmaf(h[4 * v + e], cvv[t][4 * v + e], g[v]);
+      }
+      const float yp = (g[0] + g[1]) + (g[2] + g[3]);
+      st_io(y, (t - k0) * ys + rc, __builtin_fmaf(Dc, u, yp) * silu(zv[t]));
+    }
+    if (t == cstep) {  // the state after step t becomes the checkpoint
+      float* so = ssm_state + rc * NMAX;
 #pragma unroll
-    for (int n = 0; n < NMAX; ++n) nt_store(h[n], so + n);
-    // new conv state = [X(k-2), X(k-1), X(k)]
+      for (int n = 0; n < NMAX; ++n) nt_store(h[n], so + n);
 #pragma unroll
-    for (int m = 0; m < kKS; ++m) {
-      float v = X(m - 2);
-      if (k == 1) v = X(m - 1);
-      if (k == 2) v = X(m);
-      if (k == 3) v = X(m + 1);
-      conv_state[rc * kKS + m] = v;
+      for (int m = 0; m < kKS; ++m) conv_state[rc * kKS + m] = X(t - 2 + m);  // [X(t-2), X(t-1), X(t)]
     }
   }
 }

@@ -111,3 +111,64 @@ def test_replay_7b_shape_window():
     for s in range(steps):
         assert np.array_equal(yr[s], ye[s]), s
     assert np.array_equal(ck[W - 1][1], st[W - 1][1])
+
+
+def _rings(toks, W, io):
+    def stack(key):
+        return dev(np.stack([t[key] for t in toks[:W]]))
+    return {k: stack(k) for k in ("x", "dt", "B", "z", "C")}
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_replay_multi_equals_eager_steps(io):
+    """One call emitting window steps k0..k1 equals the eager decode step by step, bit for bit,
+    with no state written unless a commit step is given (then the state after that step)."""
+    W, Bs, d, N = 4, 3, 300, 16
+    toks, p, cs, ss = _stream(33, W, Bs, d, N, io)
+    prm = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    ye, st = _run_eager(toks, p, cs, ss, set(range(W)))
+    R = _rings(toks, W, io)
+    for k0, k1, cstep in ((0, 3, -1), (1, 2, -1), (2, 2, 2), (0, 3, 1), (3, 3, 0), (0, 1, 1)):
+        csd, ssd = dev(cs), dev(ss)
+        y = torch.full((W, Bs, d), float("nan"), dtype=R["x"].dtype, device="cuda")
+        mm.decode_replay_multi(R["x"], R["dt"], R["B"], R["z"], R["C"], *prm, csd, ssd, k0, k1, cstep, y_ring=y)
+        yh = host(y)
+        for t in range(W):
+            if k0 <= t <= k1:
+                assert np.array_equal(yh[t], ye[t]), (k0, k1, cstep, t)
+            else:
+                assert np.all(np.isnan(yh[t])), f"slot {t} written outside {k0}..{k1}"
+        if (k0, k1) == (0, 3):  # and against the oracle's replay of each step
+            ring = {k: np.stack([t[k] for t in toks]) for k in ("x", "dt", "B")}
+            for t in range(W):
+                yo, _, _ = oracle.decode_replay(ring["x"], ring["dt"], ring["B"], t, toks[t]["z"], toks[t]["C"],
+                                                p["A_log"], p["D"], p["dt_bias"], p["conv_w"], p["conv_b"], cs, ss)
+                assert_within(yh[t], yo, io, f"multi step {t} vs oracle")
+        if cstep < 0:
+            assert np.array_equal(host(csd), cs) and np.array_equal(host(ssd), ss), "state written without commit"
+        else:
+            assert np.array_equal(host(csd), st[cstep][0]) and np.array_equal(host(ssd), st[cstep][1]), (k0, k1, cstep)
+
+
+def test_speculative_accept_prefix_and_continue():
+    """Draft four tokens, verify all four outputs in one call without writing state, accept two
+    (commit after step 1), then continue from the accepted prefix with two new tokens: every
+    output equals the eager decode that took exactly the accepted tokens."""
+    W, Bs, d, N = 4, 4, 256, 16
+    toks, p, cs, ss = _stream(44, 6, Bs, d, N, "bf16")
+    prm = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    draft = toks[:4]
+    R = _rings(draft, W, "bf16")
+    csd, ssd = dev(cs), dev(ss)
+    y = mm.decode_replay_multi(R["x"], R["dt"], R["B"], R["z"], R["C"], *prm, csd, ssd, 0, 3, -1)
+    ye, _ = _run_eager(draft, p, cs, ss, set())
+    for t in range(4):
+        assert np.array_equal(host(y[t]), ye[t]), t
+    # accept tokens 0 and 1: commit after window step 1 (a second call, outputs of step 1 again)
+    mm.decode_replay_multi(R["x"], R["dt"], R["B"], R["z"], R["C"], *prm, csd, ssd, 1, 1, 1)
+    # continue with two new tokens (toks 4 and 5) in a fresh window
+    accepted = toks[:2] + toks[4:6]
+    ye2, _ = _run_eager(accepted, p, cs, ss, set())
+    R2 = _rings(toks[4:6] + toks[4:6], W, "bf16")  # slots 0, 1 hold the new tokens
+    y2 = mm.decode_replay_multi(R2["x"], R2["dt"], R2["B"], R2["z"], R2["C"], *prm, csd, ssd, 0, 1, -1)
+    assert np.array_equal(host(y2[0]), ye2[2]) and np.array_equal(host(y2[1]), ye2[3])

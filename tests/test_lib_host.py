@@ -196,3 +196,29 @@ def test_decode_replay_validation(lib):
     q[11] = q[10]  # ssm_state overlaps conv_state
     assert _replay(lib, q) == MM_ERR_ALIAS
     assert _replay(lib, [ctypes.c_void_p(0)] * 13, Bs=0) == 0
+
+
+def _multi(lib, ptrs, Bs=2, d=64, N=16, K=4, io=1, W=4, k0=0, k1=3, cstep=-1):
+    return lib.mamba_mixer_decode_replay_multi(*ptrs, Bs, d, N, K, io, W, k0, k1, cstep, None)
+
+
+def test_decode_replay_multi_validation(lib):
+    p = _ptrs(13)
+    assert _multi(lib, p, N=12) == MM_ERR_UNSUPPORTED
+    assert _multi(lib, p, k0=2, k1=1) == MM_ERR_DIM
+    assert _multi(lib, p, k1=4) == MM_ERR_DIM
+    assert _multi(lib, p, W=2, k1=2) == MM_ERR_DIM
+    assert _multi(lib, p, cstep=4) == MM_ERR_DIM
+    assert _multi(lib, p, k1=2, cstep=3) == MM_ERR_DIM
+    assert _multi(lib, p, cstep=-2) == MM_ERR_DIM
+    for i in range(13):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert _multi(lib, q) == MM_ERR_NULL, i
+    q = list(p)
+    q[4] = ctypes.c_void_p(A + 2)  # C_ring rows are read 4 bf16 at a time
+    assert _multi(lib, q) == MM_ERR_ALIGN
+    q = list(p)
+    q[12] = ctypes.c_void_p(p[3].value + 64)  # y_ring overlaps z_ring
+    assert _multi(lib, q) == MM_ERR_ALIAS
+    assert _multi(lib, [ctypes.c_void_p(0)] * 13, d=0) == 0
