@@ -214,6 +214,97 @@ def bench_prefill(args):
                 chunk_len=plan["chunk_len"], engine=plan["engine_name"])
 
 
+def _time_prefill_call(mm, st, lens, d, N, reps, chunk_len=0, events=True):
+    """Mean event time (ms) of whole prefill calls on resident inputs (the library launches on torch's
+    current stream), states zeroed before each call; the first call is a warm-up."""
+    import torch
+
+    times = []
+    for r in range(reps + 1):
+        st["cs"].zero_()
+        st["ss"].zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mm.prefill(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"], st["dt_bias"],
+                   st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], y=st["y"], chunk_len=chunk_len)
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:
+            times.append(e0.elapsed_time(e1))
+    return float(np.mean(times))
+
+
+def bench_other_prefills(args):
+    """Prefill rates of the other configurations (context; the headline is the 130m step):
+    the packed 1.4B-shaped stream, the same sequences one call each (PackMamba's comparison),
+    one 8192-token chunk of the 2.8B-shaped long sequence, and that sequence's 16 chunk calls."""
+    import torch
+
+    import selective_state_space_causal_amd as mm
+    from selective_state_space_causal_amd import inputs
+
+    out = {}
+
+    def resident(lens, d, N, seed=0):
+        tok, p, cs, ss, cu = make_prefill_set(seed, lens, d, N, "bf16")
+        st = {k: dev(v) for k, v in tok.items()}
+        st.update({k: dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")})
+        st.update(cu=dev(cu), cs=dev(cs), ss=dev(ss))
+        st["y"] = torch.empty((int(sum(lens)), d), dtype=torch.bfloat16, device="cuda")
+        return st
+
+    # 1.4B-shaped packed stream, and the same sequences one call each
+    lens = inputs.packed_lengths(0, 16384, 128, 4096).tolist()
+    d = 4096
+    st = resident(lens, d, 16)
+    T = int(sum(lens))
+    ms = _time_prefill_call(mm, st, lens, d, 16, reps=5)
+    plan = mm.plan(len(lens), T, d, 16)
+    sep_ms = 0.0
+    off = 0
+    for L in lens:  # one call per sequence, each on its own slice of the same inputs
+        sub = dict(st)
+        for k in ("x", "z", "dt", "B", "C", "y"):
+            sub[k] = st[k][off:off + L]
+        sub["cu"] = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        sub["cs"], sub["ss"] = st["cs"][:1].clone(), st["ss"][:1].clone()
+        sep_ms += _time_prefill_call(mm, sub, [L], d, 16, reps=3)
+        off += L
+    out["m1p4b_packed"] = dict(
+        workload=f"1.4B-shaped packed prefill: {len(lens)} sequences, lengths U[128,4096] to T={T}, d_inner {d}",
+        tokens_per_s=round(T / (ms * 1e-3), 1), ms=round(ms, 4), engine=plan["engine_name"],
+        chunk_len=plan["chunk_len"], kernels=plan["kernels"],
+        separate_calls_ms=round(sep_ms, 4), packed_speedup_over_separate=round(sep_ms / ms, 3))
+    del st
+    # 2.8B-shaped long sequence: 16 chunk calls of 8192 tokens carrying the state (for timing,
+    # every call takes the same 8192 resident input tokens; the parity tests use distinct ones)
+    d, L, nch = 5120, 8192, 16
+    st = resident([L], d, 16)
+    plan = mm.plan(1, L, d, 16)
+    times = []
+    st["cs"].zero_()
+    st["ss"].zero_()
+    for k in range(nch + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mm.prefill(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"], st["dt_bias"],
+                   st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], y=st["y"])
+        e1.record()
+        torch.cuda.synchronize()
+        if k > 0:  # the first call is a warm-up
+            times.append(e0.elapsed_time(e1))
+    tot = float(np.sum(times))
+    out["m2p8b_long_chunked"] = dict(
+        workload=f"2.8B-shaped long prefill: 1 sequence of {L * nch} tokens in {nch} calls of {L}, d_inner {d}, "
+                 "state carried between calls",
+        tokens_per_s=round(L * nch / (tot * 1e-3), 1), ms_total=round(tot, 3),
+        ms_per_chunk_call=round(tot / nch, 4), engine=plan["engine_name"], chunk_len=plan["chunk_len"],
+        kernels=plan["kernels"])
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(args):
     """Batch-256 decode: a 512-token prefill initialises the states, then 128 decode steps.
 
@@ -393,9 +484,28 @@ def cpu_baseline(lens, d, N, io):
         runs += 1
     el = time.perf_counter() - t0
     cpu = time.process_time() - c0
+    # one thread, on one sequence of the workload (the oracle's cost is linear in tokens x channels)
+    oracle.threads(1)
+    t1 = time.perf_counter()
+    L0 = lens[0]
+    oracle.prefill(tok["x"][:L0], tok["z"][:L0], tok["dt"][:L0], tok["B"][:L0], tok["C"][:L0], p["A_log"], p["D"],
+                   p["dt_bias"], p["conv_w"], p["conv_b"], np.array([0, L0], dtype=np.int32), cs[:1], ss[:1])
+    el1 = time.perf_counter() - t1
+    oracle.threads(threads)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=round(runs * T / el, 1), unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{runs} full prefills of the bench workload ({len(lens)} x {lens[0]} tokens, d={d}, N={N}), "
-                       f"fp64, {el:.2f} s wall, {cpu:.1f} s CPU on {threads} threads (input widening to fp64 included)")
+                       f"fp64, {el:.2f} s wall, {cpu:.1f} s CPU on {threads} threads (input widening to fp64 included)",
+                single_thread=dict(value=round(L0 / el1, 1), unit="tokens/s",
+                                   sample=f"one sequence of {L0} tokens, d={d}, N={N}, {el1:.2f} s"),
+                cpu_model=model)
 
 
 def copy_calibration():
@@ -443,6 +553,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode measurement only (for profiling)")
+    ap.add_argument("--no-other-prefills", action="store_true",
+                    help="skip the context prefill rates of the other configurations")
     ap.add_argument("--decode-flushed-only", action="store_true",
                     help="with --no-prefill: only the flushed-cache eager and replay decode dispatches "
                          "(the kernel-trace and counter runs of the profiles)")
@@ -481,6 +593,8 @@ def main():
         out = dict(metric=METRIC, note="decode-only diagnostic run (--no-prefill); no headline value")
     else:
         out = prefill_result(args)
+    if not args.no_prefill and not args.no_other_prefills:
+        out["other_prefills"] = bench_other_prefills(args)
     if not args.no_decode:
         out["decode"] = decode_result(args) if not args.decode_flushed_only else bench_decode(args)
     if not args.no_cpu_baseline:
