@@ -59,6 +59,27 @@ def test_state_sizes(N, engine):
     _check_prefill(case, 48, f"N={N}", engine)
 
 
+@pytest.mark.parametrize("engine", [0] + ENGINES)
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_many_short_sequences(io, engine):
+    """Hundreds of short sequences (lengths 0..20, so many shorter than the conv window) with a
+    ragged channel count: every sequence starts from its own slot, and empty ones stay untouched."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(0, 21, size=300).tolist()
+    case = make_prefill(17, lens, 48, 16, io)
+    _check_prefill(case, 0, f"300 short sequences io={io}", engine)
+
+
+def test_auto_plan_picks_lane_engine_for_many_sequences():
+    """4096 sequences x 64 channels reach the lane engine's wave threshold: the automatic plan
+    uses it, and the result matches the oracle."""
+    rng = np.random.default_rng(23)
+    lens = rng.integers(1, 9, size=4096).tolist()
+    case = make_prefill(23, lens, 64, 16, "bf16")
+    assert mm.plan(case["S"], case["T"], 64, 16)["engine_name"] == "lane"
+    _check_prefill(case, 0, "4096 sequences (auto -> lane)", 0)
+
+
 @pytest.mark.parametrize("engine", ENGINES)
 def test_sequences_ending_on_chunk_boundaries(engine):
     lens = [64, 64, 128, 1, 63, 64, 1, 16, 17, 15]
