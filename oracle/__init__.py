@@ -50,6 +50,8 @@ def _load():
         lib.oracle_prefill.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [i32, i32, i32, i32] + [P] * 13 + [ctypes.c_int]
         lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_prefill_backward.argtypes = [i64, i32, i32, i32, i32] + [P] * 26
+        lib.oracle_prefill_backward.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [ctypes.c_int]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -96,6 +98,35 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
     if rc != 0:
         raise ValueError("oracle_prefill rejected its arguments (cu_seqlens or dims)")
     return y, cs, ss
+
+
+def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, dy):
+    """Gradients of a loss with dL/dy = dy (and no dependence on the final states) with respect to
+    every prefill input and the initial states (reverse mode of ``prefill``; see
+    ``oracle_prefill_backward`` in mamba_oracle.c).  Returns a dict of float64 arrays: dx, dz, ddt
+    [T, d]; dB, dC [T, N]; dA_log [d, N]; dD, ddt_bias, dconv_b [d]; dconv_w [d, K];
+    dconv_state [S, d, K-1]; dssm_state [S, d, N]."""
+    x, z, dt, B, C, dy = (as_f64(a) for a in (x, z, dt, B, C, dy))
+    A_log, D, dt_bias, conv_w, conv_b = (as_f64(a) for a in (A_log, D, dt_bias, conv_w, conv_b))
+    T, d = x.shape
+    N = B.shape[1]
+    K = conv_w.shape[1]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    S = cu.shape[0] - 1
+    cs = as_f64(conv_state).reshape(S, d, K - 1).copy()
+    ss = as_f64(ssm_state).reshape(S, d, N).copy()
+    out = dict(dx=np.zeros((T, d)), dz=np.zeros((T, d)), ddt=np.zeros((T, d)), dB=np.zeros((T, N)),
+               dC=np.zeros((T, N)), dA_log=np.zeros((d, N)), dD=np.zeros(d), ddt_bias=np.zeros(d),
+               dconv_w=np.zeros((d, K)), dconv_b=np.zeros(d), dconv_state=np.zeros((S, d, K - 1)),
+               dssm_state=np.zeros((S, d, N)))
+    rc = _load().oracle_prefill_backward(
+        T, S, d, N, K, _p(x), _p(z), _p(dt), _p(B), _p(C), _p(A_log), _p(D), _p(dt_bias), _p(conv_w), _p(conv_b),
+        cu.ctypes.data_as(ctypes.c_void_p), _p(cs), _p(ss), _p(dy),
+        *[_p(out[k]) for k in ("dx", "dz", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dconv_w", "dconv_b",
+                               "dconv_state", "dssm_state")])
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward rejected its arguments")
+    return out
 
 
 def decode(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, nthreads: int = 0):

@@ -368,3 +368,67 @@ def test_oracle_bf16_inputs_are_widened_exactly(oracle_lib):
     # RNE: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> rounds to even (1.0)
     assert inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(np.array([1.0 + 2.0 ** -8], np.float32)))[0] == 1.0
     assert inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(np.array([1.0 + 3 * 2.0 ** -8], np.float32)))[0] == 1.0 + 2.0 ** -6
+
+
+# --- backward: reverse mode pinned by central finite differences of the forward oracle -------
+
+def _fd_case(seed, lens, d, N, K=4):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    S = len(lens)
+    f = dict(x=rng.standard_normal((T, d)), z=rng.standard_normal((T, d)), dt=rng.standard_normal((T, d)),
+             B=rng.standard_normal((T, N)), C=rng.standard_normal((T, N)),
+             A_log=np.log(rng.uniform(0.5, 3.0, (d, N))), D=rng.standard_normal(d),
+             dt_bias=rng.uniform(-2.0, 0.5, d), conv_w=rng.uniform(-0.5, 0.5, (d, K)),
+             conv_b=rng.uniform(-0.5, 0.5, d), conv_state=rng.standard_normal((S, d, K - 1)),
+             ssm_state=rng.standard_normal((S, d, N)))
+    return f, inputs.cu_from_lengths(lens), rng.standard_normal((T, d))
+
+
+def _loss(oracle_lib, f, cu, dy):
+    y, _, _ = oracle_lib.prefill(f["x"], f["z"], f["dt"], f["B"], f["C"], f["A_log"], f["D"], f["dt_bias"],
+                                 f["conv_w"], f["conv_b"], cu, f["conv_state"], f["ssm_state"])
+    return float(np.sum(y * dy))
+
+
+@pytest.mark.parametrize("lens,d,N,seed", [([5, 3], 2, 3, 0), ([1, 0, 6, 2], 3, 2, 1)])
+def test_oracle_backward_matches_finite_differences(oracle_lib, lens, d, N, seed):
+    """Every gradient of the reverse-mode oracle against central differences of the forward oracle
+    (step 1e-6, loss sum(y * dy)): a dropped term, a wrong sign or an index slip in any adjoint fails."""
+    f, cu, dy = _fd_case(seed, lens, d, N)
+    g = oracle_lib.prefill_backward(f["x"], f["z"], f["dt"], f["B"], f["C"], f["A_log"], f["D"], f["dt_bias"],
+                                    f["conv_w"], f["conv_b"], cu, f["conv_state"], f["ssm_state"], dy)
+    eps = 1e-6
+    names = {"x": "dx", "z": "dz", "dt": "ddt", "B": "dB", "C": "dC", "A_log": "dA_log", "D": "dD",
+             "dt_bias": "ddt_bias", "conv_w": "dconv_w", "conv_b": "dconv_b", "conv_state": "dconv_state",
+             "ssm_state": "dssm_state"}
+    for key, gname in names.items():
+        num = np.zeros_like(f[key])
+        flat = f[key].reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = _loss(oracle_lib, f, cu, dy)
+            flat[i] = old - eps
+            lm = _loss(oracle_lib, f, cu, dy)
+            flat[i] = old
+            num.reshape(-1)[i] = (lp - lm) / (2 * eps)
+        ana = g[gname]
+        scale = max(1.0, float(np.max(np.abs(num))))
+        assert np.max(np.abs(ana - num)) <= 2e-6 * scale, f"{gname}: max diff {np.max(np.abs(ana - num)):.3g}"
+
+
+def test_oracle_backward_separates_sequences(oracle_lib):
+    """A gradient flowing into one sequence's outputs leaves every other sequence's input
+    gradients exactly zero (no adjoint crosses a cu_seqlens boundary)."""
+    lens = [4, 7, 3]
+    f, cu, dy = _fd_case(9, lens, 3, 4)
+    dy[:] = 0.0
+    dy[cu[1]:cu[2]] = 1.0  # only the middle sequence's outputs matter
+    g = oracle_lib.prefill_backward(f["x"], f["z"], f["dt"], f["B"], f["C"], f["A_log"], f["D"], f["dt_bias"],
+                                    f["conv_w"], f["conv_b"], cu, f["conv_state"], f["ssm_state"], dy)
+    for k in ("dx", "dz", "ddt", "dB", "dC"):
+        assert np.all(g[k][:cu[1]] == 0.0) and np.all(g[k][cu[2]:] == 0.0), k
+        assert np.any(g[k][cu[1]:cu[2]] != 0.0), k
+    for k in ("dconv_state", "dssm_state"):
+        assert np.all(g[k][0] == 0.0) and np.all(g[k][2] == 0.0) and np.any(g[k][1] != 0.0), k
