@@ -305,6 +305,57 @@ def bench_other_prefills(args):
     return out
 
 
+def bench_backward(args):
+    """Prefill backward of the 130M training shape (8 x 2048 tokens, d 1536, bf16 io): every kernel
+    timed with HIP events over several calls on resident inputs, and the whole call."""
+    import torch
+
+    import selective_state_space_causal_amd as mm
+    from selective_state_space_causal_amd import inputs
+
+    S, L, d, N = 8, 2048, 1536, 16
+    T = S * L
+    tok, p, cs, ss, cu = make_prefill_set(0, [L] * S, d, N, "bf16")
+    st = {k: dev(v) for k, v in tok.items()}
+    st.update({k: dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")})
+    st.update(cu=dev(cu), cs=dev(cs), ss=dev(ss), dy=dev(inputs.grad_output(0, T, d, "bf16")))
+    plan = mm.backward_plan(S, T, d, N)
+    nk = plan["kernels"]
+    ws = torch.empty(plan["workspace"], dtype=torch.uint8, device="cuda")
+    out = None
+    names = ["k_row_ckpt", "k_row_bwd", "k_bwd_sum_bc", "k_bwd_sum_params"]
+    hev = HipEvents(nk + 1)
+    reps = 10
+    kern = {n: [] for n in names}
+    whole = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = mm.prefill_backward(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"],
+                                  st["dt_bias"], st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], st["dy"],
+                                  out=out, workspace=ws, events=hev.ev)
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:  # the first call is a warm-up
+            whole.append(e0.elapsed_time(e1))
+            for i, n in enumerate(names):
+                kern[n].append(hev.ms(i, i + 1))
+    hev.close()
+    ms = float(np.mean(whole))
+    kms = {n: float(np.mean(v)) for n, v in kern.items()}
+    io_bytes = T * d * 2 * 4 + T * d * 2 * 3 + 2 * T * N * 2 * 2  # x, z, dt, dy in; dx, dz, ddt out; B, C in, dB, dC out
+    del st, ws, out
+    torch.cuda.empty_cache()
+    return dict(
+        workload=f"mamba-130m-shaped layer backward: {S} packed sequences x {L} tokens, d_inner {d}, d_state {N}, "
+                 "conv 4, bf16 io, fp32 state; gradients of all inputs, parameters and initial states",
+        tokens_per_s=round(T / (ms * 1e-3), 1), ms=round(ms, 4),
+        kernels_ms={n: round(v, 4) for n, v in kms.items()},
+        workspace_bytes=plan["workspace"],
+        io_bytes=io_bytes, io_GBs=round(io_bytes / (ms * 1e-3) / 1e9, 1),
+        note="checkpoint pass (forward states before every 16-token block), reverse pass, fixed-order sums")
+
+
 def bench_decode(args):
     """Batch-256 decode: a 512-token prefill initialises the states, then 128 decode steps.
 
@@ -555,6 +606,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="decode measurement only (for profiling)")
     ap.add_argument("--no-other-prefills", action="store_true",
                     help="skip the context prefill rates of the other configurations")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward timing")
     ap.add_argument("--decode-flushed-only", action="store_true",
                     help="with --no-prefill: only the flushed-cache eager and replay decode dispatches "
                          "(the kernel-trace and counter runs of the profiles)")
@@ -595,6 +647,8 @@ def main():
         out = prefill_result(args)
     if not args.no_prefill and not args.no_other_prefills:
         out["other_prefills"] = bench_other_prefills(args)
+    if not args.no_prefill and not args.no_backward:
+        out["backward"] = bench_backward(args)
     if not args.no_decode:
         out["decode"] = decode_result(args) if not args.decode_flushed_only else bench_decode(args)
     if not args.no_cpu_baseline:

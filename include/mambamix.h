@@ -237,6 +237,53 @@ int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, con
                                     void* y_ring, int32_t Bs, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
                                     int32_t W, int32_t k0, int32_t k1, int32_t commit_step, void* stream);
 
+/*
+ * mamba_mixer_prefill_backward -- the gradients of a loss L with respect to every input of
+ * a prefill call, its parameters and its initial states, given dy = dL/dy (L does not
+ * depend on the final states).  This is the reverse mode of the step above, by the chain
+ * rule, sequence by sequence: no gradient crosses a cu_seqlens boundary (PackMamba page,
+ * abstract: packed sequences do not influence one another).  Training with packed
+ * sequences needs it; the pages describe the forward step only, so the gradients follow
+ * from that step alone.
+ *
+ * Inputs, with the layouts and dtypes of mamba_mixer_prefill (read only):
+ *   x, z, dt [T, d], B, C [T, N] (io), A_log, D, dt_bias, conv_w, conv_b (f32),
+ *   cu_seqlens [S+1], conv_state [S, d, K-1] and ssm_state [S, d, N]: the INITIAL states
+ *   (those a forward call reads; the backward does not change them)
+ *   dy            [T, d]      io     dL/dy
+ * Outputs (all overwritten):
+ *   dx, dz, ddt   [T, d]      io     ddt is dL/d(dt) (equal to the share of dt_bias)
+ *   dB, dC        [T, N]      io     summed over channels
+ *   dA_log        [d, N]      f32
+ *   dD, ddt_bias, dconv_b [d] f32
+ *   dconv_w       [d, K]      f32
+ *   dconv_state   [S, d, K-1] f32    dL/d(initial conv state)
+ *   dssm_state    [S, d, N]   f32    dL/d(initial SSM state)
+ *   workspace     device scratch of at least mamba_mixer_prefill_backward_workspace_bytes
+ *                 bytes, 256-byte aligned (about 64 * (T/16 + S) * d + 128 * T * N * d/16
+ *                 bytes: the state before every 16-token block, and per-16-channel partial
+ *                 sums of dB and dC)
+ *   events, n_events   optional, as in mamba_mixer_prefill_ex: events[i] is recorded before
+ *                 the i-th kernel and events[n] after the last; n is the kernel count
+ *                 mamba_mixer_prefill_backward_plan reports (4, or 1 when S == 0).
+ * The sums over channels, tokens and sequences are taken in a fixed order: the results do
+ * not vary from run to run.  An empty sequence gets zero state gradients.  d == 0 is a
+ * successful no-op; with T == 0 the parameter and state gradients are zeros.  Arrays of
+ * zero bytes may be NULL.  Outputs overlapping an input or one another are MM_ERR_ALIAS.
+ */
+int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                 const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
+                                 const float* conv_b, const int32_t* cu_seqlens, const float* conv_state,
+                                 const float* ssm_state, const void* dy, void* dx, void* dz, void* ddt, void* dB,
+                                 void* dC, float* dA_log, float* dD, float* ddt_bias, float* dconv_w, float* dconv_b,
+                                 float* dconv_state, float* dssm_state, int32_t S, int64_t T, int32_t d, int32_t N,
+                                 int32_t K, int32_t io_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events, int32_t n_events);
+/* Workspace bytes and kernel count of mamba_mixer_prefill_backward for these sizes (host only;
+ * either output pointer may be NULL).  Returns MM_OK or the size error the call would return. */
+int mamba_mixer_prefill_backward_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, size_t* workspace_out,
+                                      int32_t* kernels_out);
+size_t mamba_mixer_prefill_backward_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
 /* Static text for a status code (never NULL).  Host only. */
 const char* mamba_mixer_status_string(int status);
 

@@ -21,6 +21,7 @@
 #include <cmath>
 
 #include "mambamix.h"
+#include "mm_backward.h"
 #include "mm_decode.h"
 #include "mm_device.h"
 #include "mm_prefill.h"
@@ -200,7 +201,7 @@ void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st,
     evs.mark(st);
     hipLaunchKernelGGL((k_row<IO, false>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias,
                        a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d,
-                       a.N, p.Lc, whole);
+                       a.N, p.Lc, whole, nullptr);
     evs.mark(st);
     const int64_t q = static_cast<int64_t>(a.d) * kRow;
     hipLaunchKernelGGL((k_carry<kRow>), dim3(static_cast<unsigned>(cdiv(q, kBlock))), dim3(kBlock), 0, st, cw,
@@ -209,7 +210,7 @@ void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st,
   evs.mark(st);
   hipLaunchKernelGGL((k_row<IO, true>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w,
                      a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d, a.N, p.Lc,
-                     whole);
+                     whole, nullptr);
 }
 
 template <typename IO, int NMAX>
@@ -359,6 +360,93 @@ int replay_launch(const void* x_ring, const void* dt_ring, const void* B_ring, c
   }
   return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }
+
+// ---------------------------------------------------------------- prefill backward
+
+// The reverse pass gives each workgroup row every G-th sequence; G is chosen for
+// about this many workgroups (8 per CU).
+constexpr int64_t kBwdWgs = 2048;
+
+struct BwdPlan {
+  int nchb;      // 16-channel blocks
+  int G;         // workgroup rows of the reverse pass (0 when S == 0)
+  int64_t rows;  // checkpoint rows: ceil(T / 16) + S
+  size_t off_ckpt, off_pbc, off_prm, total;
+  int kernels;
+};
+
+int make_bwd_plan(BwdPlan& p, int64_t S, int64_t T, int d, int N) {
+  p = BwdPlan{};
+  p.nchb = static_cast<int>(cdiv(d, kRowChans));
+  p.rows = cdiv(T, kRow) + S;
+  int64_t g = cdiv(kBwdWgs, p.nchb > 0 ? p.nchb : 1);
+  if (g > S) g = S;
+  p.G = static_cast<int>(g);
+  size_t off = 0;
+  p.off_ckpt = off; off += align256(static_cast<size_t>(p.rows) * d * kRow * sizeof(float));
+  p.off_pbc = off; off += align256(static_cast<size_t>(p.nchb) * 2 * T * N * sizeof(float));
+  p.off_prm = off; off += align256(static_cast<size_t>(p.G) * kPrm * d * sizeof(float));
+  p.total = off;
+  p.kernels = S > 0 ? 4 : 1;
+  if (row_grid(S, d) > INT32_MAX || cdiv(2 * T * N, kBlock) > INT32_MAX) return MM_ERR_DIM;
+  return MM_OK;
+}
+
+struct BwdArgs {
+  const void *x, *z, *dt, *B, *C, *dy;
+  const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
+  const int32_t* cu;
+  const float *conv_state, *ssm_state;
+  void *dx, *dz, *ddt, *dB, *dC;
+  float *dA_log, *dD, *ddt_bias, *dconv_w, *dconv_b, *dconv_state, *dssm_state;
+  int S;
+  int64_t T;
+  int d, N;
+};
+
+template <typename IO>
+int launch_backward(const BwdPlan& p, const BwdArgs& a, char* ws, hipStream_t st, StageEvents evs) {
+  float* ckpt = reinterpret_cast<float*>(ws + p.off_ckpt);
+  float* pbc = reinterpret_cast<float*>(ws + p.off_pbc);
+  float* pprm = reinterpret_cast<float*>(ws + p.off_prm);
+  const IO* xi = static_cast<const IO*>(a.x);
+  const IO* zi = static_cast<const IO*>(a.z);
+  const IO* di = static_cast<const IO*>(a.dt);
+  const IO* Bi = static_cast<const IO*>(a.B);
+  const IO* Ci = static_cast<const IO*>(a.C);
+  const dim3 block(kRowThreads);
+  if (a.S > 0) {
+    // 1. checkpoints: the forward's states before every 16-token block
+    evs.mark(st);
+    hipLaunchKernelGGL((k_row<IO, false, true>), dim3(static_cast<unsigned>(row_grid(a.S, a.d))), block, 0, st, xi,
+                       zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu,
+                       const_cast<float*>(a.conv_state), const_cast<float*>(a.ssm_state), static_cast<IO*>(nullptr),
+                       CarryWs{}, a.S, a.T, a.d, a.N, a.T + 1, 1, ckpt);
+    // 2. the reverse pass
+    evs.mark(st);
+    hipLaunchKernelGGL((k_row_bwd<IO>), dim3(static_cast<unsigned>(row_grid(p.G, a.d))), block, 0, st, xi, zi, di, Bi,
+                       Ci, static_cast<const IO*>(a.dy), a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu,
+                       a.conv_state, ckpt, static_cast<IO*>(a.dx), static_cast<IO*>(a.dz), static_cast<IO*>(a.ddt),
+                       a.dconv_state, a.dssm_state, pbc, pprm, a.S, a.T, a.d, a.N, p.G);
+    // 3. dB, dC
+    evs.mark(st);
+    const int64_t TN = a.T * a.N;
+    const int64_t nbc = cdiv(2 * TN, kBlock);
+    hipLaunchKernelGGL((k_bwd_sum_bc<IO>), dim3(static_cast<unsigned>(nbc > 0 ? nbc : 1)), dim3(kBlock), 0, st, pbc,
+                       static_cast<IO*>(a.dB), static_cast<IO*>(a.dC), TN, p.nchb);
+  }
+  // 4. parameter gradients (zeros when there is no sequence)
+  evs.mark(st);
+  hipLaunchKernelGGL(k_bwd_sum_params, dim3(static_cast<unsigned>(cdiv(static_cast<int64_t>(kPrm) * a.d, kBlock))),
+                     dim3(kBlock), 0, st, pprm, a.dA_log, a.dD, a.ddt_bias, a.dconv_b, a.dconv_w, a.d, a.N, p.G);
+  evs.mark(st);
+  return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
+}
+
+struct Span {
+  const void* p;
+  size_t n;
+};
 
 }  // namespace
 }  // namespace mm
@@ -544,6 +632,82 @@ int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, con
                                     int32_t W, int32_t k0, int32_t k1, int32_t commit_step, void* stream) {
   return replay_launch(x_ring, dt_ring, B_ring, z_ring, C_ring, A_log, D, dt_bias, conv_w, conv_b, conv_state,
                        ssm_state, y_ring, Bs, d, N, K, io_dtype, W, k0, k1, commit_step, true, stream);
+}
+
+int mamba_mixer_prefill_backward_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, size_t* workspace_out,
+                                      int32_t* kernels_out) {
+  int rc = check_prefill_sizes(S, T, d, N, K, MM_IO_F32);
+  if (rc != MM_OK) return rc;
+  BwdPlan p{};
+  if (d > 0) {
+    rc = make_bwd_plan(p, S, T, d, N);
+    if (rc != MM_OK) return rc;
+  }
+  if (workspace_out) *workspace_out = p.total;
+  if (kernels_out) *kernels_out = p.kernels;
+  return MM_OK;
+}
+
+size_t mamba_mixer_prefill_backward_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K) {
+  size_t w = 0;
+  if (mamba_mixer_prefill_backward_plan(S, T, d, N, K, &w, nullptr) != MM_OK) return 0;
+  return w;
+}
+
+int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                 const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
+                                 const float* conv_b, const int32_t* cu_seqlens, const float* conv_state,
+                                 const float* ssm_state, const void* dy, void* dx, void* dz, void* ddt, void* dB,
+                                 void* dC, float* dA_log, float* dD, float* ddt_bias, float* dconv_w, float* dconv_b,
+                                 float* dconv_state, float* dssm_state, int32_t S, int64_t T, int32_t d, int32_t N,
+                                 int32_t K, int32_t io_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events, int32_t n_events) {
+  int rc = check_prefill_sizes(S, T, d, N, K, io_dtype);
+  if (rc != MM_OK) return rc;
+  if (d == 0) return MM_OK;
+  const size_t es = io_dtype == MM_IO_BF16 ? 2 : 4;
+  const size_t ntd = static_cast<size_t>(T) * d * es, ntn = static_cast<size_t>(T) * N * es;
+  const size_t nsk = static_cast<size_t>(S) * d * kKS * 4, nsn = static_cast<size_t>(S) * d * N * 4;
+  const size_t nd = static_cast<size_t>(d) * 4;
+  // inputs and outputs; an array of zero bytes may be NULL
+  const Span in[] = {{x, ntd}, {z, ntd}, {dt, ntd}, {B, ntn}, {C, ntn}, {dy, ntd},
+                     {A_log, nd * N}, {D, nd}, {dt_bias, nd}, {conv_w, nd * K}, {conv_b, nd},
+                     {cu_seqlens, static_cast<size_t>(S + 1) * 4}, {conv_state, nsk}, {ssm_state, nsn}};
+  const Span out[] = {{dx, ntd}, {dz, ntd}, {ddt, ntd}, {dB, ntn}, {dC, ntn},
+                      {dA_log, nd * N}, {dD, nd}, {ddt_bias, nd}, {dconv_w, nd * K}, {dconv_b, nd},
+                      {dconv_state, nsk}, {dssm_state, nsn}};
+  for (const Span& v : in)
+    if (v.n > 0 && v.p == nullptr) return MM_ERR_NULL;
+  for (const Span& v : out)
+    if (v.n > 0 && v.p == nullptr) return MM_ERR_NULL;
+  for (int i = 0; i < 6; ++i)
+    if (!aligned(in[i].p, es)) return MM_ERR_ALIGN;
+  for (int i = 0; i < 5; ++i)
+    if (!aligned(out[i].p, es)) return MM_ERR_ALIGN;
+  for (size_t i = 6; i < sizeof(in) / sizeof(in[0]); ++i)
+    if (!aligned(in[i].p, 4)) return MM_ERR_ALIGN;
+  for (size_t i = 5; i < sizeof(out) / sizeof(out[0]); ++i)
+    if (!aligned(out[i].p, 4)) return MM_ERR_ALIGN;
+  for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+    for (const Span& v : in)
+      if (overlap(out[i].p, out[i].n, v.p, v.n)) return MM_ERR_ALIAS;
+    for (size_t k = i + 1; k < sizeof(out) / sizeof(out[0]); ++k)
+      if (overlap(out[i].p, out[i].n, out[k].p, out[k].n)) return MM_ERR_ALIAS;
+  }
+  BwdPlan p{};
+  rc = make_bwd_plan(p, S, T, d, N);
+  if (rc != MM_OK) return rc;
+  if (p.total > 0 && (workspace == nullptr || workspace_bytes < p.total)) return MM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MM_ERR_ALIGN;
+  if (events != nullptr && n_events < p.kernels + 1) return MM_ERR_DIM;
+  const BwdArgs a{x, z, dt, B, C, dy, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state,
+                  dx, dz, ddt, dB, dC, dA_log, dD, ddt_bias, dconv_w, dconv_b, dconv_state, dssm_state,
+                  S, T, d, N};
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const StageEvents evs{events, n_events, 0};
+  if (io_dtype == MM_IO_BF16) return launch_backward<uint16_t>(p, a, ws, st, evs);
+  return launch_backward<float>(p, a, ws, st, evs);
 }
 
 }  // extern "C"

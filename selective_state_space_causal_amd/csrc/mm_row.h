@@ -196,14 +196,18 @@ __device__ __forceinline__ void row_work(int64_t w, int ncg, int64_t& k, int& cb
 
 // FINAL = false: pass 1 (sum(delta) and local end state of every non-last chunk).
 // FINAL = true: pass 2 (y, and the final states at a sequence's last chunk).
+// CKPT = true (with FINAL = false, whole sequences): the forward pass of the backward,
+// which only writes the state before every 16-token block to ckpt (block ib of
+// sequence s at ckpt row (cu[s] >> 4) + s + ib, [rows][d][16]).
 // whole != 0: one chunk per sequence, workgroup chunk index = sequence (no plan).
-template <typename IO, bool FINAL>
+template <typename IO, bool FINAL, bool CKPT = false>
 __global__ void __launch_bounds__(kRowThreads) k_row(
     const IO* __restrict__ x, const IO* __restrict__ z, const IO* __restrict__ dt, const IO* __restrict__ B,
     const IO* __restrict__ C, const float* __restrict__ A_log, const float* __restrict__ D,
     const float* __restrict__ dt_bias, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     const int32_t* __restrict__ cu, float* __restrict__ conv_state, float* __restrict__ ssm_state,
-    IO* __restrict__ y, CarryWs ws, int S, int64_t T, int d, int N, int64_t Lc, int whole) {
+    IO* __restrict__ y, CarryWs ws, int S, int64_t T, int d, int N, int64_t Lc, int whole,
+    float* __restrict__ ckpt) {
   constexpr int NMAX = kRow;
   constexpr int64_t kMask = ~static_cast<int64_t>(kRow - 1);
   __shared__ RowTiles L;
@@ -227,7 +231,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     R = chunk_ref(cu, ws.off, ws.moff, S, k, Lc);
     if (!R.ok) return;
   }
-  if (!FINAL && R.j == R.ns - 1) return;
+  if (!FINAL && !CKPT && R.j == R.ns - 1) return;
 
   const int j = threadIdx.x & (kRow - 1);             // state entry in the scan; token of the block in the per-token work
   const int ch = static_cast<int>(threadIdx.x >> 4);  // row = channel within the workgroup
@@ -249,7 +253,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const bool multi = R.ns > 1;
   const float* cs0 = conv_state + sc * kKS;
   float h = 0.0f;
-  if (!FINAL) {
+  if (!FINAL && !CKPT) {
     if (R.j == 0) {
       h = (j < N) ? ssm_state[sc * N + j] : 0.0f;
       if (cvalid) {
@@ -305,6 +309,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   for (int ib = 0; ib < nb; ++ib) {
     const int buf = ib & 1;
     const int64_t tb = tb0 + static_cast<int64_t>(ib) * kRow;
+    if (CKPT && cvalid)  // the state before this block
+      ckpt[((static_cast<int64_t>(R.start >> 4) + R.s + ib) * d + c) * NMAX + j] = h;
     {
       const int64_t t = tb + j;
       const bool act = t >= R.start && t < R.end;
@@ -350,6 +356,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     if (t >= R.start && t < R.end && ych_ok) st_io(y, t * d64 + c0 + ych, L.y[(nb - 1) & 1][yt][ych]);
   }
 
+  if (CKPT) return;
   if (!FINAL) {
     const float ds = row_sum(dsum);
     if (cvalid) {

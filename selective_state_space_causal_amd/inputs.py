@@ -33,6 +33,7 @@ COL_BLOCK = 64
 
 # sub-stream tags
 TAG_X, TAG_Z, TAG_DT, TAG_B, TAG_C, TAG_PARAMS, TAG_LENS = 1, 2, 3, 4, 5, 6, 7
+TAG_DY = 8
 TAG_STEP = 100  # decode step k uses tags TAG_STEP * (k + 1) + {TAG_X, ...}
 
 
@@ -152,6 +153,12 @@ def prefill_inputs(seed: int, T: int, d: int, N: int, io: str, rows: tuple[int, 
         B=shared_tensor(seed, tag_base + TAG_B, rows, N, io),
         C=shared_tensor(seed, tag_base + TAG_C, rows, N, io),
     )
+
+
+def grad_output(seed: int, T: int, d: int, io: str, rows: tuple[int, int] | None = None,
+                cols: tuple[int, int] | None = None) -> np.ndarray:
+    """dL/dy [rows, cols] of a T-token stream for the backward: N(0,1) draws."""
+    return token_tensor(seed, TAG_DY, rows or (0, T), cols or (0, d), io)
 
 
 def decode_inputs(seed: int, step: int, Bs: int, d: int, N: int, io: str,

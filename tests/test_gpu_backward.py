@@ -1,0 +1,152 @@
+"""Prefill backward on the GPU against the fp64 oracle's reverse mode (oracle.prefill_backward,
+itself pinned by finite differences of the oracle's forward).
+
+Tolerance: |g - r| <= rtol (|r| + rms(r)) per gradient array, rtol 1e-2 with bf16 io (the io
+gradients are rounded to bf16, 2^-9 relative) and 1e-4 with fp32 io (fp32 recurrences over
+sequences of up to 2048 tokens and sums over up to 16K tokens or 1536 channels).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_causal_amd as mm
+from selective_state_space_causal_amd import inputs
+from tests.gpu_util import dev, host, log, make_prefill
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"bf16": 1e-2, "f32": 1e-4}
+IO_GRADS = ("dx", "dz", "ddt", "dB", "dC")
+
+
+def grad_close(g, r, io, what):
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    if r.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(r * r)))
+    err = np.abs(g - r)
+    bound = RTOL[io] * (np.abs(r) + rms)
+    worst = float(np.max(err / np.where(bound > 0, bound, 1e-300)))
+    assert np.all(err <= bound), f"{what}: max err/bound {worst:.3g} (rms {rms:.3g})"
+    return worst
+
+
+def gpu_backward(case, dy):
+    S = case["S"]
+    g = mm.prefill_backward(dev(case["x"]), dev(case["z"]), dev(case["dt"]), dev(case["B"]), dev(case["C"]),
+                            dev(case["A_log"]), dev(case["D"]), dev(case["dt_bias"]), dev(case["conv_w"]),
+                            dev(case["conv_b"]), dev(case["cu"]), dev(case["cs"][:S]), dev(case["ss"][:S]), dev(dy))
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in g.items()}
+
+
+def oracle_backward(case, dy, cols=None):
+    S = case["S"]
+    if cols is None:
+        cols = np.arange(case["d"])
+    return oracle.prefill_backward(case["x"][:, cols], case["z"][:, cols], case["dt"][:, cols], case["B"], case["C"],
+                                   case["A_log"][cols], case["D"][cols], case["dt_bias"][cols],
+                                   case["conv_w"][cols], case["conv_b"][cols], case["cu"], case["cs"][:S][:, cols],
+                                   case["ss"][:S][:, cols], dy[:, cols])
+
+
+def check_all(g, r, io, tag):
+    worst = {k: grad_close(g[k], r[k], io, f"{tag} {k}") for k in mm.BACKWARD_GRADS}
+    log(f"[bwd] {tag}: " + " ".join(f"{k}={v:.2g}" for k, v in worst.items() if v is not None))
+
+
+CASES = [
+    # (lengths, d, N): ragged lengths that start mid-block, sequences of 1..3 tokens that read
+    # the initial conv state, an empty sequence, d not a multiple of 16, N < 16
+    ([37, 1, 0, 64, 2, 3, 90, 17], 40, 16),
+    ([200, 5, 111], 24, 5),
+    ([16, 16, 32, 1, 15], 16, 16),
+    ([700, 650], 64, 16),
+]
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_backward_vs_oracle(io, ci):
+    lens, d, N = CASES[ci]
+    case = make_prefill(300 + ci, lens, d, N, io)
+    dy = inputs.grad_output(300 + ci, case["T"], d, io)
+    log(f"[bwd] case {ci} io={io} lens={lens} d={d} N={N}")
+    g = gpu_backward(case, dy)
+    r = oracle_backward(case, dy)
+    check_all(g, r, io, f"case {ci} {io}")
+
+
+def test_backward_sequence_loop():
+    """More sequences than workgroup rows: each workgroup accumulates several sequences."""
+    d, N = 1040, 16  # 65 channel blocks -> 32 workgroup rows
+    lens = list(inputs.packed_lengths(17, 1600, 1, 70))
+    assert len(lens) > 32
+    case = make_prefill(17, lens, d, N, "bf16")
+    dy = inputs.grad_output(17, case["T"], d, "bf16")
+    log(f"[bwd] sequence loop: S={len(lens)} T={case['T']} d={d}")
+    g = gpu_backward(case, dy)
+    r = oracle_backward(case, dy)
+    check_all(g, r, "bf16", "sequence loop")
+
+
+def test_backward_deterministic():
+    lens, d, N = [300, 77, 5], 48, 16
+    case = make_prefill(5, lens, d, N, "bf16")
+    dy = inputs.grad_output(5, case["T"], d, "bf16")
+    g1 = gpu_backward(case, dy)
+    g2 = gpu_backward(case, dy)
+    for k in mm.BACKWARD_GRADS:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+def test_backward_no_tokens():
+    """T == 0 with sequences: every parameter and state gradient is zero (over-writing garbage)."""
+    d, N, S = 20, 16, 3
+    dz = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    z32 = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda")
+    out = {k: torch.full(v.shape, 7.0, dtype=v.dtype, device="cuda") for k, v in {
+        "dA_log": z32(d, N), "dD": z32(d), "ddt_bias": z32(d), "dconv_w": z32(d, 4), "dconv_b": z32(d),
+        "dconv_state": z32(S, d, 3), "dssm_state": z32(S, d, N)}.items()}
+    g = mm.prefill_backward(dz(0, d), dz(0, d), dz(0, d), dz(0, N), dz(0, N), z32(d, N), z32(d), z32(d),
+                            z32(d, 4), z32(d), torch.zeros(S + 1, dtype=torch.int32, device="cuda"),
+                            z32(S, d, 3), z32(S, d, N), dz(0, d), out=out)
+    torch.cuda.synchronize()
+    for k in ("dA_log", "dD", "ddt_bias", "dconv_w", "dconv_b", "dconv_state", "dssm_state"):
+        assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+def test_backward_m130_shape_sampled():
+    """The training shape of the 130M model (8 x 2048 tokens, d 1536, bf16): the io gradients and
+    dB / dC of one whole sequence against the oracle over all channels, and the parameter
+    gradients of a sample of channels against the oracle over all sequences."""
+    S, L, d, N = 8, 2048, 1536, 16
+    T = S * L
+    case = make_prefill(130, [L] * S, d, N, "bf16")
+    dy = inputs.grad_output(130, T, d, "bf16")
+    log("[bwd] m130 shape: GPU")
+    g = gpu_backward(case, dy)
+    s = 5  # one sequence, all channels
+    sl = slice(s * L, (s + 1) * L)
+    one = dict(case)
+    one.update(S=1, T=L, cu=np.array([0, L], np.int32), cs=case["cs"][s:s + 1], ss=case["ss"][s:s + 1])
+    for k in ("x", "z", "dt", "B", "C"):
+        one[k] = case[k][sl]
+    log("[bwd] m130 shape: oracle, one sequence")
+    r = oracle_backward(one, dy[sl])
+    for k in IO_GRADS:
+        grad_close(g[k][sl], r[k], "bf16", f"m130 seq {s} {k}")
+    grad_close(g["dconv_state"][s], r["dconv_state"][0], "bf16", "m130 dconv_state")
+    grad_close(g["dssm_state"][s], r["dssm_state"][0], "bf16", "m130 dssm_state")
+    cols = np.array([0, 1, 15, 16, 700, 1023, 1535])
+    log("[bwd] m130 shape: oracle, sampled channels")
+    rc = oracle_backward(case, dy, cols)
+    for k in ("dA_log", "dD", "ddt_bias", "dconv_w", "dconv_b"):
+        grad_close(g[k][cols], rc[k], "bf16", f"m130 {k}")
+    grad_close(g["dx"][:, cols], rc["dx"], "bf16", "m130 dx sampled")

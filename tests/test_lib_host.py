@@ -222,3 +222,49 @@ def test_decode_replay_multi_validation(lib):
     q[12] = ctypes.c_void_p(p[3].value + 64)  # y_ring overlaps z_ring
     assert _multi(lib, q) == MM_ERR_ALIAS
     assert _multi(lib, [ctypes.c_void_p(0)] * 13, d=0) == 0
+
+
+def _backward(lib, ptrs, S=2, T=100, d=64, N=16, K=4, io=1, ws=None, wsb=0):
+    return lib.mamba_mixer_prefill_backward(*ptrs, S, T, d, N, K, io, ws, wsb, None, None, 0)
+
+
+def test_backward_plan_and_validation(lib):
+    # workspace: per-block checkpoints + per-channel-block dB/dC partials + parameter partials
+    need = mm.backward_plan(2, 100, 64, 16)
+    rows = (100 + 15) // 16 + 2
+    assert need["kernels"] == 4
+    assert need["workspace"] >= rows * 64 * 16 * 4 + 4 * 2 * 100 * 16 * 4
+    assert lib.mamba_mixer_prefill_backward_workspace_bytes(2, 100, 64, 16, 4) == need["workspace"]
+    assert mm.backward_plan(0, 0, 64, 16) == {"workspace": 0, "kernels": 1}
+    assert mm.backward_plan(3, 0, 64, 16)["kernels"] == 4
+    p = _ptrs(26)
+    ws = ctypes.c_void_p(0x7F000000)
+    wsb = need["workspace"]
+    assert _backward(lib, p, K=3, ws=ws, wsb=wsb) == MM_ERR_UNSUPPORTED
+    assert _backward(lib, p, N=17, ws=ws, wsb=wsb) == MM_ERR_UNSUPPORTED
+    assert _backward(lib, p, io=5, ws=ws, wsb=wsb) == MM_ERR_UNSUPPORTED
+    assert _backward(lib, p, T=-1, ws=ws, wsb=wsb) == MM_ERR_DIM
+    assert _backward(lib, p, S=0, T=10, ws=ws, wsb=wsb) == MM_ERR_DIM
+    for i in range(26):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert _backward(lib, q, ws=ws, wsb=wsb) == MM_ERR_NULL, i
+    q = list(p)
+    q[14] = ctypes.c_void_p(p[14].value + 1)  # dx misaligned for bf16
+    assert _backward(lib, q, ws=ws, wsb=wsb) == MM_ERR_ALIGN
+    q = list(p)
+    q[19] = ctypes.c_void_p(p[19].value + 2)  # dA_log misaligned for fp32
+    assert _backward(lib, q, ws=ws, wsb=wsb) == MM_ERR_ALIGN
+    assert _backward(lib, p, ws=ws, wsb=wsb - 1) == MM_ERR_WORKSPACE
+    assert _backward(lib, p, ws=None, wsb=wsb) == MM_ERR_WORKSPACE
+    assert _backward(lib, p, ws=ctypes.c_void_p(0x7F000010), wsb=wsb) == MM_ERR_ALIGN
+    for out, other in ((14, 0), (18, 4), (24, 12), (25, 24), (19, 20)):  # an output on an input or another output
+        q = list(p)
+        q[out] = q[other]
+        assert _backward(lib, q, ws=ws, wsb=wsb) == MM_ERR_ALIAS, (out, other)
+    # d == 0 is a no-op; T == 0 needs only the parameter and state arrays
+    assert _backward(lib, [ctypes.c_void_p(0)] * 26, d=0) == 0
+    q = list(p)
+    for i in (0, 1, 2, 3, 4, 13, 14, 15, 16, 17, 18):
+        q[i] = ctypes.c_void_p(0)
+    assert _backward(lib, q, T=0, ws=None, wsb=0) == MM_ERR_WORKSPACE  # passes the pointer checks
