@@ -305,9 +305,32 @@ def bench_other_prefills(args):
     return out
 
 
+def _time_calls(fn, n_kernels, names, reps=10):
+    """Mean whole-call time (torch events) and per-kernel times (HIP events the library records
+    around each of its kernels) of fn(events) over reps calls after one warm-up call."""
+    import torch
+
+    hev = HipEvents(n_kernels + 1)
+    kern = {n: [] for n in names}
+    whole = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(hev.ev)
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:
+            whole.append(e0.elapsed_time(e1))
+            for i, n in enumerate(names):
+                kern[n].append(hev.ms(i, i + 1))
+    hev.close()
+    return float(np.mean(whole)), {n: float(np.mean(v)) for n, v in kern.items()}
+
+
 def bench_backward(args):
-    """Prefill backward of the 130M training shape (8 x 2048 tokens, d 1536, bf16 io): every kernel
-    timed with HIP events over several calls on resident inputs, and the whole call."""
+    """Prefill backward of the 130M training shape (8 x 2048 tokens, d 1536, bf16 io) on resident
+    inputs: the standalone backward (it runs its own checkpoint pass), and a training step =
+    the forward that stores checkpoints + the backward that uses them."""
     import torch
 
     import selective_state_space_causal_amd as mm
@@ -319,41 +342,55 @@ def bench_backward(args):
     st = {k: dev(v) for k, v in tok.items()}
     st.update({k: dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")})
     st.update(cu=dev(cu), cs=dev(cs), ss=dev(ss), dy=dev(inputs.grad_output(0, T, d, "bf16")))
+    prm = [st[k] for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    tk = [st[k] for k in ("x", "z", "dt", "B", "C")]
+    cs0 = st["cs"].clone()  # the initial states (the forward overwrites its copies)
+    ss0 = st["ss"].clone()
+    # standalone backward
     plan = mm.backward_plan(S, T, d, N)
-    nk = plan["kernels"]
     ws = torch.empty(plan["workspace"], dtype=torch.uint8, device="cuda")
-    out = None
+    out = mm.prefill_backward(*tk, *prm, st["cu"], cs0, ss0, st["dy"], workspace=ws)
     names = ["k_row_ckpt", "k_row_bwd", "k_bwd_sum_bc", "k_bwd_sum_params"]
-    hev = HipEvents(nk + 1)
-    reps = 10
-    kern = {n: [] for n in names}
-    whole = []
-    for r in range(reps + 1):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        out = mm.prefill_backward(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"],
-                                  st["dt_bias"], st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], st["dy"],
-                                  out=out, workspace=ws, events=hev.ev)
-        e1.record()
-        torch.cuda.synchronize()
-        if r > 0:  # the first call is a warm-up
-            whole.append(e0.elapsed_time(e1))
-            for i, n in enumerate(names):
-                kern[n].append(hev.ms(i, i + 1))
-    hev.close()
-    ms = float(np.mean(whole))
-    kms = {n: float(np.mean(v)) for n, v in kern.items()}
+    ms_b, k_b = _time_calls(lambda ev: mm.prefill_backward(*tk, *prm, st["cu"], cs0, ss0, st["dy"], out=out,
+                                                           workspace=ws, events=ev), plan["kernels"], names)
+    del ws
+    # training step: forward with checkpoints, backward from them
+    fplan = mm.plan(S, T, d, N, engine=mm.ENGINE_ROW)
+    fws = torch.empty(max(fplan["workspace_bytes"], 1), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    ck = torch.empty((mm.checkpoint_bytes(S, T, d) // 4,), dtype=torch.float32, device="cuda").view(-1, d, 16)
+    cs1, ss1 = st["cs"], st["ss"]
+
+    def fwd(ev):
+        cs1.copy_(cs0)
+        ss1.copy_(ss0)
+        mm.prefill_train(*tk, *prm, st["cu"], cs1, ss1, y=y, ckpt=ck, workspace=fws, events=ev)
+    fnames = [f"fwd_{k}" for k in fplan["kernels"]]
+    ms_f, k_f = _time_calls(fwd, len(fnames), fnames)
+    bplan = mm.backward_plan(S, T, d, N, has_ckpt=True)
+    bws = torch.empty(bplan["workspace"], dtype=torch.uint8, device="cuda")
+    bnames = ["k_row_bwd", "k_bwd_sum_bc", "k_bwd_sum_params"]
+    ms_bc, k_bc = _time_calls(lambda ev: mm.prefill_backward(*tk, *prm, st["cu"], cs0, None, st["dy"], ckpt=ck,
+                                                             out=out, workspace=bws, events=ev),
+                              bplan["kernels"], bnames)
     io_bytes = T * d * 2 * 4 + T * d * 2 * 3 + 2 * T * N * 2 * 2  # x, z, dt, dy in; dx, dz, ddt out; B, C in, dB, dC out
-    del st, ws, out
+    del st, bws, fws, out, ck, y
     torch.cuda.empty_cache()
+    step_ms = ms_f + ms_bc
     return dict(
         workload=f"mamba-130m-shaped layer backward: {S} packed sequences x {L} tokens, d_inner {d}, d_state {N}, "
                  "conv 4, bf16 io, fp32 state; gradients of all inputs, parameters and initial states",
-        tokens_per_s=round(T / (ms * 1e-3), 1), ms=round(ms, 4),
-        kernels_ms={n: round(v, 4) for n, v in kms.items()},
-        workspace_bytes=plan["workspace"],
-        io_bytes=io_bytes, io_GBs=round(io_bytes / (ms * 1e-3) / 1e9, 1),
-        note="checkpoint pass (forward states before every 16-token block), reverse pass, fixed-order sums")
+        standalone=dict(tokens_per_s=round(T / (ms_b * 1e-3), 1), ms=round(ms_b, 4),
+                        kernels_ms={n: round(v, 4) for n, v in k_b.items()}, workspace_bytes=plan["workspace"],
+                        note="own checkpoint pass (the forward's states before every 16-token block), reverse "
+                             "pass, fixed-order partial sums"),
+        train_step=dict(tokens_per_s=round(T / (step_ms * 1e-3), 1), ms=round(step_ms, 4),
+                        forward_ms=round(ms_f, 4), backward_ms=round(ms_bc, 4),
+                        kernels_ms={**{n: round(v, 4) for n, v in k_f.items()},
+                                    **{n: round(v, 4) for n, v in k_bc.items()}},
+                        note="forward storing checkpoints (row engine, state copies included in forward_ms) + "
+                             "backward from them"),
+        io_bytes=io_bytes, io_GBs_standalone=round(io_bytes / (ms_b * 1e-3) / 1e9, 1))
 
 
 def bench_decode(args):

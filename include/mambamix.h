@@ -251,6 +251,9 @@ int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, con
  *   cu_seqlens [S+1], conv_state [S, d, K-1] and ssm_state [S, d, N]: the INITIAL states
  *   (those a forward call reads; the backward does not change them)
  *   dy            [T, d]      io     dL/dy
+ *   ckpt          NULL, or the checkpoints mamba_mixer_prefill_train stored for these
+ *                 inputs and initial states: the backward then skips its own forward pass
+ *                 and does not read ssm_state (which may be NULL).
  * Outputs (all overwritten):
  *   dx, dz, ddt   [T, d]      io     ddt is dL/d(dt) (equal to the share of dt_bias)
  *   dB, dC        [T, N]      io     summed over channels
@@ -260,12 +263,13 @@ int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, con
  *   dconv_state   [S, d, K-1] f32    dL/d(initial conv state)
  *   dssm_state    [S, d, N]   f32    dL/d(initial SSM state)
  *   workspace     device scratch of at least mamba_mixer_prefill_backward_workspace_bytes
- *                 bytes, 256-byte aligned (about 64 * (T/16 + S) * d + 128 * T * N * d/16
- *                 bytes: the state before every 16-token block, and per-16-channel partial
- *                 sums of dB and dC)
+ *                 bytes (with has_ckpt = ckpt != NULL), 256-byte aligned: about
+ *                 128 * T * N * d/16 bytes of per-16-channel partial sums of dB and dC, plus
+ *                 mamba_mixer_checkpoint_bytes when ckpt is NULL
  *   events, n_events   optional, as in mamba_mixer_prefill_ex: events[i] is recorded before
  *                 the i-th kernel and events[n] after the last; n is the kernel count
- *                 mamba_mixer_prefill_backward_plan reports (4, or 1 when S == 0).
+ *                 mamba_mixer_prefill_backward_plan reports (4 without ckpt, 3 with it, 1
+ *                 when S == 0).
  * The sums over channels, tokens and sequences are taken in a fixed order: the results do
  * not vary from run to run.  An empty sequence gets zero state gradients.  d == 0 is a
  * successful no-op; with T == 0 the parameter and state gradients are zeros.  Arrays of
@@ -274,16 +278,39 @@ int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, con
 int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, const void* B, const void* C,
                                  const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
                                  const float* conv_b, const int32_t* cu_seqlens, const float* conv_state,
-                                 const float* ssm_state, const void* dy, void* dx, void* dz, void* ddt, void* dB,
-                                 void* dC, float* dA_log, float* dD, float* ddt_bias, float* dconv_w, float* dconv_b,
+                                 const float* ssm_state, const void* dy, const float* ckpt, void* dx, void* dz,
+                                 void* ddt, void* dB, void* dC, float* dA_log, float* dD, float* ddt_bias, float* dconv_w, float* dconv_b,
                                  float* dconv_state, float* dssm_state, int32_t S, int64_t T, int32_t d, int32_t N,
                                  int32_t K, int32_t io_dtype, void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* events, int32_t n_events);
-/* Workspace bytes and kernel count of mamba_mixer_prefill_backward for these sizes (host only;
- * either output pointer may be NULL).  Returns MM_OK or the size error the call would return. */
-int mamba_mixer_prefill_backward_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, size_t* workspace_out,
-                                      int32_t* kernels_out);
-size_t mamba_mixer_prefill_backward_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
+/* Workspace bytes and kernel count of mamba_mixer_prefill_backward for these sizes, with
+ * (has_ckpt != 0) or without checkpoints (host only; either output pointer may be NULL).
+ * Returns MM_OK or the size error the call would return. */
+int mamba_mixer_prefill_backward_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t has_ckpt,
+                                      size_t* workspace_out, int32_t* kernels_out);
+size_t mamba_mixer_prefill_backward_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
+                                                    int32_t has_ckpt);
+/*
+ * mamba_mixer_prefill_train -- the forward of a training step: mamba_mixer_prefill (row
+ * engine, MM_ENGINE_ROW) that also stores the SSM state before every 16-token block, so
+ * that mamba_mixer_prefill_backward need not run the forward again.
+ *   ckpt   [ceil(T/16) + S, d, 16] f32, out, mamba_mixer_checkpoint_bytes(S, T, d) bytes,
+ *          4-byte aligned: the 16-token blocks are aligned in the packed token stream; the
+ *          state before the block starting at token tb of sequence s (entries n >= N zero)
+ *          is row s + tb/16.  Rows of blocks no sequence has stay unwritten.
+ * Everything else is mamba_mixer_prefill_ex with engine MM_ENGINE_ROW (the workspace size
+ * comes from mamba_mixer_prefill_plan with that engine).  The states are overwritten with
+ * the final states as usual: a caller that runs the backward keeps a copy of the initial
+ * conv_state (the backward reads it; the initial SSM state is in the checkpoints).
+ */
+int mamba_mixer_prefill_train(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                              const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
+                              const float* conv_b, const int32_t* cu_seqlens, float* conv_state, float* ssm_state,
+                              void* y, float* ckpt, int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
+                              int32_t io_dtype, int64_t chunk_len, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int32_t n_events);
+/* Bytes of the checkpoints of a prefill of S sequences and T tokens with d channels. */
+size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d);
 /* Static text for a status code (never NULL).  Host only. */
 const char* mamba_mixer_status_string(int status);
 

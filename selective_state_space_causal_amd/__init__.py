@@ -62,13 +62,17 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_decode_replay.restype = ctypes.c_int
     lib.mamba_mixer_decode_replay_multi.argtypes = [P] * 13 + [i32] * 9 + [P]
     lib.mamba_mixer_decode_replay_multi.restype = ctypes.c_int
-    lib.mamba_mixer_prefill_backward.argtypes = [P] * 26 + [i32, i64, i32, i32, i32, i32, P, sz, P, P, i32]
+    lib.mamba_mixer_prefill_backward.argtypes = [P] * 27 + [i32, i64, i32, i32, i32, i32, P, sz, P, P, i32]
     lib.mamba_mixer_prefill_backward.restype = ctypes.c_int
-    lib.mamba_mixer_prefill_backward_plan.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(sz),
+    lib.mamba_mixer_prefill_backward_plan.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.POINTER(sz),
                                                       ctypes.POINTER(i32)]
     lib.mamba_mixer_prefill_backward_plan.restype = ctypes.c_int
-    lib.mamba_mixer_prefill_backward_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.mamba_mixer_prefill_backward_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.mamba_mixer_prefill_backward_workspace_bytes.restype = sz
+    lib.mamba_mixer_prefill_train.argtypes = [P] * 15 + [i32, i64, i32, i32, i32, i32, i64, P, sz, P, P, i32]
+    lib.mamba_mixer_prefill_train.restype = ctypes.c_int
+    lib.mamba_mixer_checkpoint_bytes.argtypes = [i32, i64, i32]
+    lib.mamba_mixer_checkpoint_bytes.restype = sz
     lib.mamba_mixer_status_string.argtypes = [ctypes.c_int]
     lib.mamba_mixer_status_string.restype = ctypes.c_char_p
     lib.mamba_mixer_version.argtypes = []
@@ -193,10 +197,11 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
     return y
 
 
-def backward_plan(S: int, T: int, d: int, N: int, K: int = CONV_K) -> dict:
+def backward_plan(S: int, T: int, d: int, N: int, K: int = CONV_K, has_ckpt: bool = False) -> dict:
     """Workspace bytes and kernel count of one prefill_backward call (host only)."""
     w, k = ctypes.c_size_t(0), ctypes.c_int32(0)
-    rc = load().mamba_mixer_prefill_backward_plan(S, T, d, N, K, ctypes.byref(w), ctypes.byref(k))
+    rc = load().mamba_mixer_prefill_backward_plan(S, T, d, N, K, int(bool(has_ckpt)), ctypes.byref(w),
+                                                  ctypes.byref(k))
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_prefill_backward_plan")
     return {"workspace": w.value, "kernels": k.value}
@@ -206,12 +211,57 @@ BACKWARD_GRADS = ("dx", "dz", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dc
                   "dconv_state", "dssm_state")
 
 
+def checkpoint_bytes(S: int, T: int, d: int) -> int:
+    return int(load().mamba_mixer_checkpoint_bytes(S, T, d))
+
+
+def prefill_train(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state,
+                  y=None, ckpt=None, workspace=None, chunk_len: int = 0, stream=None, events=None):
+    """The forward of a training step: ``prefill`` on the row engine that also stores the state
+    before every 16-token block.  Returns (y, ckpt); ckpt [ceil(T/16) + S, d, 16] float32 goes to
+    ``prefill_backward(..., ckpt=ckpt)`` together with the INITIAL conv state."""
+    import torch
+
+    T, d = x.shape
+    N = B.shape[1]
+    S = cu_seqlens.shape[0] - 1
+    io = x.dtype
+    for t, n in ((x, "x"), (z, "z"), (dt, "dt")):
+        _check(t, (T, d), io, n)
+    for t, n in ((B, "B"), (C, "C")):
+        _check(t, (T, N), io, n)
+    _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
+    if y is None:
+        y = torch.empty((T, d), dtype=io, device=x.device)
+    _check(y, (T, d), io, "y")
+    rows = (T + 15) // 16 + S
+    if ckpt is None:
+        ckpt = torch.empty((rows, d, 16), dtype=torch.float32, device=x.device)
+    _check(ckpt, (rows, d, 16), torch.float32, "ckpt")
+    need = workspace_bytes(S, T, d, N, CONV_K, chunk_len, ENGINE_ROW) if T > 0 and d > 0 and S > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ev, nev = (None, 0) if events is None else ((ctypes.c_void_p * len(events))(*events), len(events))
+    rc = load().mamba_mixer_prefill_train(
+        _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(conv_w),
+        _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(ssm_state), _ptr(y), _ptr(ckpt),
+        S, T, d, N, CONV_K, _io_code(x), int(chunk_len), wptr, wbytes, _stream(stream), ev, nev)
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_prefill_train")
+    return y, ckpt
+
+
 def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, dy,
-                     out=None, workspace=None, stream=None, events=None):
+                     ckpt=None, out=None, workspace=None, stream=None, events=None):
     """Gradients of a prefill call given dy = dL/dy; conv_state / ssm_state are the INITIAL
-    states (read only).  Returns a dict of the tensors named in BACKWARD_GRADS: dx, dz, ddt
-    [T, d] and dB, dC [T, N] in the io dtype, the rest float32 (dconv_state, dssm_state are
-    the gradients of the initial states).  `out` may pass preallocated tensors of that dict.
+    states (read only; with ``ckpt`` from ``prefill_train`` the forward is not run again and
+    ssm_state is not read, so it may be None).  Returns a dict of the tensors named in
+    BACKWARD_GRADS: dx, dz, ddt [T, d] and dB, dC [T, N] in the io dtype, the rest float32
+    (dconv_state, dssm_state are the gradients of the initial states).  `out` may pass
+    preallocated tensors of that dict.
     """
     import torch
 
@@ -229,7 +279,12 @@ def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqle
     _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
     _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
     _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
-    _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
+    if ssm_state is not None:
+        _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
+    elif ckpt is None:
+        raise ValueError("ssm_state is needed unless ckpt is given")
+    if ckpt is not None:
+        _check(ckpt, ((T + 15) // 16 + S, d, 16), torch.float32, "ckpt")
     shapes = {"dx": ((T, d), io), "dz": ((T, d), io), "ddt": ((T, d), io), "dB": ((T, N), io),
               "dC": ((T, N), io), "dA_log": ((d, N), torch.float32), "dD": ((d,), torch.float32),
               "ddt_bias": ((d,), torch.float32), "dconv_w": ((d, CONV_K), torch.float32),
@@ -240,7 +295,7 @@ def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqle
         if k not in g:
             g[k] = torch.empty(shape, dtype=dt_, device=x.device)
         _check(g[k], shape, dt_, k)
-    need = backward_plan(S, T, d, N)["workspace"] if d > 0 else 0
+    need = backward_plan(S, T, d, N, has_ckpt=ckpt is not None)["workspace"] if d > 0 else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
@@ -252,7 +307,9 @@ def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqle
         nev = len(events)
     rc = load().mamba_mixer_prefill_backward(
         _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(conv_w),
-        _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(ssm_state), _ptr(dy),
+        _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state),
+        _ptr(ssm_state) if ssm_state is not None else ctypes.c_void_p(0), _ptr(dy),
+        _ptr(ckpt) if ckpt is not None else ctypes.c_void_p(0),
         *[_ptr(g[k]) for k in BACKWARD_GRADS],
         S, T, d, N, CONV_K, _io_code(x), wptr, wbytes, _stream(stream), ev, nev)
     if rc != MM_OK:

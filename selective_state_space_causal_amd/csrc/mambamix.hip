@@ -184,7 +184,7 @@ struct PrefillArgs {
 };
 
 template <typename IO>
-void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st, StageEvents& evs) {
+void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st, StageEvents& evs, float* ckpt) {
   const IO* xi = static_cast<const IO*>(a.x);
   const IO* zi = static_cast<const IO*>(a.z);
   const IO* di = static_cast<const IO*>(a.dt);
@@ -208,13 +208,20 @@ void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st,
                        a.A_log, a.S, a.d, a.N);
   }
   evs.mark(st);
-  hipLaunchKernelGGL((k_row<IO, true>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w,
-                     a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d, a.N, p.Lc,
-                     whole, nullptr);
+  if (ckpt != nullptr) {
+    hipLaunchKernelGGL((k_row<IO, true, true>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias,
+                       a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d,
+                       a.N, p.Lc, whole, ckpt);
+  } else {
+    hipLaunchKernelGGL((k_row<IO, true>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w,
+                       a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d, a.N, p.Lc,
+                       whole, nullptr);
+  }
 }
 
 template <typename IO, int NMAX>
-int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st, StageEvents evs) {
+int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st, StageEvents evs,
+                   float* ckpt = nullptr) {
   CarryWs cw{};
   cw.off = reinterpret_cast<int32_t*>(ws + p.off_off);
   cw.moff = reinterpret_cast<int32_t*>(ws + p.off_moff);
@@ -224,7 +231,7 @@ int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st
     cw.stash = reinterpret_cast<float*>(ws + p.off_stash);
   }
   if (p.engine == MM_ENGINE_ROW) {
-    if constexpr (NMAX == kRow) launch_row<IO>(p, a, cw, st, evs);
+    if constexpr (NMAX == kRow) launch_row<IO>(p, a, cw, st, evs, ckpt);
     evs.mark(st);
     return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
   }
@@ -375,7 +382,7 @@ struct BwdPlan {
   int kernels;
 };
 
-int make_bwd_plan(BwdPlan& p, int64_t S, int64_t T, int d, int N) {
+int make_bwd_plan(BwdPlan& p, int64_t S, int64_t T, int d, int N, bool has_ckpt) {
   p = BwdPlan{};
   p.nchb = static_cast<int>(cdiv(d, kRowChans));
   p.rows = cdiv(T, kRow) + S;
@@ -383,11 +390,12 @@ int make_bwd_plan(BwdPlan& p, int64_t S, int64_t T, int d, int N) {
   if (g > S) g = S;
   p.G = static_cast<int>(g);
   size_t off = 0;
-  p.off_ckpt = off; off += align256(static_cast<size_t>(p.rows) * d * kRow * sizeof(float));
+  p.off_ckpt = off;
+  if (!has_ckpt) off += align256(static_cast<size_t>(p.rows) * d * kRow * sizeof(float));
   p.off_pbc = off; off += align256(static_cast<size_t>(p.nchb) * 2 * T * N * sizeof(float));
   p.off_prm = off; off += align256(static_cast<size_t>(p.G) * kPrm * d * sizeof(float));
   p.total = off;
-  p.kernels = S > 0 ? 4 : 1;
+  p.kernels = S > 0 ? (has_ckpt ? 3 : 4) : 1;
   if (row_grid(S, d) > INT32_MAX || cdiv(2 * T * N, kBlock) > INT32_MAX) return MM_ERR_DIM;
   return MM_OK;
 }
@@ -396,7 +404,7 @@ struct BwdArgs {
   const void *x, *z, *dt, *B, *C, *dy;
   const float *A_log, *D, *dt_bias, *conv_w, *conv_b;
   const int32_t* cu;
-  const float *conv_state, *ssm_state;
+  const float *conv_state, *ssm_state, *ckpt;  // ckpt: NULL, or the training forward's checkpoints
   void *dx, *dz, *ddt, *dB, *dC;
   float *dA_log, *dD, *ddt_bias, *dconv_w, *dconv_b, *dconv_state, *dssm_state;
   int S;
@@ -406,7 +414,7 @@ struct BwdArgs {
 
 template <typename IO>
 int launch_backward(const BwdPlan& p, const BwdArgs& a, char* ws, hipStream_t st, StageEvents evs) {
-  float* ckpt = reinterpret_cast<float*>(ws + p.off_ckpt);
+  float* ckpt = a.ckpt != nullptr ? const_cast<float*>(a.ckpt) : reinterpret_cast<float*>(ws + p.off_ckpt);
   float* pbc = reinterpret_cast<float*>(ws + p.off_pbc);
   float* pprm = reinterpret_cast<float*>(ws + p.off_prm);
   const IO* xi = static_cast<const IO*>(a.x);
@@ -416,12 +424,14 @@ int launch_backward(const BwdPlan& p, const BwdArgs& a, char* ws, hipStream_t st
   const IO* Ci = static_cast<const IO*>(a.C);
   const dim3 block(kRowThreads);
   if (a.S > 0) {
-    // 1. checkpoints: the forward's states before every 16-token block
-    evs.mark(st);
-    hipLaunchKernelGGL((k_row<IO, false, true>), dim3(static_cast<unsigned>(row_grid(a.S, a.d))), block, 0, st, xi,
-                       zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu,
-                       const_cast<float*>(a.conv_state), const_cast<float*>(a.ssm_state), static_cast<IO*>(nullptr),
-                       CarryWs{}, a.S, a.T, a.d, a.N, a.T + 1, 1, ckpt);
+    // 1. checkpoints: the forward's states before every 16-token block (unless given)
+    if (a.ckpt == nullptr) {
+      evs.mark(st);
+      hipLaunchKernelGGL((k_row<IO, false, true>), dim3(static_cast<unsigned>(row_grid(a.S, a.d))), block, 0, st,
+                         xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu,
+                         const_cast<float*>(a.conv_state), const_cast<float*>(a.ssm_state),
+                         static_cast<IO*>(nullptr), CarryWs{}, a.S, a.T, a.d, a.N, a.T + 1, 1, ckpt);
+    }
     // 2. the reverse pass
     evs.mark(st);
     hipLaunchKernelGGL((k_row_bwd<IO>), dim3(static_cast<unsigned>(row_grid(p.G, a.d))), block, 0, st, xi, zi, di, Bi,
@@ -508,13 +518,14 @@ size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int3
   return mamba_mixer_prefill_workspace_bytes_chunked(S, T, d, N, K, 0);
 }
 
-int mamba_mixer_prefill_ex(const void* x, const void* z, const void* dt, const void* B, const void* C,
-                           const float* A_log, const float* D, const float* dt_bias,
-                           const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
-                           float* conv_state, float* ssm_state, void* y,
-                           int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
-                           int64_t chunk_len, int32_t engine, void* workspace, size_t workspace_bytes,
-                           void* stream, void* const* events, int32_t n_events) {
+// The prefill call; with ckpt != NULL (row engine only) the final pass also stores the
+// state before every 16-token block.
+static int prefill_call(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                        const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
+                        const float* conv_b, const int32_t* cu_seqlens, float* conv_state, float* ssm_state,
+                        void* y, float* ckpt, int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
+                        int32_t io_dtype, int64_t chunk_len, int32_t engine, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* events, int32_t n_events) {
   int rc = check_prefill_sizes(S, T, d, N, K, io_dtype);
   if (rc != MM_OK) return rc;
   if (T == 0 || d == 0 || S == 0) return MM_OK;
@@ -534,6 +545,15 @@ int mamba_mixer_prefill_ex(const void* x, const void* z, const void* dt, const v
     return MM_ERR_ALIAS;
   if (overlap(conv_state, static_cast<size_t>(S) * d * kKS * 4, ssm_state, static_cast<size_t>(S) * d * N * 4))
     return MM_ERR_ALIAS;
+  if (ckpt != nullptr) {
+    const size_t nck = static_cast<size_t>(cdiv(T, kRow) + S) * d * kRow * 4;
+    const Span other[] = {{x, ny}, {z, ny}, {dt, ny}, {B, nbc}, {C, nbc}, {y, ny},
+                          {conv_state, static_cast<size_t>(S) * d * kKS * 4},
+                          {ssm_state, static_cast<size_t>(S) * d * N * 4}};
+    for (const Span& v : other)
+      if (overlap(ckpt, nck, v.p, v.n)) return MM_ERR_ALIAS;
+    if (!aligned(ckpt, 4)) return MM_ERR_ALIGN;
+  }
   Plan p{};
   rc = make_plan(p, S, T, d, N, chunk_len, engine);
   if (rc != MM_OK) return rc;
@@ -545,6 +565,11 @@ int mamba_mixer_prefill_ex(const void* x, const void* z, const void* dt, const v
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const StageEvents evs{events, n_events, 0};
+  if (ckpt != nullptr) {
+    if (p.engine != MM_ENGINE_ROW) return MM_ERR_UNSUPPORTED;
+    if (io_dtype == MM_IO_BF16) return launch_prefill<uint16_t, 16>(p, a, ws, st, evs, ckpt);
+    return launch_prefill<float, 16>(p, a, ws, st, evs, ckpt);
+  }
   if (io_dtype == MM_IO_BF16) {
     if (p.nmax == 4) return launch_prefill<uint16_t, 4>(p, a, ws, st, evs);
     if (p.nmax == 8) return launch_prefill<uint16_t, 8>(p, a, ws, st, evs);
@@ -553,6 +578,35 @@ int mamba_mixer_prefill_ex(const void* x, const void* z, const void* dt, const v
   if (p.nmax == 4) return launch_prefill<float, 4>(p, a, ws, st, evs);
   if (p.nmax == 8) return launch_prefill<float, 8>(p, a, ws, st, evs);
   return launch_prefill<float, 16>(p, a, ws, st, evs);
+}
+
+int mamba_mixer_prefill_ex(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                           const float* A_log, const float* D, const float* dt_bias,
+                           const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                           float* conv_state, float* ssm_state, void* y,
+                           int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                           int64_t chunk_len, int32_t engine, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events, int32_t n_events) {
+  return prefill_call(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, y,
+                      nullptr, S, T, d, N, K, io_dtype, chunk_len, engine, workspace, workspace_bytes, stream,
+                      events, n_events);
+}
+
+size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d) {
+  if (S < 0 || T < 0 || d < 0) return 0;
+  return static_cast<size_t>(cdiv(T, kRow) + S) * d * kRow * sizeof(float);
+}
+
+int mamba_mixer_prefill_train(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                              const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
+                              const float* conv_b, const int32_t* cu_seqlens, float* conv_state, float* ssm_state,
+                              void* y, float* ckpt, int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
+                              int32_t io_dtype, int64_t chunk_len, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int32_t n_events) {
+  if (ckpt == nullptr && T > 0 && d > 0 && S > 0) return MM_ERR_NULL;
+  return prefill_call(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, y,
+                      ckpt, S, T, d, N, K, io_dtype, chunk_len, MM_ENGINE_ROW, workspace, workspace_bytes, stream,
+                      events, n_events);
 }
 
 int mamba_mixer_prefill_chunked(const void* x, const void* z, const void* dt, const void* B, const void* C,
@@ -634,13 +688,13 @@ int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, con
                        ssm_state, y_ring, Bs, d, N, K, io_dtype, W, k0, k1, commit_step, true, stream);
 }
 
-int mamba_mixer_prefill_backward_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, size_t* workspace_out,
-                                      int32_t* kernels_out) {
+int mamba_mixer_prefill_backward_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t has_ckpt,
+                                      size_t* workspace_out, int32_t* kernels_out) {
   int rc = check_prefill_sizes(S, T, d, N, K, MM_IO_F32);
   if (rc != MM_OK) return rc;
   BwdPlan p{};
   if (d > 0) {
-    rc = make_bwd_plan(p, S, T, d, N);
+    rc = make_bwd_plan(p, S, T, d, N, has_ckpt != 0);
     if (rc != MM_OK) return rc;
   }
   if (workspace_out) *workspace_out = p.total;
@@ -648,16 +702,18 @@ int mamba_mixer_prefill_backward_plan(int32_t S, int64_t T, int32_t d, int32_t N
   return MM_OK;
 }
 
-size_t mamba_mixer_prefill_backward_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K) {
+size_t mamba_mixer_prefill_backward_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
+                                                    int32_t has_ckpt) {
   size_t w = 0;
-  if (mamba_mixer_prefill_backward_plan(S, T, d, N, K, &w, nullptr) != MM_OK) return 0;
+  if (mamba_mixer_prefill_backward_plan(S, T, d, N, K, has_ckpt, &w, nullptr) != MM_OK) return 0;
   return w;
 }
 
 int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, const void* B, const void* C,
                                  const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
                                  const float* conv_b, const int32_t* cu_seqlens, const float* conv_state,
-                                 const float* ssm_state, const void* dy, void* dx, void* dz, void* ddt, void* dB,
+                                 const float* ssm_state, const void* dy, const float* ckpt, void* dx, void* dz,
+                                 void* ddt, void* dB,
                                  void* dC, float* dA_log, float* dD, float* ddt_bias, float* dconv_w, float* dconv_b,
                                  float* dconv_state, float* dssm_state, int32_t S, int64_t T, int32_t d, int32_t N,
                                  int32_t K, int32_t io_dtype, void* workspace, size_t workspace_bytes, void* stream,
@@ -670,9 +726,12 @@ int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, c
   const size_t nsk = static_cast<size_t>(S) * d * kKS * 4, nsn = static_cast<size_t>(S) * d * N * 4;
   const size_t nd = static_cast<size_t>(d) * 4;
   // inputs and outputs; an array of zero bytes may be NULL
+  // with checkpoints given, the initial SSM state is not read (their first rows hold it)
+  const size_t nck = ckpt != nullptr ? mamba_mixer_checkpoint_bytes(S, T, d) : 0;
   const Span in[] = {{x, ntd}, {z, ntd}, {dt, ntd}, {B, ntn}, {C, ntn}, {dy, ntd},
                      {A_log, nd * N}, {D, nd}, {dt_bias, nd}, {conv_w, nd * K}, {conv_b, nd},
-                     {cu_seqlens, static_cast<size_t>(S + 1) * 4}, {conv_state, nsk}, {ssm_state, nsn}};
+                     {cu_seqlens, static_cast<size_t>(S + 1) * 4}, {conv_state, nsk},
+                     {ssm_state, ckpt != nullptr ? 0 : nsn}, {ckpt, nck}};
   const Span out[] = {{dx, ntd}, {dz, ntd}, {ddt, ntd}, {dB, ntn}, {dC, ntn},
                       {dA_log, nd * N}, {dD, nd}, {ddt_bias, nd}, {dconv_w, nd * K}, {dconv_b, nd},
                       {dconv_state, nsk}, {dssm_state, nsn}};
@@ -695,12 +754,12 @@ int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, c
       if (overlap(out[i].p, out[i].n, out[k].p, out[k].n)) return MM_ERR_ALIAS;
   }
   BwdPlan p{};
-  rc = make_bwd_plan(p, S, T, d, N);
+  rc = make_bwd_plan(p, S, T, d, N, ckpt != nullptr);
   if (rc != MM_OK) return rc;
   if (p.total > 0 && (workspace == nullptr || workspace_bytes < p.total)) return MM_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MM_ERR_ALIGN;
   if (events != nullptr && n_events < p.kernels + 1) return MM_ERR_DIM;
-  const BwdArgs a{x, z, dt, B, C, dy, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state,
+  const BwdArgs a{x, z, dt, B, C, dy, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, ckpt,
                   dx, dz, ddt, dB, dC, dA_log, dD, ddt_bias, dconv_w, dconv_b, dconv_state, dssm_state,
                   S, T, d, N};
   char* ws = static_cast<char*>(workspace);

@@ -51,6 +51,13 @@ __device__ __forceinline__ float sigmoid_hw(float v) { return rcp_hw(1.0f + exp2
 // d SiLU(v) / dv from s = sigmoid(v)
 __device__ __forceinline__ float dsilu_s(float v, float s) { return s * __builtin_fmaf(v, 1.0f - s, 1.0f); }
 
+// one row's dB or dC terms [token][n]; the padding puts the four rows of a wave on
+// different LDS banks
+struct RedRow {
+  float v[kRow][kRow];
+  float pad[kRow];
+};
+
 struct BwdTiles {
   float x[2][kRow][kRowChans + 1];
   float z[2][kRow][kRowChans + 1];
@@ -58,7 +65,7 @@ struct BwdTiles {
   float dy[2][kRow][kRowChans + 1];
   float4 bc[2][2][4][kRow];
   float o[3][kRow][kRowChans + 1];      // dx, dz, ddt of the block, [token][channel]
-  float red[2][kRowChans][kRow][kRow];  // dB, dC terms [row][token][n] before the sum over rows
+  RedRow red[2][kRowChans];  // dB, dC terms [row][token][n] before the sum over rows
 };
 
 template <typename IO>
@@ -111,49 +118,55 @@ __device__ __forceinline__ void bwd_stage_store(const BwdStage<IO>& r, BwdTiles&
 // forward recompute, token I of the block: decay, state after the token, readout term
 template <int I>
 __device__ __forceinline__ void bwd_fwd_step(float delta, float du, float A2, const float4 (&Bq)[4],
-                                             const float4 (&Cq)[4], float& h, float (&hs)[kRow], float (&as)[kRow],
+                                             const float4 (&Cq)[4], float& h, float* hsl, float* asl,
                                              float (&pr)[kRow]) {
   const float a = exp2_hw(bcast<I>(delta) * A2);
   h = __builtin_fmaf(a, h, bcast<I>(du) * comp(Bq[I >> 2], I & 3));
-  hs[I] = h;
-  as[I] = a;
+  hsl[I * kRow] = h;
+  asl[I * kRow] = a;
   pr[I] = comp(Cq[I >> 2], I & 3) * h;
 }
 
 template <int... I>
 __device__ __forceinline__ void bwd_fwd_steps(std::integer_sequence<int, I...>, float delta, float du, float A2,
                                               const float4 (&Bq)[4], const float4 (&Cq)[4], float& h,
-                                              float (&hs)[kRow], float (&as)[kRow], float (&pr)[kRow]) {
-  (bwd_fwd_step<I>(delta, du, A2, Bq, Cq, h, hs, as, pr), ...);
+                                              float* hsl, float* asl, float (&pr)[kRow]) {
+  (bwd_fwd_step<I>(delta, du, A2, Bq, Cq, h, hsl, asl, pr), ...);
 }
 
 // adjoint step, token I of the block (called for I = 15 down to 0).  lam holds
-// lambda of token I+1 on entry and of token I on exit; anext the decay of token I+1.
+// lambda of token I+1 on entry and of token I on exit; anext the decay of token I+1
+// on entry and of token I on exit.  The forward phase left the state h_I in rC[I]
+// and the decay a_I in rB[I]; each is read before the slot is overwritten with the
+// dC or dB term.  lambda h_{I-1} a_I = lambda (h_I - du_I B_I).
 template <int I>
-__device__ __forceinline__ void bwd_rev_step(float dp, float du, float delta, float An, float h0,
-                                             const float4 (&Bq)[4], const float4 (&Cq)[4], const float (&hs)[kRow],
-                                             const float (&as)[kRow], float& lam, float& anext, float& accA,
+__device__ __forceinline__ void bwd_rev_step(float dp, float du, float delta, float An,
+                                             const float4 (&Bq)[4], const float4 (&Cq)[4],
+                                             float& lam, float& anext, float& accA,
                                              float (&s1)[kRow], float (&s2)[kRow], float (&rB)[kRow][kRow],
                                              float (&rC)[kRow][kRow], int j) {
   const float dpi = bcast<I>(dp);
   lam = __builtin_fmaf(anext, lam, dpi * comp(Cq[I >> 2], I & 3));
-  rC[I][j] = dpi * hs[I];
-  rB[I][j] = lam * bcast<I>(du);
-  const float hp = I > 0 ? hs[I > 0 ? I - 1 : 0] : h0;
-  const float q = lam * hp * as[I];
+  const float hI = rC[I][j];  // the state after token I, left here by the forward phase
+  rC[I][j] = dpi * hI;
+  const float dui = bcast<I>(du);
+  const float aI = rB[I][j];
+  rB[I][j] = lam * dui;
+  const float sb = lam * comp(Bq[I >> 2], I & 3);
+  s1[I] = sb;
+  const float q = __builtin_fmaf(-dui, sb, lam * hI);
   s2[I] = q * An;
-  accA = __builtin_fmaf(q, bcast<I>(delta), accA);
-  s1[I] = lam * comp(Bq[I >> 2], I & 3);
-  anext = as[I];
+  accA = __builtin_fmaf(bcast<I>(delta), q, accA);
+  anext = aI;
 }
 
 template <int... I>
 __device__ __forceinline__ void bwd_rev_steps(std::integer_sequence<int, I...>, float dp, float du, float delta,
-                                              float An, float h0, const float4 (&Bq)[4], const float4 (&Cq)[4],
-                                              const float (&hs)[kRow], const float (&as)[kRow], float& lam,
+                                              float An, const float4 (&Bq)[4], const float4 (&Cq)[4],
+                                              float& lam,
                                               float& anext, float& accA, float (&s1)[kRow], float (&s2)[kRow],
                                               float (&rB)[kRow][kRow], float (&rC)[kRow][kRow], int j) {
-  (bwd_rev_step<kRow - 1 - I>(dp, du, delta, An, h0, Bq, Cq, hs, as, lam, anext, accA, s1, s2, rB, rC, j), ...);
+  (bwd_rev_step<kRow - 1 - I>(dp, du, delta, An, Bq, Cq, lam, anext, accA, s1, s2, rB, rC, j), ...);
 }
 
 // The reverse pass.  Workgroup (k, cb) takes channels 16 cb .. 16 cb + 15 of
@@ -163,7 +176,7 @@ __device__ __forceinline__ void bwd_rev_steps(std::integer_sequence<int, I...>, 
 // and dC sums over each 16-channel block; pprm [G][kPrm][d], the parameter
 // gradients summed over each workgroup row's sequences.
 template <typename IO>
-__global__ void __launch_bounds__(kRowThreads) k_row_bwd(
+__global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(3))) k_row_bwd(
     const IO* __restrict__ x, const IO* __restrict__ z, const IO* __restrict__ dt, const IO* __restrict__ B,
     const IO* __restrict__ C, const IO* __restrict__ dy, const float* __restrict__ A_log,
     const float* __restrict__ D, const float* __restrict__ dt_bias, const float* __restrict__ conv_w,
@@ -273,24 +286,43 @@ __global__ void __launch_bounds__(kRowThreads) k_row_bwd(
         Cq[q] = L.bc[buf][1][q][j];
       }
 
+      __builtin_amdgcn_sched_barrier(0);
       // the block's states from its checkpoint, and the readout p
-      float hs[kRow], as[kRow], pr[kRow];
+      float pr[kRow];
       float h = h0;
-      bwd_fwd_steps(std::make_integer_sequence<int, kRow>{}, delta, du, A2, Bq, Cq, h, hs, as, pr);
+      bwd_fwd_steps(std::make_integer_sequence<int, kRow>{}, delta, du, A2, Bq, Cq, h, &L.red[1][ch].v[0][j],
+                    &L.red[0][ch].v[0][j], pr);
       const float pt = __builtin_fmaf(Dc, u, row_transpose_sum(pr, j));
       const float sz = sigmoid_hw(zv);
       const float dp = dyv * (zv * sz);
       const float dzv = dyv * pt * dsilu_s(zv, sz);
 
-      // the adjoint recurrence over the block, last token first
+      __builtin_amdgcn_sched_barrier(0);
+      // the adjoint recurrence over the block, last token first.  The reverse broadcasts
+      // from copies the compiler cannot merge with the forward's: a merged broadcast has
+      // several uses, cannot fold into them and stays live across both phases.
       float s1[kRow], s2[kRow];
-      float(&rB)[kRow][kRow] = L.red[0][ch];
-      float(&rC)[kRow][kRow] = L.red[1][ch];
-      bwd_rev_steps(std::make_integer_sequence<int, kRow>{}, dp, du, delta, An, h0, Bq, Cq, hs, as, lam, anext,
-                    accA, s1, s2, rB, rC, j);
+      float du_r = du, delta_r = delta, dp_r = dp;
+      int lz = 0;  // a zero the compiler cannot see: the LDS reads below are not merged with earlier ones
+      asm volatile("" : "+v"(du_r), "+v"(delta_r), "+v"(dp_r), "+v"(lz));
+      const int jz = j + lz;
+      // B and C again from LDS rather than kept in registers across the forward phase, and
+      // the states from LDS where the forward phase left them
+      float4 Br[4], Cr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        Br[q] = L.bc[buf][0][q][jz];
+        Cr[q] = L.bc[buf][1][q][jz];
+      }
+      float(&rB)[kRow][kRow] = L.red[0][ch].v;
+      float(&rC)[kRow][kRow] = L.red[1][ch].v;
+      bwd_rev_steps(std::make_integer_sequence<int, kRow>{}, dp_r, du_r, delta_r, An, Br, Cr, lam, anext,
+                    accA, s1, s2, rB, rC, jz);
+      __builtin_amdgcn_sched_barrier(0);
       const float S1 = row_transpose_sum(s1, j);
       const float S2 = row_transpose_sum(s2, j);
 
+      __builtin_amdgcn_sched_barrier(0);
       // per-token tail
       const float dut = __builtin_fmaf(dp, Dc, delta * S1);
       const float ddel = __builtin_fmaf(u, S1, S2);
@@ -319,6 +351,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row_bwd(
       h0 = h0n;
       prev = prevn;
 
+      __builtin_amdgcn_sched_barrier(0);
       if (ib >= 1) bwd_stage_store<IO>(stg, L, buf ^ 1, N);
       if (ib >= 2) bwd_stage_load<IO>(stg, x, z, dt, dy, B, C, tb - 2 * kRow, T32, d, N, c0);
       __syncthreads();
@@ -328,8 +361,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row_bwd(
         float sB = 0.0f, sC = 0.0f;
 #pragma unroll
         for (int r = 0; r < kRowChans; ++r) {
-          sB += L.red[0][r][tt][n];
-          sC += L.red[1][r][tt][n];
+          sB += L.red[0][r].v[tt][n];
+          sC += L.red[1][r].v[tt][n];
         }
         if (tg >= start && tg < end) {
           if (n < N) {

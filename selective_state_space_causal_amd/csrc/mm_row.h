@@ -196,9 +196,11 @@ __device__ __forceinline__ void row_work(int64_t w, int ncg, int64_t& k, int& cb
 
 // FINAL = false: pass 1 (sum(delta) and local end state of every non-last chunk).
 // FINAL = true: pass 2 (y, and the final states at a sequence's last chunk).
-// CKPT = true (with FINAL = false, whole sequences): the forward pass of the backward,
-// which only writes the state before every 16-token block to ckpt (block ib of
-// sequence s at ckpt row (cu[s] >> 4) + s + ib, [rows][d][16]).
+// CKPT = true: also write the state before every 16-token block to ckpt, [rows][d][16],
+// the block starting at token tb of sequence s at row s + tb / 16.  With FINAL = false
+// (whole sequences only) that is all the pass writes: the checkpoint pass of the
+// backward.  With FINAL = true it is the forward of a training step; a continuing
+// chunk leaves a block it shares with the chunk before to that chunk.
 // whole != 0: one chunk per sequence, workgroup chunk index = sequence (no plan).
 template <typename IO, bool FINAL, bool CKPT = false>
 __global__ void __launch_bounds__(kRowThreads) k_row(
@@ -309,8 +311,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   for (int ib = 0; ib < nb; ++ib) {
     const int buf = ib & 1;
     const int64_t tb = tb0 + static_cast<int64_t>(ib) * kRow;
-    if (CKPT && cvalid)  // the state before this block
-      ckpt[((static_cast<int64_t>(R.start >> 4) + R.s + ib) * d + c) * NMAX + j] = h;
+    if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0))  // the state before this block
+      ckpt[((static_cast<int64_t>(tb >> 4) + R.s) * d + c) * NMAX + j] = h;
     {
       const int64_t t = tb + j;
       const bool act = t >= R.start && t < R.end;
@@ -356,7 +358,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     if (t >= R.start && t < R.end && ych_ok) st_io(y, t * d64 + c0 + ych, L.y[(nb - 1) & 1][yt][ych]);
   }
 
-  if (CKPT) return;
+  if (CKPT && !FINAL) return;
   if (!FINAL) {
     const float ds = row_sum(dsum);
     if (cvalid) {

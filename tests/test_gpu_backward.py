@@ -150,3 +150,75 @@ def test_backward_m130_shape_sampled():
     for k in ("dA_log", "dD", "ddt_bias", "dconv_w", "dconv_b"):
         grad_close(g[k][cols], rc[k], "bf16", f"m130 {k}")
     grad_close(g["dx"][:, cols], rc["dx"], "bf16", "m130 dx sampled")
+
+
+def _train(case, chunk_len):
+    S = case["S"]
+    cs, ss = dev(case["cs"][:S]), dev(case["ss"][:S])
+    y, ck = mm.prefill_train(dev(case["x"]), dev(case["z"]), dev(case["dt"]), dev(case["B"]), dev(case["C"]),
+                             dev(case["A_log"]), dev(case["D"]), dev(case["dt_bias"]), dev(case["conv_w"]),
+                             dev(case["conv_b"]), dev(case["cu"]), cs, ss, chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return y, ck, cs, ss
+
+
+@pytest.mark.parametrize("chunk_len", [0, 32])
+def test_train_forward_checkpoints(chunk_len):
+    """prefill_train: y and the final states equal the row-engine prefill bit for bit, and the
+    checkpoint row s + tb/16 holds the state before the block at tb (the oracle's state after
+    the sequence's tokens before tb; entries past N zero)."""
+    lens, d, N = [37, 50, 3, 0, 70, 16], 24, 12
+    case = make_prefill(41, lens, d, N, "f32")
+    y, ck, cs, ss = _train(case, chunk_len)
+    S = case["S"]
+    cs2, ss2 = dev(case["cs"][:S]), dev(case["ss"][:S])
+    y2 = mm.prefill(dev(case["x"]), dev(case["z"]), dev(case["dt"]), dev(case["B"]), dev(case["C"]),
+                    dev(case["A_log"]), dev(case["D"]), dev(case["dt_bias"]), dev(case["conv_w"]),
+                    dev(case["conv_b"]), dev(case["cu"]), cs2, ss2, chunk_len=chunk_len, engine=mm.ENGINE_ROW)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(cs, cs2) and torch.equal(ss, ss2)
+    ck = host(ck)
+    cu = case["cu"]
+    nblk = 0
+    for s in range(S):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue  # an empty sequence has no blocks
+        for tb in range(a - a % 16, b, 16):
+            if tb <= a:
+                want = case["ss"][s]
+            else:  # the oracle over the sequence's tokens before tb
+                sub = {k: case[k][a:tb] for k in ("x", "z", "dt", "B", "C")}
+                _, _, want = oracle.prefill(sub["x"], sub["z"], sub["dt"], sub["B"], sub["C"], case["A_log"],
+                                            case["D"], case["dt_bias"], case["conv_w"], case["conv_b"],
+                                            np.array([0, tb - a], np.int32), case["cs"][s:s + 1], case["ss"][s:s + 1])
+                want = want[0]
+            got = ck[s + tb // 16]
+            grad_close(got[:, :N], want, "f32", f"checkpoint s={s} tb={tb}")
+            assert np.all(got[:, N:] == 0), f"checkpoint s={s} tb={tb}: entries past N"
+            nblk += 1
+    assert nblk > 10
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_backward_from_train_checkpoints(io):
+    """The backward with the training forward's checkpoints: bit-identical to the backward that
+    runs its own checkpoint pass when the forward takes whole sequences, and within tolerance of
+    the oracle when the forward is chunked (its chunk states come through the carries)."""
+    lens, d, N = [37, 1, 0, 64, 2, 3, 90, 17, 300], 40, 16
+    case = make_prefill(42, lens, d, N, io)
+    dy = inputs.grad_output(42, case["T"], d, io)
+    S = case["S"]
+    ref = gpu_backward(case, dy)
+    r = oracle_backward(case, dy)
+    for chunk_len in (0, 32):
+        _, ck, _, _ = _train(case, chunk_len)
+        g = mm.prefill_backward(dev(case["x"]), dev(case["z"]), dev(case["dt"]), dev(case["B"]), dev(case["C"]),
+                                dev(case["A_log"]), dev(case["D"]), dev(case["dt_bias"]), dev(case["conv_w"]),
+                                dev(case["conv_b"]), dev(case["cu"]), dev(case["cs"][:S]), None, dev(dy), ckpt=ck)
+        torch.cuda.synchronize()
+        g = {k: host(v) for k, v in g.items()}
+        if chunk_len == 0:
+            for k in mm.BACKWARD_GRADS:
+                assert np.array_equal(g[k], ref[k]), f"{k} differs from the backward's own checkpoints"
+        check_all(g, r, io, f"from checkpoints, chunk {chunk_len}")

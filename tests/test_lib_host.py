@@ -225,7 +225,8 @@ def test_decode_replay_multi_validation(lib):
 
 
 def _backward(lib, ptrs, S=2, T=100, d=64, N=16, K=4, io=1, ws=None, wsb=0):
-    return lib.mamba_mixer_prefill_backward(*ptrs, S, T, d, N, K, io, ws, wsb, None, None, 0)
+    # ptrs: the 14 inputs, dy, then the 12 outputs; the checkpoint pointer (NULL) goes in after dy
+    return lib.mamba_mixer_prefill_backward(*ptrs[:14], None, *ptrs[14:], S, T, d, N, K, io, ws, wsb, None, None, 0)
 
 
 def test_backward_plan_and_validation(lib):
@@ -234,7 +235,11 @@ def test_backward_plan_and_validation(lib):
     rows = (100 + 15) // 16 + 2
     assert need["kernels"] == 4
     assert need["workspace"] >= rows * 64 * 16 * 4 + 4 * 2 * 100 * 16 * 4
-    assert lib.mamba_mixer_prefill_backward_workspace_bytes(2, 100, 64, 16, 4) == need["workspace"]
+    assert lib.mamba_mixer_prefill_backward_workspace_bytes(2, 100, 64, 16, 4, 0) == need["workspace"]
+    with_ck = mm.backward_plan(2, 100, 64, 16, has_ckpt=True)
+    assert with_ck["kernels"] == 3
+    assert with_ck["workspace"] == need["workspace"] - mm.checkpoint_bytes(2, 100, 64)
+    assert mm.checkpoint_bytes(2, 100, 64) == rows * 64 * 16 * 4
     assert mm.backward_plan(0, 0, 64, 16) == {"workspace": 0, "kernels": 1}
     assert mm.backward_plan(3, 0, 64, 16)["kernels"] == 4
     p = _ptrs(26)
@@ -268,3 +273,25 @@ def test_backward_plan_and_validation(lib):
     for i in (0, 1, 2, 3, 4, 13, 14, 15, 16, 17, 18):
         q[i] = ctypes.c_void_p(0)
     assert _backward(lib, q, T=0, ws=None, wsb=0) == MM_ERR_WORKSPACE  # passes the pointer checks
+
+
+def test_prefill_train_validation(lib):
+    p = _ptrs(15)  # the 14 prefill pointers (y last) and ckpt
+    need = mm.workspace_bytes(2, 100, 64, 16, chunk_len=32, engine=mm.ENGINE_ROW)
+    ws = ctypes.c_void_p(0x7F000000)
+
+    def call(q, **kw):
+        a = dict(S=2, T=100, d=64, N=16, K=4, io=1, chunk=32)
+        a.update(kw)
+        return lib.mamba_mixer_prefill_train(*q, a["S"], a["T"], a["d"], a["N"], a["K"], a["io"], a["chunk"], ws,
+                                             need, None, None, 0)
+    q = list(p)
+    q[14] = ctypes.c_void_p(0)
+    assert call(q) == MM_ERR_NULL
+    q = list(p)
+    q[14] = q[13]  # checkpoints on top of y
+    assert call(q) == MM_ERR_ALIAS
+    q = list(p)
+    q[14] = ctypes.c_void_p(p[14].value + 2)
+    assert call(q) == MM_ERR_ALIGN
+    assert call([ctypes.c_void_p(0)] * 15, T=0) == 0
