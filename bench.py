@@ -87,6 +87,7 @@ def kernel_source_sha256():
 PREFILL_PROFILE_SUFFIX = "__m130_prefill_8x2048_d1536_N16_bf16.txt"  # profiles/<final kernel><suffix>
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d8192_N16_bf16.txt")
 PROFILE_REPLAY = os.path.join(ROOT, "profiles", "k_decode_replay__m7b_decode_b256_d8192_N16_W4_bf16.txt")
+PROFILE_BACKWARD = os.path.join(ROOT, "profiles", "k_row_bwd__m130_backward_8x2048_d1536_N16_bf16.txt")
 
 
 def counted_traffic(profile_path):
@@ -151,6 +152,19 @@ def alu_slots_per_token_channel(N):
     """
     plain = 4 + 2 + 2 + 1 + 4 * N + 1 + 2 + 1
     trans = 2 + 2 + N + 2
+    return plain + TRANS_SLOTS * trans, plain, trans
+
+
+def alu_slots_backward(N):
+    """Issue slots of the backward's fp32 arithmetic per (token, channel): the forward's (its
+    per-token quantities and states are recomputed, not stored) plus the adjoint's.  Adjoint per
+    state index: the lambda update 2, the dC term 1, the dB term 1, the S1 term and sum 2, the S2
+    term lambda h a A and sum 4, the dA term 1 (11); per token: dp 1, dz 3, du 2, d(delta) 2,
+    d(dt) 1 + sigmoid (add + exp, rcp), d(xc) 4 + sigmoid (add + exp, rcp), dconv_w 4, dconv_b 1,
+    dx 4, dD 1, ddt_bias 1, dt + dt_bias and masks 3 (29 plain + 4 transcendentals)."""
+    f_slots, f_plain, f_trans = alu_slots_per_token_channel(N)
+    plain = f_plain + 11 * N + 29
+    trans = f_trans + 4
     return plain + TRANS_SLOTS * trans, plain, trans
 
 
@@ -377,6 +391,9 @@ def bench_backward(args):
     del st, bws, fws, out, ck, y
     torch.cuda.empty_cache()
     step_ms = ms_f + ms_bc
+    slots, plain, trans = alu_slots_backward(N)
+    kb = k_bc["k_row_bwd"]
+    ach = T * d * slots * 2 / (kb * 1e-3) / 1e12
     return dict(
         workload=f"mamba-130m-shaped layer backward: {S} packed sequences x {L} tokens, d_inner {d}, d_state {N}, "
                  "conv 4, bf16 io, fp32 state; gradients of all inputs, parameters and initial states",
@@ -390,6 +407,12 @@ def bench_backward(args):
                                     **{n: round(v, 4) for n, v in k_bc.items()}},
                         note="forward storing checkpoints (row engine, state copies included in forward_ms) + "
                              "backward from them"),
+        roofline=dict(bound="alu", achieved=round(ach, 2), peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=round(ach / ALU_PEAK_TFLOPS, 4), traffic=counted_traffic(PROFILE_BACKWARD),
+                      kernel="k_row_bwd", kernel_ms=round(kb, 4),
+                      per_unit=f"{slots} issue slots per (token, channel) = {plain} plain fp32 ops + {trans} "
+                               f"transcendentals x {TRANS_SLOTS} (the forward's, recomputed, and the adjoint's); "
+                               "FLOP = 2 x slots", note="the reverse kernel of the training step's backward"),
         io_bytes=io_bytes, io_GBs_standalone=round(io_bytes / (ms_b * 1e-3) / 1e9, 1))
 
 
@@ -644,6 +667,8 @@ def main():
     ap.add_argument("--no-other-prefills", action="store_true",
                     help="skip the context prefill rates of the other configurations")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward timing")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="only the backward timing (the kernel-trace and counter runs of its profile)")
     ap.add_argument("--decode-flushed-only", action="store_true",
                     help="with --no-prefill: only the flushed-cache eager and replay decode dispatches "
                          "(the kernel-trace and counter runs of the profiles)")
@@ -676,6 +701,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     mm.load()
     log(f"[bench] {mm.version()} on {torch.cuda.get_device_name(0)}")
+    if args.only_backward:
+        print(json.dumps(dict(metric=METRIC, note="backward-only diagnostic run (--only-backward); no headline value",
+                              backward=bench_backward(args))), flush=True)
+        return
 
     if args.no_prefill:
         args.no_cpu_baseline = True
