@@ -6,7 +6,7 @@ binding never import it, and it never imports them.
 
 ``prefill`` and ``decode`` wrap the plain C routines in ``mamba_oracle.c``
 (one token at a time, double precision; see that file for the passages each
-step follows).  ``check`` holds the independent numpy pins (brute-force
+step follows).  ``project`` is plain numpy (the projections ahead of the scan).  ``check`` holds the independent numpy pins (brute-force
 materialised sums, closed forms, library routines) the oracle is tested
 against.
 
@@ -168,3 +168,36 @@ def decode_replay(x_ring, dt_ring, B_ring, k, z, C, A_log, D, dt_bias, conv_w, c
         _, cs, ss = decode(x_ring[s], zero_z, dt_ring[s], B_ring[s], zero_c, A_log, D, dt_bias, conv_w, conv_b,
                            cs, ss, nthreads)
     return decode(x_ring[k], z, dt_ring[k], B_ring[k], C, A_log, D, dt_bias, conv_w, conv_b, cs, ss, nthreads)
+
+
+def project(x, conv_w, conv_b, cu_seqlens, conv_state, w_x, w_dt, R: int, N: int):
+    """The input-dependent projections ahead of the scan, as the TensorRT Mamba tensor-parallel
+    builder (_add_mamba_tp_layer) lays them out: the conv activation u (window = the state's K-1
+    older raw inputs, then x; weighted sum with conv_w, plus conv_b, SiLU) is multiplied by the
+    three input-major weights w_dt_in [d, R], w_B [d, N] and w_C [d, N] -- here the columns of
+    w_x [d, R + 2N] in that order -- and dt_in is multiplied by w_dt_out [R, d] (w_dt here).  The
+    builder then adds dt_proj_bias and takes softplus, which the mixer core does with dt_bias.
+
+    x [T, d]; conv_w [d, K]; conv_b [d]; cu_seqlens [S+1]; conv_state [S, d, K-1] (the initial
+    state, read only).  Returns a dict of float64 arrays u [T, d], dt_in [T, R], B [T, N],
+    C [T, N], dt [T, d].  Sequences never see one another's tokens (PackMamba).
+    """
+    x = as_f64(x)
+    conv_w, conv_b, w_x, w_dt = (as_f64(a) for a in (conv_w, conv_b, w_x, w_dt))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    S = cu.shape[0] - 1
+    T, d = x.shape
+    K = conv_w.shape[1]
+    cs = as_f64(conv_state).reshape(S, d, K - 1)
+    u = np.zeros((T, d))
+    for s in range(S):
+        a, b = int(cu[s]), int(cu[s + 1])
+        window = np.concatenate([cs[s].T, x[a:b]], axis=0)  # rows oldest first: K-1 state columns, then tokens
+        for t in range(b - a):
+            xc = conv_b.copy()
+            for k in range(K):
+                xc += conv_w[:, k] * window[t + k]
+            u[a + t] = xc / (1.0 + np.exp(-xc))
+    xdbl = u @ w_x
+    dt_in = xdbl[:, :R]
+    return dict(u=u, dt_in=dt_in, B=xdbl[:, R:R + N], C=xdbl[:, R + N:R + 2 * N], dt=dt_in @ w_dt)

@@ -15,6 +15,8 @@ unstable softplus) disagrees with at least one of them.
   index.
 * ``lfilter_scan``: with one state index, constant delta and B = C = 1 the scan
   is a first-order IIR filter (``scipy.signal.lfilter``).
+* ``conv_silu`` and ``matmul_loops``: the conv activation by ``np.convolve`` and
+  ``expit``, and a matrix product written as Python loops, for the projections.
 """
 from __future__ import annotations
 
@@ -88,3 +90,32 @@ def lfilter_scan(u, delta, A, h0):
     a = np.exp(delta * A)
     h, _ = lfilter([1.0], [1.0, -a], delta * np.asarray(u, dtype=np.float64), zi=[a * h0])
     return h
+
+
+def conv_silu(x, conv_w, conv_b, conv0):
+    """SiLU of the causal conv of one sequence by np.convolve: x [L, d], conv0 [d, K-1] (older
+    first); returns u [L, d]."""
+    x, conv_w, conv_b, conv0 = (to64(a) for a in (x, conv_w, conv_b, conv0))
+    L, d = x.shape
+    X = np.concatenate([conv0.T, x], axis=0)
+    u = np.empty((L, d))
+    for c in range(d):
+        xc = np.convolve(X[:, c], conv_w[c, ::-1], mode="valid") + conv_b[c]
+        u[:, c] = xc * expit(xc)
+    return u
+
+
+def matmul_loops(a, b):
+    """a @ b by explicit loops (tiny sizes only)."""
+    a, b = to64(a), to64(b)
+    m, k = a.shape
+    k2, n = b.shape
+    assert k == k2
+    out = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            acc = 0.0
+            for q in range(k):
+                acc += float(a[i, q]) * float(b[q, j])
+            out[i, j] = acc
+    return out

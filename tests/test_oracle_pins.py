@@ -432,3 +432,77 @@ def test_oracle_backward_separates_sequences(oracle_lib):
         assert np.any(g[k][cu[1]:cu[2]] != 0.0), k
     for k in ("dconv_state", "dssm_state"):
         assert np.all(g[k][0] == 0.0) and np.all(g[k][2] == 0.0) and np.any(g[k][1] != 0.0), k
+
+
+# --- projections ahead of the scan ---------------------------------------------------------
+
+def _proj_case(seed, lens, d, R, N, K=4):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    return dict(x=rng.standard_normal((T, d)), conv_w=rng.uniform(-0.5, 0.5, (d, K)),
+                conv_b=rng.uniform(-0.5, 0.5, d), cs=rng.standard_normal((len(lens), d, K - 1)),
+                w_x=rng.standard_normal((d, R + 2 * N)) / np.sqrt(d), w_dt=rng.standard_normal((R, d)) / np.sqrt(R),
+                cu=inputs.cu_from_lengths(lens))
+
+
+def _proj(f, R, N):
+    import oracle
+
+    return oracle.project(f["x"], f["conv_w"], f["conv_b"], f["cu"], f["cs"], f["w_x"], f["w_dt"], R, N)
+
+
+def test_oracle_project_conv_matches_convolve():
+    """The projection's conv activation against np.convolve + expit, sequence by sequence,
+    with 1- and 2-token sequences reading the initial conv state."""
+    lens, d, R, N = [9, 1, 0, 2, 14], 6, 3, 2
+    f = _proj_case(3, lens, d, R, N)
+    o = _proj(f, R, N)
+    cu = f["cu"]
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b > a:
+            ref = pins.conv_silu(f["x"][a:b], f["conv_w"], f["conv_b"], f["cs"][s])
+            np.testing.assert_allclose(o["u"][a:b], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_oracle_project_products_by_loops():
+    """dt_in, B, C and dt against the products written as loops over the same u."""
+    lens, d, R, N = [4, 3], 5, 3, 2
+    f = _proj_case(4, lens, d, R, N)
+    o = _proj(f, R, N)
+    xdbl = pins.matmul_loops(o["u"], f["w_x"])
+    np.testing.assert_allclose(o["dt_in"], xdbl[:, :R], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(o["B"], xdbl[:, R:R + N], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(o["C"], xdbl[:, R + N:], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(o["dt"], pins.matmul_loops(xdbl[:, :R], f["w_dt"]), rtol=1e-13, atol=1e-14)
+
+
+def test_oracle_project_column_order_one_hot():
+    """One-hot weights pick single u columns: dt_in, B, C come from the first R, next N and last N
+    columns of w_x in that order, and dt_in multiplies w_dt from the left (exact)."""
+    lens, d, R, N = [5, 6], 8, 2, 3
+    f = _proj_case(5, lens, d, R, N)
+    P = R + 2 * N
+    f["w_x"] = np.zeros((d, P))
+    pick = [7, 0, 3, 5, 1, 6, 2, 4]  # output column j reads u column pick[j]
+    for j in range(P):
+        f["w_x"][pick[j], j] = 1.0
+    f["w_dt"] = np.zeros((R, d))
+    f["w_dt"][1, :] = 1.0  # every dt channel = dt_in column 1
+    o = _proj(f, R, N)
+    u = o["u"]
+    assert np.array_equal(o["dt_in"], u[:, pick[:R]])
+    assert np.array_equal(o["B"], u[:, pick[R:R + N]])
+    assert np.array_equal(o["C"], u[:, pick[R + N:]])
+    assert np.array_equal(o["dt"], np.repeat(u[:, [pick[1]]], d, axis=1))
+
+
+def test_oracle_project_isolates_sequences():
+    lens, d, R, N = [6, 5, 7], 4, 2, 2
+    f = _proj_case(6, lens, d, R, N)
+    o1 = _proj(f, R, N)
+    f["x"][6:11] += 1.0  # perturb the middle sequence only
+    o2 = _proj(f, R, N)
+    for k in ("u", "dt", "B", "C"):
+        assert np.array_equal(o1[k][:6], o2[k][:6]) and np.array_equal(o1[k][11:], o2[k][11:]), k
+        assert not np.array_equal(o1[k][6:11], o2[k][6:11]), k
