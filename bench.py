@@ -88,6 +88,7 @@ PREFILL_PROFILE_SUFFIX = "__m130_prefill_8x2048_d1536_N16_bf16.txt"  # profiles/
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d8192_N16_bf16.txt")
 PROFILE_REPLAY = os.path.join(ROOT, "profiles", "k_decode_replay__m7b_decode_b256_d8192_N16_W4_bf16.txt")
 PROFILE_BACKWARD = os.path.join(ROOT, "profiles", "k_row_bwd__m130_backward_8x2048_d1536_N16_bf16.txt")
+PROFILE_PROJECT = os.path.join(ROOT, "profiles", "k_project__m130_project_8x2048_d1536_R48_N16_bf16.txt")
 
 
 def counted_traffic(profile_path):
@@ -416,6 +417,63 @@ def bench_backward(args):
         io_bytes=io_bytes, io_GBs_standalone=round(io_bytes / (ms_b * 1e-3) / 1e9, 1))
 
 
+def project_alg_bytes(T, S, d, N, R):
+    """HBM bytes one k_project launch must move: x in, dt, B, C out (bf16), the re-laid weights,
+    the conv parameters, the initial conv state and cu_seqlens."""
+    P = R + 2 * N
+    Pp = -(-P // 16) * 16
+    dk = -(-d // 32) * 32
+    Rp = -(-R // 32) * 32
+    return T * d * 2 * 2 + 2 * T * N * 2 + (Pp * dk + d * Rp) * 2 + d * 5 * 4 + S * d * 3 * 4 + (S + 1) * 4
+
+
+def bench_project(args):
+    """The dt/B/C projections (conv activation x w_x, dt_in x w_dt on the matrix cores) at the 130m
+    layer shape (T 16384, d 1536, dt_rank 48, N 16) and the 1.4B one (d 4096, dt_rank 128)."""
+    import torch
+
+    import selective_state_space_causal_amd as mm
+    from selective_state_space_causal_amd import inputs
+
+    out = {}
+    for name, S, L, d, R in (("m130", 8, 2048, 1536, 48), ("m1p4b", 8, 2048, 4096, 128)):
+        N = 16
+        T = S * L
+        rng = np.random.default_rng(3)
+        x = dev(inputs.token_tensor(0, 1, (0, T), (0, d), "bf16"))
+        p = inputs.params(0, d, N, 4)
+        w_x = dev(inputs.f32_to_bf16_bits((rng.standard_normal((d, R + 2 * N)) / np.sqrt(d)).astype(np.float32)))
+        w_dt = dev(inputs.f32_to_bf16_bits((rng.standard_normal((R, d)) / np.sqrt(R)).astype(np.float32)))
+        cu = dev(inputs.cu_from_lengths([L] * S))
+        cs = torch.zeros((S, d, 3), device="cuda")
+        cw, cb = dev(p["conv_w"]), dev(p["conv_b"])
+        dt = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        Bo = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+        Co = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(int(mm.load().mamba_mixer_project_workspace_bytes(d, N, R)), 1), dtype=torch.uint8,
+                         device="cuda")
+        ms, kern = _time_calls(lambda ev: mm.project(x, cw, cb, cu, cs, w_x, w_dt, dt=dt, B=Bo, C=Co, workspace=ws,
+                                                     events=ev), 2, ["k_proj_pack", "k_project"], reps=20)
+        kp = kern["k_project"]
+        alg = project_alg_bytes(T, S, d, N, R)
+        gbs = alg / (kp * 1e-3) / 1e9
+        flops = 2.0 * T * d * (R + 2 * N) + 2.0 * T * R * d
+        out[name] = dict(
+            workload=f"dt/B/C projections: {S} x {L} tokens, d_inner {d}, dt_rank {R}, d_state {N}, bf16",
+            ms=round(ms, 4), kernels_ms={k: round(v, 4) for k, v in kern.items()},
+            tokens_per_s=round(T / (ms * 1e-3), 1),
+            roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(gbs / HBM_PEAK_GBS, 4),
+                          traffic=counted_traffic(PROFILE_PROJECT) if name == "m130" else None,
+                          kernel="k_project", kernel_ms=round(kp, 4), alg_bytes_per_launch=alg,
+                          mfma_view=dict(achieved_TFLOPs=round(flops / (kp * 1e-3) / 1e12, 2), peak_TFLOPs=2500.0,
+                                         note="algorithmic bf16 FLOP (2 T d (R+2N) + 2 T R d); the kernel issues "
+                                              "twice that (high and low operand parts)")))
+        del x, dt, Bo, Co, ws, w_x, w_dt
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(args):
     """Batch-256 decode: a 512-token prefill initialises the states, then 128 decode steps.
 
@@ -667,6 +725,9 @@ def main():
     ap.add_argument("--no-other-prefills", action="store_true",
                     help="skip the context prefill rates of the other configurations")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward timing")
+    ap.add_argument("--no-project", action="store_true", help="skip the projection timing")
+    ap.add_argument("--only-project", action="store_true",
+                    help="only the projection timing (the kernel-trace and counter runs of its profile)")
     ap.add_argument("--only-backward", action="store_true",
                     help="only the backward timing (the kernel-trace and counter runs of its profile)")
     ap.add_argument("--decode-flushed-only", action="store_true",
@@ -701,6 +762,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     mm.load()
     log(f"[bench] {mm.version()} on {torch.cuda.get_device_name(0)}")
+    if args.only_project:
+        print(json.dumps(dict(metric=METRIC, note="projection-only diagnostic run (--only-project); no headline value",
+                              project=bench_project(args))), flush=True)
+        return
     if args.only_backward:
         print(json.dumps(dict(metric=METRIC, note="backward-only diagnostic run (--only-backward); no headline value",
                               backward=bench_backward(args))), flush=True)
@@ -715,6 +780,8 @@ def main():
         out["other_prefills"] = bench_other_prefills(args)
     if not args.no_prefill and not args.no_backward:
         out["backward"] = bench_backward(args)
+    if not args.no_prefill and not args.no_project:
+        out["project"] = bench_project(args)
     if not args.no_decode:
         out["decode"] = decode_result(args) if not args.decode_flushed_only else bench_decode(args)
     if not args.no_cpu_baseline:

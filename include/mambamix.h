@@ -311,6 +311,41 @@ int mamba_mixer_prefill_train(const void* x, const void* z, const void* dt, cons
                               void* stream, void* const* events, int32_t n_events);
 /* Bytes of the checkpoints of a prefill of S sequences and T tokens with d channels. */
 size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d);
+/*
+ * mamba_mixer_project -- the input-dependent projections that produce the scan's dt, B and C
+ * from x, in the layer order of the TensorRT Mamba tensor-parallel builder (builder page,
+ * _add_mamba_tp_layer): the conv activation u = SiLU(conv(x)) (the same window, weights and
+ * initial conv state as the mixer), then dt_in = u w_dt_in, B = u w_B, C = u w_C, and
+ * dt = dt_in w_dt_out.  The outputs are exactly what mamba_mixer_prefill takes: dt before
+ * dt_bias (the mixer adds it before its softplus, as the builder adds dt_proj_bias), B and C.
+ * In a tensor-parallel layer the builder all-reduces dt_in, B and C between the two products;
+ * on one GPU nothing is reduced.
+ *
+ *   x            [T, d]      bf16   raw SSM-path input (before the conv), 16-byte aligned
+ *   conv_w [d, K], conv_b [d]  f32  16-byte aligned;  cu_seqlens [S+1]
+ *   conv_state   [S, d, K-1] f32    the INITIAL conv state (read only)
+ *   w_x          [d, R+2N]   bf16   input-major: columns 0..R-1 are w_dt_in, then w_B, then w_C
+ *   w_dt         [R, d]      bf16   w_dt_out
+ *   dt           [T, d]      bf16   out
+ *   B, C         [T, N]      bf16   out
+ *   workspace    mamba_mixer_project_workspace_bytes(d, N, R) bytes, 256-byte aligned (the
+ *                weights re-laid for the matrix cores; contents on entry do not matter)
+ * Both products run on the matrix cores (bf16 MFMA, fp32 accumulation); the computed operands
+ * u and dt_in enter as bf16 high + low parts, so the products have fp32-quality operands and
+ * the outputs are rounded once, to bf16 (nearest even).
+ * Limits: io MM_IO_BF16 only, d a multiple of 16, 1 <= R <= 256 (else MM_ERR_UNSUPPORTED).
+ * T == 0 or d == 0 is a successful no-op.  Outputs overlapping an input or one another are
+ * MM_ERR_ALIAS.  Two kernels are enqueued (weight re-layout, projection); events, n_events are
+ * optional as in mamba_mixer_prefill_ex (n = 2: events[0] before the first kernel, events[1]
+ * between them, events[2] after the second).
+ */
+int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                        const float* conv_state, const void* w_x, const void* w_dt, void* dt, void* B, void* C,
+                        int32_t S, int64_t T, int32_t d, int32_t N, int32_t R, int32_t K, int32_t io_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                        int32_t n_events);
+/* Workspace bytes of mamba_mixer_project (0 for invalid sizes).  Host only. */
+size_t mamba_mixer_project_workspace_bytes(int32_t d, int32_t N, int32_t R);
 /* Static text for a status code (never NULL).  Host only. */
 const char* mamba_mixer_status_string(int status);
 

@@ -73,6 +73,10 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_prefill_train.restype = ctypes.c_int
     lib.mamba_mixer_checkpoint_bytes.argtypes = [i32, i64, i32]
     lib.mamba_mixer_checkpoint_bytes.restype = sz
+    lib.mamba_mixer_project.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, P, sz, P, P, i32]
+    lib.mamba_mixer_project.restype = ctypes.c_int
+    lib.mamba_mixer_project_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.mamba_mixer_project_workspace_bytes.restype = sz
     lib.mamba_mixer_status_string.argtypes = [ctypes.c_int]
     lib.mamba_mixer_status_string.restype = ctypes.c_char_p
     lib.mamba_mixer_version.argtypes = []
@@ -315,6 +319,50 @@ def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqle
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_prefill_backward")
     return g
+
+
+def project(x, conv_w, conv_b, cu_seqlens, conv_state, w_x, w_dt, dt=None, B=None, C=None, workspace=None,
+            stream=None, events=None):
+    """dt [T, d], B, C [T, N] (bf16) from x [T, d] (bf16): the conv activation times w_x [d, R + 2N]
+    (columns: w_dt_in, w_B, w_C) and dt_in times w_dt [R, d], on the matrix cores.  conv_state is the
+    initial conv state [S, d, 3] (read only).  Returns (dt, B, C)."""
+    import torch
+
+    T, d = x.shape
+    S = cu_seqlens.shape[0] - 1
+    R = w_dt.shape[0]
+    P = w_x.shape[1]
+    if (P - R) % 2 != 0 or P <= R:
+        raise ValueError(f"w_x has {P} columns; expected R + 2N with R = {R}")
+    N = (P - R) // 2
+    _check(x, (T, d), torch.bfloat16, "x")
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(conv_b, (d,), torch.float32, "conv_b")
+    _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(w_x, (d, P), torch.bfloat16, "w_x")
+    _check(w_dt, (R, d), torch.bfloat16, "w_dt")
+    if dt is None:
+        dt = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+    if B is None:
+        B = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if C is None:
+        C = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check(dt, (T, d), torch.bfloat16, "dt")
+    _check(B, (T, N), torch.bfloat16, "B")
+    _check(C, (T, N), torch.bfloat16, "C")
+    need = int(load().mamba_mixer_project_workspace_bytes(d, N, R))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    rc = load().mamba_mixer_project(
+        _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(w_x), _ptr(w_dt), _ptr(dt),
+        _ptr(B), _ptr(C), S, T, d, N, R, CONV_K, MM_IO_BF16, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream),
+        (ctypes.c_void_p * len(events))(*events) if events is not None else None,
+        len(events) if events is not None else 0)
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_project")
+    return dt, B, C
 
 
 def decode(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y=None, stream=None):

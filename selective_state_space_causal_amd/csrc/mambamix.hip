@@ -25,6 +25,7 @@
 #include "mm_decode.h"
 #include "mm_device.h"
 #include "mm_prefill.h"
+#include "mm_project.h"
 #include "mm_row.h"
 
 namespace mm {
@@ -458,6 +459,32 @@ struct Span {
   size_t n;
 };
 
+// ---------------------------------------------------------------- projections
+
+struct ProjPlan {
+  int P, Pp, dk, Rp;
+  size_t off_wx, off_wdt, total;
+};
+
+void make_proj_plan(ProjPlan& p, int d, int N, int R) {
+  p.P = R + 2 * N;
+  p.Pp = static_cast<int>(cdiv(p.P, 16) * 16);
+  p.dk = static_cast<int>(cdiv(d, kProjK) * kProjK);
+  p.Rp = static_cast<int>(cdiv(R, kProjK) * kProjK);
+  size_t off = 0;
+  p.off_wx = off; off += align256(static_cast<size_t>(p.Pp) * p.dk * 2);
+  p.off_wdt = off; off += align256(static_cast<size_t>(d) * p.Rp * 2);
+  p.total = off;
+}
+
+int check_proj_sizes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t R, int32_t K, int32_t io) {
+  const int rc = check_prefill_sizes(S, T, d, N, K, io);
+  if (rc != MM_OK) return rc;
+  if (R < 0) return MM_ERR_DIM;
+  if (io != MM_IO_BF16 || R < 1 || R > kProjMaxR || d % 16 != 0) return MM_ERR_UNSUPPORTED;
+  return MM_OK;
+}
+
 }  // namespace
 }  // namespace mm
 
@@ -767,6 +794,75 @@ int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, c
   const StageEvents evs{events, n_events, 0};
   if (io_dtype == MM_IO_BF16) return launch_backward<uint16_t>(p, a, ws, st, evs);
   return launch_backward<float>(p, a, ws, st, evs);
+}
+
+size_t mamba_mixer_project_workspace_bytes(int32_t d, int32_t N, int32_t R) {
+  if (d < 0 || N < 1 || N > MM_MAX_N || R < 1 || R > kProjMaxR) return 0;
+  ProjPlan p{};
+  make_proj_plan(p, d, N, R);
+  return p.total;
+}
+
+int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                        const float* conv_state, const void* w_x, const void* w_dt, void* dt, void* B, void* C,
+                        int32_t S, int64_t T, int32_t d, int32_t N, int32_t R, int32_t K, int32_t io_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                        int32_t n_events) {
+  int rc = check_proj_sizes(S, T, d, N, R, K, io_dtype);
+  if (rc != MM_OK) return rc;
+  if (T == 0 || d == 0) return MM_OK;
+  const size_t P = static_cast<size_t>(R) + 2 * N;
+  const size_t ntd = static_cast<size_t>(T) * d * 2, ntn = static_cast<size_t>(T) * N * 2;
+  const Span in[] = {{x, ntd}, {conv_w, static_cast<size_t>(d) * kK * 4}, {conv_b, static_cast<size_t>(d) * 4},
+                     {cu_seqlens, static_cast<size_t>(S + 1) * 4}, {conv_state, static_cast<size_t>(S) * d * kKS * 4},
+                     {w_x, static_cast<size_t>(d) * P * 2}, {w_dt, static_cast<size_t>(R) * d * 2}};
+  const Span out[] = {{dt, ntd}, {B, ntn}, {C, ntn}};
+  for (const Span& v : in)
+    if (v.p == nullptr) return MM_ERR_NULL;
+  for (const Span& v : out)
+    if (v.p == nullptr) return MM_ERR_NULL;
+  // 16-byte rows of x, conv_w and conv_b are read whole
+  if (!aligned(x, 16) || !aligned(conv_w, 16) || !aligned(conv_b, 16)) return MM_ERR_ALIGN;
+  if (!aligned(cu_seqlens, 4) || !aligned(conv_state, 4)) return MM_ERR_ALIGN;
+  const void* two[] = {w_x, w_dt, dt, B, C};
+  for (const void* q : two)
+    if (!aligned(q, 2)) return MM_ERR_ALIGN;
+  for (size_t i = 0; i < 3; ++i) {
+    for (const Span& v : in)
+      if (overlap(out[i].p, out[i].n, v.p, v.n)) return MM_ERR_ALIAS;
+    for (size_t k = i + 1; k < 3; ++k)
+      if (overlap(out[i].p, out[i].n, out[k].p, out[k].n)) return MM_ERR_ALIAS;
+  }
+  ProjPlan p{};
+  make_proj_plan(p, d, N, R);
+  if (workspace == nullptr || workspace_bytes < p.total) return MM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MM_ERR_ALIGN;
+  if (cdiv(T, kProjTokens) > INT32_MAX) return MM_ERR_DIM;
+  if (events != nullptr && n_events < 3) return MM_ERR_DIM;
+  StageEvents evs{events, n_events, 0};
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* wxT = reinterpret_cast<uint16_t*>(ws + p.off_wx);
+  uint16_t* wdtT = reinterpret_cast<uint16_t*>(ws + p.off_wdt);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t npack = static_cast<int64_t>(p.Pp) * p.dk + static_cast<int64_t>(d) * p.Rp;
+  evs.mark(st);
+  hipLaunchKernelGGL(k_proj_pack, dim3(static_cast<unsigned>(cdiv(npack, kBlock))), dim3(kBlock), 0, st,
+                     static_cast<const uint16_t*>(w_x), static_cast<const uint16_t*>(w_dt), wxT, wdtT, d,
+                     static_cast<int>(P), p.Pp, p.dk, R, p.Rp);
+  const size_t lds = proj_lds_bytes(p.Pp, p.Rp);
+  const int nt = p.Pp / 16;
+  auto kern = nt <= 6 ? k_project<6> : (nt <= 12 ? k_project<12> : k_project<18>);
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(lds)) != hipSuccess)
+    return MM_ERR_HIP;
+  evs.mark(st);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(cdiv(T, kProjTokens))), dim3(kProjThreads), lds, st,
+                     static_cast<const uint16_t*>(x), conv_w, conv_b, cu_seqlens, conv_state, wxT, wdtT,
+                     static_cast<uint16_t*>(dt), static_cast<uint16_t*>(B), static_cast<uint16_t*>(C), S, T, d, N, R,
+                     p.dk, p.Rp, nt);
+  evs.mark(st);
+  return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }
 
 }  // extern "C"

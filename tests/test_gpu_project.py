@@ -1,0 +1,94 @@
+"""The dt/B/C projections on the matrix cores against the oracle's fp64 products.
+
+Tolerance: |g - r| <= 4e-3 |r| + 2e-4 rms(r) per output.  The products run with fp32-quality
+operands (u and dt_in split into bf16 high and low parts) and fp32 accumulation, so the error is
+the rounding of the outputs to bf16 (at most half an ulp, 2^-8 = 3.9e-3 relative) plus fp32
+rounding of the sums.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_causal_amd as mm
+from selective_state_space_causal_amd import inputs
+from tests.gpu_util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, lens, d, N, R):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    x = inputs.token_tensor(seed, 1, (0, T), (0, d), "bf16")
+    p = inputs.params(seed, d, N, 4)
+    cs = rng.standard_normal((len(lens), d, 3)).astype(np.float32)
+    cs = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(cs)).reshape(cs.shape)
+    w_x = inputs.f32_to_bf16_bits((rng.standard_normal((d, R + 2 * N)) / np.sqrt(d)).astype(np.float32))
+    w_dt = inputs.f32_to_bf16_bits((rng.standard_normal((R, d)) / np.sqrt(R)).astype(np.float32))
+    return dict(x=x, conv_w=p["conv_w"], conv_b=p["conv_b"], cu=inputs.cu_from_lengths(lens), cs=cs, w_x=w_x,
+                w_dt=w_dt, T=T, d=d, N=N, R=R)
+
+
+def _close(g, r, what):
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    err = np.abs(g - r)
+    bound = 4e-3 * np.abs(r) + 2e-4 * rms
+    worst = float(np.max(err / np.maximum(bound, 1e-300))) if r.size else 0.0
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    assert np.all(err <= bound), f"{what}: max err/bound {worst:.3g}"
+    return worst
+
+
+def _run(f):
+    dt, B, C = mm.project(dev(f["x"]), dev(f["conv_w"]), dev(f["conv_b"]), dev(f["cu"]), dev(f["cs"]),
+                          dev(f["w_x"]), dev(f["w_dt"]))
+    torch.cuda.synchronize()
+    return host(dt), host(B), host(C)
+
+
+CASES = [
+    ([37, 1, 0, 64, 2, 3, 90, 17], 48, 16, 3),   # short and empty sequences, d not a multiple of 32
+    ([300, 200], 1536, 16, 48),                   # the 130m layer's d_inner and dt_rank
+    ([100], 256, 8, 256),                         # the largest dt_rank, N < 16
+    ([70, 5], 64, 16, 33),                        # dt_rank padded to 64, 65 output columns
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_project_vs_oracle(ci):
+    lens, d, N, R = CASES[ci]
+    f = _case(60 + ci, lens, d, N, R)
+    log(f"[proj] case {ci}: lens={lens} d={d} N={N} R={R}")
+    dt, B, C = _run(f)
+    o = oracle.project(f["x"], f["conv_w"], f["conv_b"], f["cu"], f["cs"], f["w_x"], f["w_dt"], R, N)
+    w = [_close(dt, o["dt"], "dt"), _close(B, o["B"], "B"), _close(C, o["C"], "C")]
+    log(f"[proj] case {ci}: worst err/bound dt {w[0]:.3g} B {w[1]:.3g} C {w[2]:.3g}")
+
+
+def test_project_m130_shape():
+    """8 x 2048 tokens, d_inner 1536, dt_rank 48, N 16: every output against the oracle."""
+    lens, d, N, R = [2048] * 8, 1536, 16, 48
+    f = _case(130, lens, d, N, R)
+    dt, B, C = _run(f)
+    o = oracle.project(f["x"], f["conv_w"], f["conv_b"], f["cu"], f["cs"], f["w_x"], f["w_dt"], R, N)
+    w = [_close(dt, o["dt"], "dt"), _close(B, o["B"], "B"), _close(C, o["C"], "C")]
+    log(f"[proj] m130 shape: worst err/bound dt {w[0]:.3g} B {w[1]:.3g} C {w[2]:.3g}")
+
+
+def test_project_feeds_prefill():
+    """The projection's outputs are the prefill's dt, B, C: a packed call on them equals separate
+    calls (the projections, like the scan, keep sequences apart) bit for bit."""
+    lens, d, N, R = [50, 77], 64, 16, 8
+    f = _case(7, lens, d, N, R)
+    dt, B, C = mm.project(dev(f["x"]), dev(f["conv_w"]), dev(f["conv_b"]), dev(f["cu"]), dev(f["cs"]),
+                          dev(f["w_x"]), dev(f["w_dt"]))
+    for s in range(2):
+        a, b = int(f["cu"][s]), int(f["cu"][s + 1])
+        dts, Bs, Cs = mm.project(dev(f["x"][a:b]), dev(f["conv_w"]), dev(f["conv_b"]),
+                                 torch.tensor([0, b - a], dtype=torch.int32, device="cuda"), dev(f["cs"][s:s + 1]),
+                                 dev(f["w_x"]), dev(f["w_dt"]))
+        torch.cuda.synchronize()
+        assert torch.equal(dts, dt[a:b]) and torch.equal(Bs, B[a:b]) and torch.equal(Cs, C[a:b]), s

@@ -295,3 +295,31 @@ def test_prefill_train_validation(lib):
     q[14] = ctypes.c_void_p(p[14].value + 2)
     assert call(q) == MM_ERR_ALIGN
     assert call([ctypes.c_void_p(0)] * 15, T=0) == 0
+
+
+def test_project_validation(lib):
+    # x, conv_w, conv_b, cu, conv_state, w_x, w_dt, dt, B, C
+    p = _ptrs(10)
+    need = lib.mamba_mixer_project_workspace_bytes(64, 16, 4)
+    assert need >= (48 * 64 + 64 * 32) * 2  # w_x^T padded to 48 x 64, w_dt^T 64 x 32, bf16
+    ws = ctypes.c_void_p(0x7F000000)
+
+    def call(q, S=2, T=100, d=64, N=16, R=4, K=4, io=1, wsb=need, w=ws):
+        return lib.mamba_mixer_project(*q, S, T, d, N, R, K, io, w, wsb, None, None, 0)
+    assert call(p, io=0) == MM_ERR_UNSUPPORTED       # fp32 io: not supported
+    assert call(p, d=40) == MM_ERR_UNSUPPORTED       # d not a multiple of 16
+    assert call(p, R=0) == MM_ERR_UNSUPPORTED
+    assert call(p, R=257) == MM_ERR_UNSUPPORTED
+    assert call(p, S=0) == MM_ERR_DIM
+    for i in range(10):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert call(q) == MM_ERR_NULL, i
+    q = list(p)
+    q[0] = ctypes.c_void_p(p[0].value + 2)  # x needs 16-byte rows
+    assert call(q) == MM_ERR_ALIGN
+    q = list(p)
+    q[7] = q[0]  # dt on top of x
+    assert call(q) == MM_ERR_ALIAS
+    assert call(p, wsb=need - 1) == MM_ERR_WORKSPACE
+    assert call([ctypes.c_void_p(0)] * 10, T=0) == 0
