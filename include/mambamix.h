@@ -326,7 +326,7 @@ size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d);
  *   conv_state   [S, d, K-1] f32    the INITIAL conv state (read only)
  *   w_x          [d, R+2N]   bf16   input-major: columns 0..R-1 are w_dt_in, then w_B, then w_C
  *   w_dt         [R, d]      bf16   w_dt_out
- *   dt           [T, d]      bf16   out
+ *   dt           [T, d]      bf16   out, 16-byte aligned
  *   B, C         [T, N]      bf16   out
  *   workspace    mamba_mixer_project_workspace_bytes(d, N, R) bytes, 256-byte aligned (the
  *                weights re-laid for the matrix cores; contents on entry do not matter)

@@ -821,10 +821,10 @@ int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b,
     if (v.p == nullptr) return MM_ERR_NULL;
   for (const Span& v : out)
     if (v.p == nullptr) return MM_ERR_NULL;
-  // 16-byte rows of x, conv_w and conv_b are read whole
-  if (!aligned(x, 16) || !aligned(conv_w, 16) || !aligned(conv_b, 16)) return MM_ERR_ALIGN;
+  // x, conv_w and conv_b are read, and dt written, in 16-byte pieces
+  if (!aligned(x, 16) || !aligned(conv_w, 16) || !aligned(conv_b, 16) || !aligned(dt, 16)) return MM_ERR_ALIGN;
   if (!aligned(cu_seqlens, 4) || !aligned(conv_state, 4)) return MM_ERR_ALIGN;
-  const void* two[] = {w_x, w_dt, dt, B, C};
+  const void* two[] = {w_x, w_dt, B, C};
   for (const void* q : two)
     if (!aligned(q, 2)) return MM_ERR_ALIGN;
   for (size_t i = 0; i < 3; ++i) {

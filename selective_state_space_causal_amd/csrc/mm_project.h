@@ -90,7 +90,10 @@ __global__ void __launch_bounds__(kBlock) k_proj_pack(const uint16_t* __restrict
 // and conv parameters [40] float4 (32 channels' weights, then 8 x 4 biases); the K quarters'
 // partial accumulators [row tile][quarter 1..3][Pp / 16][64 lanes] floatx4; dt_in's high and
 // low bf16 parts [kProjTokens][Rp + 8] (rows padded to keep the 16-byte reads aligned).
-constexpr size_t kProjWaveBytes = kProjXRows * kProjXStride * 2 + 40 * 16;
+constexpr int kProjOStride = 32 + 8;  // bf16 per row of a wave's dt output tile [32 tokens][32 channels]
+constexpr size_t kProjWaveBytes = (kProjXRows * kProjXStride * 2 + 40 * 16 > kProjTokens * kProjOStride * 2)
+                                      ? kProjXRows * kProjXStride * 2 + 40 * 16
+                                      : kProjTokens * kProjOStride * 2;
 __host__ __device__ inline size_t proj_red_bytes(int Pp) {
   return static_cast<size_t>(kProjRowTiles) * (kProjKSplit - 1) * (Pp / 16) * kWave * 16;
 }
@@ -107,7 +110,7 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
 // NT = Pp / 16 output column tiles of the first product, at most MAXNT (6, 12 or 18: the
 // accumulators of MAXNT tiles stay in registers)
 template <int MAXNT>
-__global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(MAXNT <= 12 ? 4 : 2))) k_project(
+__global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(MAXNT <= 6 ? 4 : (MAXNT <= 12 ? 3 : 2)))) k_project(
     const uint16_t* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     const int32_t* __restrict__ cu, const float* __restrict__ conv_state, const uint16_t* __restrict__ wxP,
     const uint16_t* __restrict__ wdtP, uint16_t* __restrict__ dt, uint16_t* __restrict__ B, uint16_t* __restrict__ C,
@@ -157,18 +160,37 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
   const int ks0 = kq * nks / kProjKSplit, ks1 = (kq + 1) * nks / kProjKSplit;
   // A wave holding one of a sequence's first three tokens takes the loop that reads the conv
   // state; every other wave runs the loop without that branch.
+  // the staging loads of K step ks: x rows and conv parameters (channels past d read valid
+  // ones; their u is 0), issued one step ahead of their use
+  struct StepLoads {
+    uint4 va, vb;
+    float4 vp;
+  };
+  auto step_load = [&](int ks, StepLoads& L) {
+    const int c0 = ks * kProjK;
+    const int cx = c0 + q4 * 8 < d ? c0 : d - 8 - q4 * 8;
+    L.va = *reinterpret_cast<const uint4*>(xa + cx);
+    L.vb = *reinterpret_cast<const uint4*>(xb + cx);
+    const int pc = lane < kProjK ? c0 + lane : c0 + (lane - kProjK) * 4;  // weight channel, or first bias
+    const float* psrc = lane < kProjK ? conv_w + static_cast<int64_t>(pc < d ? pc : d - 1) * kK
+                                      : conv_b + (pc < d ? pc : d - 4);
+    L.vp = *reinterpret_cast<const float4*>(psrc);
+  };
   auto kloop = [&](auto state) {
     constexpr bool STATE = decltype(state)::value;
+    StepLoads cur, nxt;
+    if (ks0 < ks1) step_load(ks0, cur);
     for (int ks = ks0; ks < ks1; ++ks) {
       const int c0 = ks * kProjK;
-      // stage x rows and conv parameters (channels past d read valid ones; their u is 0)
-      const int cx = c0 + q4 * 8 < d ? c0 : d - 8 - q4 * 8;
-      const uint4 va = *reinterpret_cast<const uint4*>(xa + cx);
-      const uint4 vb = *reinterpret_cast<const uint4*>(xb + cx);
-      const int pc = lane < kProjK ? c0 + lane : c0 + (lane - kProjK) * 4;  // weight channel, or first bias
-      const float* psrc = lane < kProjK ? conv_w + static_cast<int64_t>(pc < d ? pc : d - 1) * kK
-                                        : conv_b + (pc < d ? pc : d - 4);
-      const float4 vp = *reinterpret_cast<const float4*>(psrc);
+      step_load(ks + 1 < ks1 ? ks + 1 : ks, nxt);  // on the last step a harmless repeat
+      // this step's w_x operands, used after the u arithmetic
+      uint4 wb[kMaxNT];
+      const uint16_t* wk = wxP + (static_cast<int64_t>(ks * 4 + kg) * Pp + row) * 8;
+#pragma unroll
+      for (int j = 0; j < kMaxNT; ++j)
+        if (j < NT) wb[j] = *reinterpret_cast<const uint4*>(wk + j * 16 * 8);
+      const uint4 va = cur.va, vb = cur.vb;
+      const float4 vp = cur.vp;
       *reinterpret_cast<uint4*>(xt + (lane >> 2) * kProjXStride + q4 * 8) = va;
       if (lane < 4 * kKS) *reinterpret_cast<uint4*>(xt + (16 + (lane >> 2)) * kProjXStride + q4 * 8) = vb;
       if (lane < 40) cpar[lane] = vp;
@@ -212,16 +234,15 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
         ua[e] = hi;
         ul[e] = lo;
       }
-      const uint16_t* wk = wxP + (static_cast<int64_t>(ks * 4 + kg) * Pp + row) * 8;
+      // the high parts over all column tiles, then the low parts: consecutive MFMAs are independent
 #pragma unroll
-      for (int j = 0; j < kMaxNT; ++j) {
-        if (j < NT) {
-          const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wk + j * 16 * 8));
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, wb, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, wb, acc[j], 0, 0, 0);
-        }
-      }
+      for (int j = 0; j < kMaxNT; ++j)
+        if (j < NT) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kMaxNT; ++j)
+        if (j < NT) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this step's tile reads before the next staging
+      cur = nxt;
     }
   };
   if (__any(back < kKS)) kloop(std::true_type{});
@@ -273,37 +294,54 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
   }
   __syncthreads();
 
-  // dt = dt_in x w_dt: the waves take 16-channel tiles w, w + 8, ...
+  // dt = dt_in x w_dt: wave w takes a contiguous run of 16-channel tiles, two at a time; the
+  // 32 tokens x 32 channels of a tile pair go through the wave's LDS area so that they leave as
+  // 16-byte row pieces (a quarter wave writes four 64-byte row segments)
   constexpr int kMaxKR = kProjMaxR / kProjK;
   const int nkr = Rp / kProjK;
   const int ntiles = d / 16;
-  for (int nt = w; nt < ntiles; nt += kProjWaves) {
-    const int cch = nt * 16 + row;
-    bf16x8_t wv[kMaxKR];
+  const int per_wave = (ntiles + kProjWaves - 1) / kProjWaves;
+  const int nt_lo = w * per_wave;
+  const int nt_hi = nt_lo + per_wave < ntiles ? nt_lo + per_wave : ntiles;
+  uint16_t* ot = reinterpret_cast<uint16_t*>(smem + w * kProjWaveBytes);  // [kProjTokens][kProjOStride]
+  for (int nt = nt_lo; nt < nt_hi; nt += 2) {
 #pragma unroll
-    for (int kk = 0; kk < kMaxKR; ++kk)
-      if (kk < nkr)
-        wv[kk] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(wdtP + (static_cast<int64_t>(kk * 4 + kg) * d + cch) * 8));
+    for (int h = 0; h < 2; ++h) {
+      const int ntile = nt + h < nt_hi ? nt + h : nt;  // a lone last tile computes twice, stores once
+      const int cch = ntile * 16 + row;
+      bf16x8_t wv[kMaxKR];
 #pragma unroll
-    for (int m = 0; m < kProjRowTiles; ++m) {
-      floatx4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int kk = 0; kk < kMaxKR; ++kk)
+        if (kk < nkr)
+          wv[kk] = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(wdtP + (static_cast<int64_t>(kk * 4 + kg) * d + cch) * 8));
 #pragma unroll
-      for (int kk = 0; kk < kMaxKR; ++kk) {
-        if (kk < nkr) {
-          const size_t o = static_cast<size_t>(m * 16 + row) * dstride + kk * kProjK + kg * 8;
-          const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dh + o));
-          const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dl + o));
-          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wv[kk], a, 0, 0, 0);
-          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wv[kk], a, 0, 0, 0);
+      for (int m = 0; m < kProjRowTiles; ++m) {
+        floatx4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < kMaxKR; ++kk) {
+          if (kk < nkr) {
+            const size_t o = static_cast<size_t>(m * 16 + row) * dstride + kk * kProjK + kg * 8;
+            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dh + o));
+            const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dl + o));
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wv[kk], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wv[kk], a, 0, 0, 0);
+          }
         }
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t tg = t0 + m * 16 + kg * 4 + i;
-        if (tg < T) dt[tg * d64 + cch] = bf16_bits(a[i]);
+        for (int i = 0; i < 4; ++i) ot[(m * 16 + kg * 4 + i) * kProjOStride + h * 16 + row] = bf16_bits(a[i]);
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile written before this wave reads it
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int tl = half * 16 + (lane >> 2), part = lane & 3;
+      const int64_t tg = t0 + tl;
+      const int ch = nt * 16 + part * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(ot + tl * kProjOStride + part * 8);
+      if (tg < T && ch < nt_hi * 16) *reinterpret_cast<uint4*>(dt + tg * d64 + ch) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile read before the next pair overwrites it
   }
 }
 
