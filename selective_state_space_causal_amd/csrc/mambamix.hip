@@ -851,7 +851,13 @@ int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b,
                      static_cast<int>(P), p.Pp, p.dk, R, p.Rp);
   const size_t lds = proj_lds_bytes(p.Pp, p.Rp);
   const int nt = p.Pp / 16;
-  auto kern = nt <= 6 ? k_project<6> : (nt <= 12 ? k_project<12> : k_project<18>);
+  const int nkr = p.Rp / kProjK;
+  using KernP = void (*)(const uint16_t*, const float*, const float*, const int32_t*, const float*, const uint16_t*,
+                         const uint16_t*, uint16_t*, uint16_t*, uint16_t*, int, int64_t, int, int, int, int, int, int);
+  static const KernP table[3][3] = {{k_project<6, 2>, k_project<6, 4>, k_project<6, 8>},
+                                    {k_project<12, 2>, k_project<12, 4>, k_project<12, 8>},
+                                    {k_project<18, 2>, k_project<18, 4>, k_project<18, 8>}};
+  const KernP kern = table[nt <= 6 ? 0 : (nt <= 12 ? 1 : 2)][nkr <= 2 ? 0 : (nkr <= 4 ? 1 : 2)];
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds)) != hipSuccess)

@@ -86,19 +86,26 @@ __global__ void __launch_bounds__(kBlock) k_proj_pack(const uint16_t* __restrict
   wdtP[i2] = r < R ? w_dt[static_cast<int64_t>(r) * d + c] : static_cast<uint16_t>(0);
 }
 
-// LDS (dynamic, sized per call): per wave the staged x rows [kProjXRows][kProjXStride] bf16
-// and conv parameters [40] float4 (32 channels' weights, then 8 x 4 biases); the K quarters'
-// partial accumulators [row tile][quarter 1..3][Pp / 16][64 lanes] floatx4; dt_in's high and
-// low bf16 parts [kProjTokens][Rp + 8] (rows padded to keep the 16-byte reads aligned).
+// LDS (dynamic, sized per call): a first region that holds, in turn, per wave two staging
+// buffers (double-buffered across K steps), each the x rows [kProjXRows][kProjXStride] bf16 and
+// conv parameters [40] float4 (32 channels' weights, then 8 x 4 biases); the K quarters' partial
+// accumulators [row tile][quarter 1..3][Pp / 16][64 lanes] floatx4; and per wave the dt output
+// tile.  After it, dt_in's high and low bf16 parts [kProjTokens][Rp + 8] (rows padded to keep
+// the 16-byte reads aligned).
 constexpr int kProjOStride = 32 + 8;  // bf16 per row of a wave's dt output tile [32 tokens][32 channels]
-constexpr size_t kProjWaveBytes = (kProjXRows * kProjXStride * 2 + 40 * 16 > kProjTokens * kProjOStride * 2)
-                                      ? kProjXRows * kProjXStride * 2 + 40 * 16
+constexpr size_t kProjStageBytes = kProjXRows * kProjXStride * 2 + 40 * 16;  // one staging buffer
+constexpr size_t kProjWaveBytes = (2 * kProjStageBytes > kProjTokens * kProjOStride * 2)
+                                      ? 2 * kProjStageBytes
                                       : kProjTokens * kProjOStride * 2;
 __host__ __device__ inline size_t proj_red_bytes(int Pp) {
   return static_cast<size_t>(kProjRowTiles) * (kProjKSplit - 1) * (Pp / 16) * kWave * 16;
 }
+__host__ __device__ inline size_t proj_region_bytes(int Pp) {
+  const size_t a = kProjWaves * kProjWaveBytes, b = proj_red_bytes(Pp);
+  return a > b ? a : b;
+}
 inline size_t proj_lds_bytes(int Pp, int Rp) {
-  return kProjWaves * kProjWaveBytes + proj_red_bytes(Pp) + static_cast<size_t>(2) * kProjTokens * (Rp + 8) * 2;
+  return proj_region_bytes(Pp) + static_cast<size_t>(2) * kProjTokens * (Rp + 8) * 2;
 }
 
 // split v into bf16 parts with hi + lo = v to about 2^-16 relative
@@ -108,8 +115,9 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
 }
 
 // NT = Pp / 16 output column tiles of the first product, at most MAXNT (6, 12 or 18: the
-// accumulators of MAXNT tiles stay in registers)
-template <int MAXNT>
+// accumulators of MAXNT tiles stay in registers); Rp / 32 K steps of the second, at most MAXKR
+// (2, 4 or 8: the w_dt operands of a tile pair stay in registers)
+template <int MAXNT, int MAXKR>
 __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(MAXNT <= 6 ? 4 : (MAXNT <= 12 ? 3 : 2)))) k_project(
     const uint16_t* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     const int32_t* __restrict__ cu, const float* __restrict__ conv_state, const uint16_t* __restrict__ wxP,
@@ -121,10 +129,14 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
   const int dstride = Rp + 8;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  uint16_t* xt = reinterpret_cast<uint16_t*>(smem + w * kProjWaveBytes);  // [kProjXRows][kProjXStride]
-  float4* cpar = reinterpret_cast<float4*>(smem + w * kProjWaveBytes + kProjXRows * kProjXStride * 2);  // [40]
-  floatx4_t* red = reinterpret_cast<floatx4_t*>(smem + kProjWaves * kProjWaveBytes);
-  uint16_t* dh = reinterpret_cast<uint16_t*>(smem + kProjWaves * kProjWaveBytes + proj_red_bytes(Pp));
+  auto xt = [&](int b) {  // staged x rows of buffer b, [kProjXRows][kProjXStride]
+    return reinterpret_cast<uint16_t*>(smem + w * kProjWaveBytes + b * kProjStageBytes);
+  };
+  auto cpar = [&](int b) {  // conv parameters of buffer b, [40]
+    return reinterpret_cast<float4*>(smem + w * kProjWaveBytes + b * kProjStageBytes + kProjXRows * kProjXStride * 2);
+  };
+  floatx4_t* red = reinterpret_cast<floatx4_t*>(smem);  // over the staging buffers, after the K loops
+  uint16_t* dh = reinterpret_cast<uint16_t*>(smem + proj_region_bytes(Pp));
   uint16_t* dl = dh + static_cast<size_t>(kProjTokens) * dstride;
   const int mt = w % kProjRowTiles;  // row tile
   const int kq = w / kProjRowTiles;  // K quarter
@@ -162,45 +174,47 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
   // state; every other wave runs the loop without that branch.
   // the staging loads of K step ks: x rows and conv parameters (channels past d read valid
   // ones; their u is 0), issued one step ahead of their use
-  struct StepLoads {
-    uint4 va, vb;
-    float4 vp;
-  };
-  auto step_load = [&](int ks, StepLoads& L) {
+  uint4 pva, pvb;  // prefetched staging data
+  float4 pvp;
+  auto step_load = [&](int ks) {
     const int c0 = ks * kProjK;
     const int cx = c0 + q4 * 8 < d ? c0 : d - 8 - q4 * 8;
-    L.va = *reinterpret_cast<const uint4*>(xa + cx);
-    L.vb = *reinterpret_cast<const uint4*>(xb + cx);
+    pva = *reinterpret_cast<const uint4*>(xa + cx);
+    pvb = *reinterpret_cast<const uint4*>(xb + cx);
     const int pc = lane < kProjK ? c0 + lane : c0 + (lane - kProjK) * 4;  // weight channel, or first bias
     const float* psrc = lane < kProjK ? conv_w + static_cast<int64_t>(pc < d ? pc : d - 1) * kK
                                       : conv_b + (pc < d ? pc : d - 4);
-    L.vp = *reinterpret_cast<const float4*>(psrc);
+    pvp = *reinterpret_cast<const float4*>(psrc);
   };
+  auto stage_write = [&](int b) {
+    *reinterpret_cast<uint4*>(xt(b) + (lane >> 2) * kProjXStride + q4 * 8) = pva;
+    if (lane < 4 * kKS) *reinterpret_cast<uint4*>(xt(b) + (16 + (lane >> 2)) * kProjXStride + q4 * 8) = pvb;
+    if (lane < 40) cpar(b)[lane] = pvp;
+  };
+  // Per K step: the staging buffer of step ks was written at the end of the previous step (its
+  // global loads issued a step before that), so neither the loads nor the LDS round trip stall
+  // the step's arithmetic.
   auto kloop = [&](auto state) {
     constexpr bool STATE = decltype(state)::value;
-    StepLoads cur, nxt;
-    if (ks0 < ks1) step_load(ks0, cur);
+    step_load(ks0 < ks1 ? ks0 : 0);
+    stage_write(0);
+    step_load(ks0 + 1 < ks1 ? ks0 + 1 : ks0);
     for (int ks = ks0; ks < ks1; ++ks) {
       const int c0 = ks * kProjK;
-      step_load(ks + 1 < ks1 ? ks + 1 : ks, nxt);  // on the last step a harmless repeat
+      const int b = (ks - ks0) & 1;
       // this step's w_x operands, used after the u arithmetic
       uint4 wb[kMaxNT];
       const uint16_t* wk = wxP + (static_cast<int64_t>(ks * 4 + kg) * Pp + row) * 8;
 #pragma unroll
       for (int j = 0; j < kMaxNT; ++j)
         if (j < NT) wb[j] = *reinterpret_cast<const uint4*>(wk + j * 16 * 8);
-      const uint4 va = cur.va, vb = cur.vb;
-      const float4 vp = cur.vp;
-      *reinterpret_cast<uint4*>(xt + (lane >> 2) * kProjXStride + q4 * 8) = va;
-      if (lane < 4 * kKS) *reinterpret_cast<uint4*>(xt + (16 + (lane >> 2)) * kProjXStride + q4 * 8) = vb;
-      if (lane < 40) cpar[lane] = vp;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging writes before its reads
       const int c = c0 + kg * 8;
       const bool live = c < d;
       float xr[4][8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xt + (row + r) * kProjXStride + kg * 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(xt(b) + (row + r) * kProjXStride + kg * 8);
         const uint32_t pv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -218,12 +232,12 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
           }
         }
       }
-      const float4 b0 = cpar[kProjK + kg * 2], b1 = cpar[kProjK + kg * 2 + 1];
+      const float4 b0 = cpar(b)[kProjK + kg * 2], b1 = cpar(b)[kProjK + kg * 2 + 1];
       const float bias[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       bf16x8_t ua, ul;  // u's high and low parts
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float4 wv = cpar[kg * 8 + e];
+        const float4 wv = cpar(b)[kg * 8 + e];
         float xc = bias[e];
         xc = __builtin_fmaf(wv.x, xr[0][e], xc);
         xc = __builtin_fmaf(wv.y, xr[1][e], xc);
@@ -241,8 +255,8 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int j = 0; j < kMaxNT; ++j)
         if (j < NT) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this step's tile reads before the next staging
-      cur = nxt;
+      if (ks + 1 < ks1) stage_write(b ^ 1);  // step ks + 1; that buffer was last read in step ks - 1
+      step_load(ks + 2 < ks1 ? ks + 2 : ks);  // near the end a harmless repeat
     }
   };
   if (__any(back < kKS)) kloop(std::true_type{});
@@ -254,6 +268,7 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
   auto red_at = [&](int q, int j) {
     return red + ((static_cast<size_t>(mt) * (kProjKSplit - 1) + (q - 1)) * NT + j) * kWave + lane;
   };
+  __syncthreads();  // every wave's K loop done: the staging buffers become the partial sums
   if (kq > 0) {
 #pragma unroll
     for (int j = 0; j < kMaxNT; ++j)
@@ -297,41 +312,68 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
   // dt = dt_in x w_dt: wave w takes a contiguous run of 16-channel tiles, two at a time; the
   // 32 tokens x 32 channels of a tile pair go through the wave's LDS area so that they leave as
   // 16-byte row pieces (a quarter wave writes four 64-byte row segments)
-  constexpr int kMaxKR = kProjMaxR / kProjK;
+  constexpr int kMaxKR = MAXKR;
   const int nkr = Rp / kProjK;
   const int ntiles = d / 16;
   const int per_wave = (ntiles + kProjWaves - 1) / kProjWaves;
   const int nt_lo = w * per_wave;
   const int nt_hi = nt_lo + per_wave < ntiles ? nt_lo + per_wave : ntiles;
   uint16_t* ot = reinterpret_cast<uint16_t*>(smem + w * kProjWaveBytes);  // [kProjTokens][kProjOStride]
-  for (int nt = nt_lo; nt < nt_hi; nt += 2) {
+  // the w_dt operands of a tile pair (a lone last tile is taken twice and stored once), loaded a
+  // pair ahead of their use
+  bf16x8_t wv[2][kMaxKR];
+  auto wdt_load = [&](int nt) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int ntile = nt + h < nt_hi ? nt + h : nt;  // a lone last tile computes twice, stores once
-      const int cch = ntile * 16 + row;
-      bf16x8_t wv[kMaxKR];
+      const int ntile = nt + h < nt_hi ? nt + h : nt;
+      const int64_t base = static_cast<int64_t>(ntile * 16 + row) * 8;
 #pragma unroll
       for (int kk = 0; kk < kMaxKR; ++kk)
         if (kk < nkr)
-          wv[kk] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(wdtP + (static_cast<int64_t>(kk * 4 + kg) * d + cch) * 8));
+          wv[h][kk] = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(wdtP + static_cast<int64_t>(kk * 4 + kg) * d * 8 + base));
+    }
+  };
+  if (nt_lo < nt_hi) wdt_load(nt_lo);
+  for (int nt = nt_lo; nt < nt_hi; nt += 2) {
+    bf16x8_t wc[2][kMaxKR];
 #pragma unroll
-      for (int m = 0; m < kProjRowTiles; ++m) {
-        floatx4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int kk = 0; kk < kMaxKR; ++kk) {
-          if (kk < nkr) {
-            const size_t o = static_cast<size_t>(m * 16 + row) * dstride + kk * kProjK + kg * 8;
-            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dh + o));
-            const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dl + o));
-            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wv[kk], a, 0, 0, 0);
-            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wv[kk], a, 0, 0, 0);
-          }
+      for (int kk = 0; kk < kMaxKR; ++kk) wc[h][kk] = wv[h][kk];
+    wdt_load(nt + 2 < nt_hi ? nt + 2 : nt);  // on the last pair a harmless repeat
+    // four independent accumulations (two tiles x two row tiles), interleaved
+    floatx4_t a[2][kProjRowTiles];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < kProjRowTiles; ++m) a[h][m] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < kMaxKR; ++kk) {
+      if (kk < nkr) {
+        bf16x8_t ah[kProjRowTiles], al[kProjRowTiles];
+#pragma unroll
+        for (int m = 0; m < kProjRowTiles; ++m) {
+          const size_t o = static_cast<size_t>(m * 16 + row) * dstride + kk * kProjK + kg * 8;
+          ah[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dh + o));
+          al[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dl + o));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ot[(m * 16 + kg * 4 + i) * kProjOStride + h * 16 + row] = bf16_bits(a[i]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int m = 0; m < kProjRowTiles; ++m) a[h][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], wc[h][kk], a[h][m], 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int m = 0; m < kProjRowTiles; ++m) a[h][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], wc[h][kk], a[h][m], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < kProjRowTiles; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ot[(m * 16 + kg * 4 + i) * kProjOStride + h * 16 + row] = bf16_bits(a[h][m][i]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile written before this wave reads it
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
