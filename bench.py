@@ -427,7 +427,7 @@ def project_alg_bytes(T, S, d, N, R):
     return T * d * 2 * 2 + 2 * T * N * 2 + (Pp * dk + d * Rp) * 2 + d * 5 * 4 + S * d * 3 * 4 + (S + 1) * 4
 
 
-def bench_project(args):
+def bench_project(args, only_m130=False):
     """The dt/B/C projections (conv activation x w_x, dt_in x w_dt on the matrix cores) at the 130m
     layer shape (T 16384, d 1536, dt_rank 48, N 16) and the 1.4B one (d 4096, dt_rank 128)."""
     import torch
@@ -436,7 +436,8 @@ def bench_project(args):
     from selective_state_space_causal_amd import inputs
 
     out = {}
-    for name, S, L, d, R in (("m130", 8, 2048, 1536, 48), ("m1p4b", 8, 2048, 4096, 128)):
+    shapes = (("m130", 8, 2048, 1536, 48), ("m1p4b", 8, 2048, 4096, 128))
+    for name, S, L, d, R in shapes[:1] if only_m130 else shapes:
         N = 16
         T = S * L
         rng = np.random.default_rng(3)
@@ -727,7 +728,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward timing")
     ap.add_argument("--no-project", action="store_true", help="skip the projection timing")
     ap.add_argument("--only-project", action="store_true",
-                    help="only the projection timing (the kernel-trace and counter runs of its profile)")
+                    help="only the projection timing at the 130m shape (the kernel-trace and counter runs of its "
+                         "profile)")
     ap.add_argument("--only-backward", action="store_true",
                     help="only the backward timing (the kernel-trace and counter runs of its profile)")
     ap.add_argument("--decode-flushed-only", action="store_true",
@@ -764,7 +766,7 @@ def main():
     log(f"[bench] {mm.version()} on {torch.cuda.get_device_name(0)}")
     if args.only_project:
         print(json.dumps(dict(metric=METRIC, note="projection-only diagnostic run (--only-project); no headline value",
-                              project=bench_project(args))), flush=True)
+                              project=bench_project(args, only_m130=True))), flush=True)
         return
     if args.only_backward:
         print(json.dumps(dict(metric=METRIC, note="backward-only diagnostic run (--only-backward); no headline value",
