@@ -89,8 +89,9 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   p.nmax = nmax_for(N);
   const int64_t nblk = cdiv(d, kWave);
   const int64_t avg = cdiv(T, S > 0 ? S : 1);
-  if (engine == MM_ENGINE_AUTO) engine = (S * nblk >= kLaneMinWaves) ? MM_ENGINE_LANE : MM_ENGINE_ROW;
+  if (engine == MM_ENGINE_AUTO) engine = (S * nblk >= kLaneMinWaves || d > kRowMaxD) ? MM_ENGINE_LANE : MM_ENGINE_ROW;
   if (engine != MM_ENGINE_LANE && engine != MM_ENGINE_ROW) return MM_ERR_UNSUPPORTED;
+  if (engine == MM_ENGINE_ROW && d > kRowMaxD) return MM_ERR_UNSUPPORTED;
   p.engine = engine;
   if (engine == MM_ENGINE_ROW) p.nmax = kRow;  // one state entry per lane of a 16-lane row
   if (chunk_len > 0) {
@@ -385,6 +386,7 @@ struct BwdPlan {
 
 int make_bwd_plan(BwdPlan& p, int64_t S, int64_t T, int d, int N, bool has_ckpt) {
   p = BwdPlan{};
+  if (d > kRowMaxD) return MM_ERR_UNSUPPORTED;
   p.nchb = static_cast<int>(cdiv(d, kRowChans));
   p.rows = cdiv(T, kRow) + S;
   int64_t g = cdiv(kBwdWgs, p.nchb > 0 ? p.nchb : 1);

@@ -25,10 +25,8 @@ __device__ __forceinline__ float ld_io(const uint16_t* p, int64_t i) {
 }
 __device__ __forceinline__ void st_io(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st_io(uint16_t* p, int64_t i, float v) {
-  // float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN
-  uint32_t u = __float_as_uint(v);
-  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  p[i] = static_cast<uint16_t>((v != v) ? 0x7FC0u : r);
+  // float32 -> bfloat16 by the hardware conversion (round to nearest even, NaN stays NaN)
+  p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
 // ---------------------------------------------------------------- math
@@ -41,15 +39,15 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 // x * sigmoid(x)
 __device__ __forceinline__ float silu(float x) { return x * rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
-// softplus(v) = log(1 + e^v).  For v > 20 it is v to within 2.1e-9.  For
-// e = e^v < 1/64 the rounding of 1 + e would cost up to ~4e-6 relative, so the
-// Taylor series e - e^2/2 + e^3/3 - e^4/4 (error < e^5/5) is used there.
+// softplus(v) = log(1 + e^v).  For e = e^v < 1/64 the rounding of 1 + e would cost
+// up to ~4e-6 relative, so the Taylor series e - e^2/2 + e^3/3 - e^4/4 (error < e^5/5)
+// is used there.  softplus(v) > v everywhere, and past v = 20 it exceeds v by less
+// than 2.1e-9: the result is the larger of v and the value at min(v, 20).
 __device__ __forceinline__ float softplus(float v) {
   const float e = exp2_hw(fminf(v, 20.0f) * kLog2e);
   const float series = e * __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, -0.25f, 1.0f / 3.0f), -0.5f), 1.0f);
   const float viaLog = log2_hw(1.0f + e) * kLn2;
-  const float r = (e < 0.015625f) ? series : viaLog;
-  return (v > 20.0f) ? v : r;
+  return fmaxf(v, (e < 0.015625f) ? series : viaLog);
 }
 
 // largest s in [0, S-1] with cu[s] <= g (the sequence that holds token g; empty

@@ -41,6 +41,7 @@ constexpr int kRowThreads = kRowWaves * kWave;         // 256
 constexpr int kRowChans = kRowWaves * (kWave / kRow);  // 16 channels per workgroup
 constexpr int kRowGroup = 4;                           // workgroups sharing 128-byte lines of bf16 io
 constexpr int kXcds = 8;                               // MI355X: workgroup w runs on XCD w % 8
+constexpr int kRowMaxD = 1 << 22;                      // channel limit of the row layout (32-bit tile offsets)
 
 // ---------------------------------------------------------------- DPP helpers
 // DPP controls (gfx9 encoding): quad_perm 0x00-0xFF, row_shr:k 0x110+k,
@@ -62,7 +63,6 @@ constexpr int kXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kRor4 = 0x124;  // reads lane j-4: partner of lanes with bit 2 set
 constexpr int kRor8 = 0x128;  // reads lane j^8
-constexpr int kRor12 = 0x12C; // reads lane j+4: partner of lanes with bit 2 clear
 
 __device__ __forceinline__ float comp(const float4& v, int e) {
   return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
@@ -86,29 +86,56 @@ __device__ __forceinline__ void row_steps(std::integer_sequence<int, I...>, floa
 // p[i] in lane n holds term n of token i; returns sum_n p[j] in lane j.
 // Each stage halves the registers: lanes on one side of the stage's lane bit keep
 // the lower half of the tokens, the others the upper half, each summed with the
-// partner lane across that bit.
+// partner lane across that bit.  The stages across lane bits 3 and 2 split the row
+// by DPP bank masks (banks of 4 lanes): per pair of registers one masked add writes
+// the lanes that keep the lower token and one the lanes that keep the upper, in
+// place of two adds and a select.  The masked adds sit in one asm block; its
+// leading and trailing `s_nop 1` give the two wait states a DPP read needs after
+// a VALU write of its source, which the compiler's hazard check does not see
+// across the asm boundary.  Bits 1 and 0 (within a bank) use adds and selects.
 __device__ __forceinline__ float row_transpose_sum(const float (&p)[kRow], int j) {
-  // keep the products C_n h_n separate from these sums, so that the lane exchange
-  // folds into the adds (an fma would need the exchanged operand in a register)
 #pragma clang fp contract(off)
-  float q[8], r[4], s[2];
-  const bool b3 = (j & 8) != 0, b2 = (j & 4) != 0, b1 = (j & 2) != 0, b0 = (j & 1) != 0;
+  float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float lo = p[i] + dpp<kRor8>(p[i]);
-    const float hi = p[i + 8] + dpp<kRor8>(p[i + 8]);
-    q[i] = b3 ? hi : lo;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = q[i] + dpp<kRor12>(q[i]);
-    const float hi = q[i + 4] + dpp<kRor4>(q[i + 4]);
-    r[i] = b2 ? hi : lo;
-  }
+  for (int i = 0; i < 8; ++i) q[i] = p[i];
+  // bit 3: banks 0-1 (j < 8) keep token i, banks 2-3 token i + 8; partner j ^ 8 = ror 8.
+  // bit 2: banks 0, 2 keep token i (partner j + 4 = ror 12), banks 1, 3 token i + 4 (ror 4).
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %4, %4, %4 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %5, %5, %5 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %6, %6, %6 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %7, %7, %7 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "s_nop 1"
+      : "+&v"(q[0]), "+&v"(q[1]), "+&v"(q[2]), "+&v"(q[3]), "+&v"(q[4]), "+&v"(q[5]), "+&v"(q[6]), "+&v"(q[7])
+      : "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
+  // q[i], i < 4: token i + 4 b2 + 8 b3, summed over lane bits 3 and 2
+  const bool b1 = (j & 2) != 0, b0 = (j & 1) != 0;
+  float s[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const float lo = r[i] + dpp<kXor2>(r[i]);
-    const float hi = r[i + 2] + dpp<kXor2>(r[i + 2]);
+    const float lo = q[i] + dpp<kXor2>(q[i]);
+    const float hi = q[i + 2] + dpp<kXor2>(q[i + 2]);
     s[i] = b1 ? hi : lo;
   }
   const float lo = s[0] + dpp<kXor1>(s[0]);
@@ -131,9 +158,12 @@ __device__ __forceinline__ float io_f32(uint16_t v) { return __uint_as_float(sta
 // ---------------------------------------------------------------- LDS tiles
 // [token][channel] tiles are padded to 17 columns; the B/C tile is laid out
 // [which][q][n] float4 holding tokens 4q..4q+3, so lane n reads B (or C) of 4
-// tokens as one float4.
+// tokens as one float4.  The x tile has three more rows in front, the raw inputs
+// of the three tokens before the block (the conv window), and three buffers: the
+// stager of block b writes its last three rows also into the front rows of block
+// b + 1, whose buffer was last read two blocks before.
 struct RowTiles {
-  float x[2][kRow][kRowChans + 1];
+  float x[3][kKS + kRow][kRowChans + 1];
   float z[2][kRow][kRowChans + 1];
   float dt[2][kRow][kRowChans + 1];
   float4 bc[2][2][4][kRow];
@@ -147,34 +177,65 @@ struct RowStage {
   IO x, z, dt, B, C;
 };
 
+// Global-memory access from a wave-uniform base held as an opaque value in scalar
+// registers: the compiler can then neither fold a thread's offset into a 64-bit
+// vector address nor split the base into per-thread induction variables, so the
+// access takes the scalar-base plus 32-bit vector-offset form (off < 2^32).
+template <typename IO>
+using gmem = __attribute__((address_space(1))) IO;
+
+template <typename IO>
+__device__ __forceinline__ gmem<IO>* sbase(IO* p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+s"(v));
+  return reinterpret_cast<gmem<IO>*>(v);
+}
+template <typename IO>
+__device__ __forceinline__ IO ld_at(gmem<const IO>* p, uint32_t off) {
+  return *reinterpret_cast<gmem<const IO>*>(reinterpret_cast<gmem<const char>*>(p) + off);
+}
+template <typename IO>
+__device__ __forceinline__ gmem<IO>* at(gmem<IO>* p, uint32_t off) {
+  return reinterpret_cast<gmem<IO>*>(reinterpret_cast<gmem<char>*>(p) + off);
+}
+__device__ __forceinline__ void st_g(gmem<float>* p, float v) { *p = v; }
+__device__ __forceinline__ void st_g(gmem<uint16_t>* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+}
+
+// Loads block tb's share of thread i (tb, T < 2^31).  xo / bco are the thread's byte
+// offsets in the [16][d] tiles (from the tile's first element, channel c0) and the
+// [16][N] B/C tiles; in the tensors' last block they are clamped to the last
+// element, so only valid memory is read (the clamped values only feed tokens past
+// the end of the chunk).
 template <typename IO, bool FINAL>
 __device__ __forceinline__ void row_stage_load(RowStage<IO>& r, const IO* __restrict__ x, const IO* __restrict__ z,
                                                const IO* __restrict__ dt, const IO* __restrict__ B,
-                                               const IO* __restrict__ C, int64_t tb, int T, int d, int N, int c0) {
-  const int i = threadIdx.x;
-  const uint32_t tmax = static_cast<uint32_t>(T - 1);
-  uint32_t t = static_cast<uint32_t>(tb) + static_cast<uint32_t>(i >> 4);  // T <= INT32_MAX: no wrap
-  t = t < tmax ? t : tmax;
-  int c = c0 + (i & (kRowChans - 1));
-  c = c < d ? c : d - 1;
-  const int64_t o = static_cast<int64_t>(t) * static_cast<uint32_t>(d) + c;
-  r.x = x[o];
-  r.dt = dt[o];
-  if (FINAL) r.z = z[o];
-  if (i < kRow * N) {
-    const int64_t last = static_cast<int64_t>(T) * N - 1;
-    int64_t e = tb * N + i;
-    e = e < last ? e : last;
-    r.B = B[e];
-    if (FINAL) r.C = C[e];
-  }
+                                               const IO* __restrict__ C, int tb, int T, int d, int N, int c0,
+                                               uint32_t xo, uint32_t bco) {
+  constexpr uint32_t es = sizeof(IO);
+  const int rem = T - tb;  // tokens left from tb, >= 1
+  uint32_t xl = rem >= kRow ? UINT32_MAX : static_cast<uint32_t>(rem * d - 1 - c0) * es;
+  uint32_t bl = rem >= kRow ? UINT32_MAX : static_cast<uint32_t>(rem * N - 1) * es;
+  asm volatile("" : "+s"(xl), "+s"(bl));  // one vector min each, not a min and a select
+  const uint32_t o = min(xo, xl), ob = min(bco, bl);
+  const int64_t e0 = static_cast<int64_t>(tb) * d + c0, b0 = static_cast<int64_t>(tb) * N;
+  r.x = ld_at(sbase(x + e0), o);
+  r.dt = ld_at(sbase(dt + e0), o);
+  if (FINAL) r.z = ld_at(sbase(z + e0), o);
+  r.B = ld_at(sbase(B + b0), ob);
+  if (FINAL) r.C = ld_at(sbase(C + b0), ob);
 }
 
+// Writes a staged block into LDS: x into buffer xb (and, for the last three token rows,
+// into the front rows of buffer xn, the next block's), z/dt/B/C into buffer buf.
 template <typename IO, bool FINAL>
-__device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles& L, int buf, int N) {
+__device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles& L, int xb, int xn, int buf, int N) {
   const int i = threadIdx.x;
   const int tt = i >> 4, ch = i & (kRowChans - 1);
-  L.x[buf][tt][ch] = io_f32(r.x);
+  const float xv = io_f32(r.x);
+  L.x[xb][kKS + tt][ch] = xv;
+  if (tt >= kRow - kKS) L.x[xn][tt - (kRow - kKS)][ch] = xv;
   L.dt[buf][tt][ch] = io_f32(r.dt);
   if (FINAL) L.z[buf][tt][ch] = io_f32(r.z);
   if (i < kRow * N) {
@@ -182,6 +243,12 @@ __device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles&
     reinterpret_cast<float*>(&L.bc[buf][0][t >> 2][n])[t & 3] = io_f32(r.B);
     if (FINAL) reinterpret_cast<float*>(&L.bc[buf][1][t >> 2][n])[t & 3] = io_f32(r.C);
   }
+}
+
+// lanes j of every row with bit j of m16 set (a wave-uniform lane mask)
+__device__ __forceinline__ bool row_lanes(uint32_t m16) {
+  const uint32_t m32 = m16 | (m16 << 16);
+  return __builtin_amdgcn_inverse_ballot_w64((static_cast<uint64_t>(m32) << 32) | m32);
 }
 
 // Workgroup -> (chunk, 16-channel block).  Groups of kRowGroup consecutive channel
@@ -202,6 +269,7 @@ __device__ __forceinline__ void row_work(int64_t w, int ncg, int64_t& k, int& cb
 // backward.  With FINAL = true it is the forward of a training step; a continuing
 // chunk leaves a block it shares with the chunk before to that chunk.
 // whole != 0: one chunk per sequence, workgroup chunk index = sequence (no plan).
+// d <= kRowMaxD keeps every per-thread offset within a block's tiles below 2^32.
 template <typename IO, bool FINAL, bool CKPT = false>
 __global__ void __launch_bounds__(kRowThreads) k_row(
     const IO* __restrict__ x, const IO* __restrict__ z, const IO* __restrict__ dt, const IO* __restrict__ B,
@@ -212,6 +280,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     float* __restrict__ ckpt) {
   constexpr int NMAX = kRow;
   constexpr int64_t kMask = ~static_cast<int64_t>(kRow - 1);
+  constexpr uint32_t es = sizeof(IO);
+  constexpr int XS = kRowChans + 1;  // x tile row stride (floats)
   __shared__ RowTiles L;
   int64_t k;
   int cb;
@@ -250,10 +320,10 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const float cbias = conv_b[cc], dtb = dt_bias[cc];
   const float Dc = FINAL ? D[cc] : 0.0f;
 
-  // initial SSM state, and the sequence's initial conv state cs0 (pass 2 reads the
-  // stashed copies of a multi-chunk sequence: its last chunk rewrites the slot)
+  // initial SSM state; the sequence's initial conv state comes from its slot or, in
+  // pass 2 of a multi-chunk sequence, from the stash (its last chunk rewrites the slot)
   const bool multi = R.ns > 1;
-  const float* cs0 = conv_state + sc * kKS;
+  const bool from_stash = (FINAL || CKPT) && multi;
   float h = 0.0f;
   if (!FINAL && !CKPT) {
     if (R.j == 0) {
@@ -261,30 +331,30 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       if (cvalid) {
         float* stash = ws.stash + (static_cast<int64_t>(R.cidx) * d + c) * (NMAX + kKS);
         stash[j] = h;
-        if (j < kKS) stash[NMAX + j] = cs0[j];
+        if (j < kKS) stash[NMAX + j] = conv_state[sc * kKS + j];
       }
     }
+  } else if (R.j == 0) {
+    h = from_stash ? ws.stash[(static_cast<int64_t>(ws.moff[R.s]) * d + cc) * (NMAX + kKS) + j]
+                   : ((j < N) ? ssm_state[sc * N + j] : 0.0f);
   } else {
-    const float* st0 = multi ? ws.stash + (static_cast<int64_t>(ws.moff[R.s]) * d + cc) * (NMAX + kKS) : nullptr;
-    if (multi) cs0 = st0 + NMAX;
-    if (R.j == 0) {
-      h = multi ? st0[j] : ((j < N) ? ssm_state[sc * N + j] : 0.0f);
-    } else {
-      h = ws.b[(static_cast<int64_t>(R.pidx) * d + cc) * NMAX + j];
-    }
+    h = ws.b[(static_cast<int64_t>(R.pidx) * d + cc) * NMAX + j];
   }
 
-  // raw input of token t of this sequence; positions before its start come from cs0
-  auto hist = [&](int64_t t) -> float {
-    if (t >= seq_start) return io_f32(x[t * d + cc]);
-    const int64_t q = t - seq_start + kKS;
-    return q >= 0 ? cs0[q] : 0.0f;
-  };
   const int64_t tb0 = R.start & kMask;
   const int64_t tlast = (R.end - 1) & kMask;
-  // lanes 13..15 of prev stand for the three tokens before the first block
-  float prev = (j >= kRow - kKS) ? hist(tb0 - kRow + j) : 0.0f;
-  const float hist0 = (tb0 + j < seq_start) ? hist(tb0 + j) : 0.0f;
+  const int nb = static_cast<int>((tlast - tb0) >> 4) + 1;
+  // token indices fit in 32 bits (T <= INT32_MAX)
+  const int T32 = static_cast<int>(T), tb0i = static_cast<int>(tb0);
+  const int rs = static_cast<int>(R.start), re = static_cast<int>(R.end);
+
+  // the staging thread's element: token row srow, channel c0 + sch (clamped to d - 1)
+  const int srow = static_cast<int>(threadIdx.x >> 4), sch = static_cast<int>(threadIdx.x & (kRowChans - 1));
+  const int schc = c0 + sch < d ? sch : d - 1 - c0;
+  const uint32_t xo = static_cast<uint32_t>(srow * d + schc) * es;
+  const uint32_t bco = static_cast<uint32_t>(min(static_cast<int>(threadIdx.x), kRow * N - 1)) * es;
+  const uint32_t yo = static_cast<uint32_t>(srow * d + sch) * es;  // the y element this thread stores
+  const bool ych_ok = c0 + sch < d;
 
   // B/C entries past N stay zero: the staging only writes n < N
   if (N < kRow) {
@@ -293,69 +363,101 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     __syncthreads();
   }
 
-  const int nb = static_cast<int>((tlast - tb0) >> 4) + 1;
-  const int T32 = static_cast<int>(T);
   RowStage<IO> stg{};
-  row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb0, T32, d, N, c0);
-  row_stage_store<IO, FINAL>(stg, L, 0, N);
-  if (nb > 1) row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb0 + kRow, T32, d, N, c0);
+  row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb0i, T32, d, N, c0, xo, bco);
+  row_stage_store<IO, FINAL>(stg, L, 0, 1, 0, N);
+  {
+    // raw input of token t for the staging channel; tokens before the sequence's start
+    // come from its initial conv state (zero before that)
+    const int cs = c0 + schc;
+    const float* cs0 = from_stash ? ws.stash + (static_cast<int64_t>(ws.moff[R.s]) * d + cs) * (NMAX + kKS) + NMAX
+                                  : conv_state + (static_cast<int64_t>(R.s) * d + cs) * kKS;
+    auto hist = [&](int64_t t) -> float {
+      if (t >= seq_start) return io_f32(x[t * d + cs]);
+      const int64_t q = t - seq_start + kKS;
+      return q >= 0 ? cs0[q] : 0.0f;
+    };
+    if (srow < kKS) L.x[0][srow][sch] = hist(tb0 - kKS + srow);  // the window before the first block
+    const int64_t t = tb0 + srow;
+    if (t < seq_start) {  // the first block starts in the sequence before: its tokens there are history
+      const float v = hist(t);
+      L.x[0][kKS + srow][sch] = v;
+      if (srow >= kRow - kKS) L.x[1][srow - (kRow - kKS)][sch] = v;
+    }
+  }
+  if (nb > 1) row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb0i + kRow, T32, d, N, c0, xo, bco);
   __syncthreads();
 
   float p[kRow];
   float dsum = 0.0f;
-  float xv = 0.0f, x1 = 0.0f, x2 = 0.0f;
-  const int64_t d64 = d;
-  const int yt = threadIdx.x >> 4, ych = threadIdx.x & (kRowChans - 1);  // y tile element this thread stores
-  const bool ych_ok = c0 + ych < d;
+  const uint32_t span = static_cast<uint32_t>(R.end - R.start);
+  const int64_t ckrow = CKPT ? static_cast<int64_t>(R.s) * d * NMAX : 0;
+  const uint32_t cko = static_cast<uint32_t>(c * NMAX + j) * 4u;
+  int xb = 0;
 
   for (int ib = 0; ib < nb; ++ib) {
     const int buf = ib & 1;
-    const int64_t tb = tb0 + static_cast<int64_t>(ib) * kRow;
+    const int xn = xb == 2 ? 0 : xb + 1;
+    const int tb = tb0i + ib * kRow;
     if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0))  // the state before this block
-      ckpt[((static_cast<int64_t>(tb >> 4) + R.s) * d + c) * NMAX + j] = h;
+      *at(sbase(ckpt + ckrow + static_cast<int64_t>(tb >> 4) * d * NMAX), cko) = h;
     {
-      const int64_t t = tb + j;
-      const bool act = t >= R.start && t < R.end;
-      xv = (t < seq_start) ? hist0 : L.x[buf][j][ch];
-      // the window: inputs of tokens t-1, t-2, t-3 from the lanes below, or from prev
-      x1 = shr_or<1>(dpp<0x121>(prev), xv);
-      x2 = shr_or<2>(dpp<0x122>(prev), xv);
-      const float x3 = shr_or<3>(dpp<0x123>(prev), xv);
-      float xc = cbias;
-      xc = __builtin_fmaf(w0, x3, xc);
-      xc = __builtin_fmaf(w1, x2, xc);
-      xc = __builtin_fmaf(w2, x1, xc);
-      xc = __builtin_fmaf(w3, xv, xc);
-      const float u = silu(xc);
-      // computed for every lane and masked with a multiply: no branch around softplus
-      const float delta = softplus(L.dt[buf][j][ch] + dtb) * (act ? 1.0f : 0.0f);
-      const float du = delta * u;
-      if (!FINAL) dsum += delta;
+      // the conv window: inputs of tokens t-3 .. t from rows j .. j+3 of the x tile
+      const float* xr = &L.x[xb][j][ch];
+      const float x3 = xr[0], x2 = xr[XS], x1 = xr[2 * XS], xv = xr[3 * XS];
+      const float dtv = L.dt[buf][j][ch];
+      const float zv = FINAL ? L.z[buf][j][ch] : 0.0f;  // read ahead of the asm blocks below
       float4 Bq[4], Cq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         Bq[q] = L.bc[buf][0][q][j];
         Cq[q] = FINAL ? L.bc[buf][1][q][j] : Bq[q];
       }
+      // all of the block's LDS reads are in flight before the per-token work starts
+      __builtin_amdgcn_sched_barrier(0);
+      // tokens of the block inside the chunk: lanes [lo, hi) of every row
+      const int lo = rs - tb, hi = re - tb;
+      const uint32_t mlo = lo <= 0 ? 0u : (1u << lo) - 1u;
+      const uint32_t mhi = hi >= kRow ? 0xFFFFu : (1u << hi) - 1u;
+      const bool act = row_lanes(mhi & ~mlo);
+      float xc = cbias;
+      xc = __builtin_fmaf(w0, x3, xc);
+      xc = __builtin_fmaf(w1, x2, xc);
+      xc = __builtin_fmaf(w2, x1, xc);
+      xc = __builtin_fmaf(w3, xv, xc);
+      const float u = silu(xc);
+      // tokens outside the chunk get delta = 0: their step is the identity (softplus is
+      // computed in every lane and then selected, not branched around)
+      float sp = softplus(dtv + dtb);
+      asm volatile("" : "+v"(sp));
+      const float delta = act ? sp : 0.0f;
+      const float du = delta * u;
+      if (!FINAL) dsum += delta;
       row_steps<FINAL>(std::make_integer_sequence<int, kRow>{}, delta, du, A2, Bq, Cq, h, p);
       if (FINAL) {
         const float s = row_transpose_sum(p, j);
-        L.y[buf][j][ch] = __builtin_fmaf(Dc, u, s) * silu(L.z[buf][j][ch]);
+        L.y[buf][j][ch] = __builtin_fmaf(Dc, u, s) * silu(zv);
       }
-      prev = xv;
     }
     // stage block ib+1 (loaded one iteration ago), prefetch block ib+2, write y of block ib-1
-    if (ib + 1 < nb) row_stage_store<IO, FINAL>(stg, L, buf ^ 1, N);
-    if (ib + 2 < nb) row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb + 2 * kRow, T32, d, N, c0);
+    if (ib + 1 < nb) row_stage_store<IO, FINAL>(stg, L, xn, xn == 2 ? 0 : xn + 1, buf ^ 1, N);
+    if (ib + 2 < nb) row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb + 2 * kRow, T32, d, N, c0, xo, bco);
     if (FINAL && ib > 0) {
-      const int64_t t = tb - kRow + yt;
-      if (t >= R.start && t < R.end && ych_ok) st_io(y, t * d64 + c0 + ych, L.y[buf ^ 1][yt][ych]);
+      const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(tb - kRow - rs);
+      if (rel < span && ych_ok) {
+        uint32_t o = yo;
+        asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
+        st_g(at(sbase(y + static_cast<int64_t>(tb - kRow) * d + c0), o), L.y[buf ^ 1][srow][sch]);
+      }
     }
+    xb = xn;
     __syncthreads();
   }
+  const int xl = xb == 0 ? 2 : xb - 1;  // buffer of the last block
   if (FINAL) {
-    const int64_t t = tb0 + static_cast<int64_t>(nb - 1) * kRow + yt;
-    if (t >= R.start && t < R.end && ych_ok) st_io(y, t * d64 + c0 + ych, L.y[(nb - 1) & 1][yt][ych]);
+    const int tb = tb0i + (nb - 1) * kRow;
+    const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(tb - rs);
+    if (rel < span && ych_ok) st_g(at(sbase(y + static_cast<int64_t>(tb) * d + c0), yo), L.y[(nb - 1) & 1][srow][sch]);
   }
 
   if (CKPT && !FINAL) return;
@@ -368,11 +470,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     }
   } else if (R.j == R.ns - 1 && cvalid) {
     if (j < N) ssm_state[sc * N + j] = h;
-    if (j == static_cast<int>((R.end - 1) & (kRow - 1))) {  // the lane of the sequence's last token
-      conv_state[sc * kKS + 0] = x2;
-      conv_state[sc * kKS + 1] = x1;
-      conv_state[sc * kKS + 2] = xv;
-    }
+    const int jl = static_cast<int>((R.end - 1) & (kRow - 1));  // the lane of the sequence's last token
+    if (j < kKS) conv_state[sc * kKS + j] = L.x[xl][jl + 1 + j][ch];
   }
 }
 
