@@ -100,7 +100,7 @@ __device__ __forceinline__ float row_transpose_sum(const float (&p)[kRow], int j
   for (int i = 0; i < 8; ++i) q[i] = p[i];
   // bit 3: banks 0-1 (j < 8) keep token i, banks 2-3 token i + 8; partner j ^ 8 = ror 8.
   // bit 2: banks 0, 2 keep token i (partner j + 4 = ror 12), banks 1, 3 token i + 4 (ror 4).
-  asm volatile(
+  asm(
       "s_nop 1\n\t"
       "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
       "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
@@ -156,19 +156,29 @@ __device__ __forceinline__ float io_f32(float v) { return v; }
 __device__ __forceinline__ float io_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 
 // ---------------------------------------------------------------- LDS tiles
-// [token][channel] tiles are padded to 17 columns; the B/C tile is laid out
-// [which][q][n] float4 holding tokens 4q..4q+3, so lane n reads B (or C) of 4
-// tokens as one float4.  The x tile has three more rows in front, the raw inputs
-// of the three tokens before the block (the conv window), and three buffers: the
-// stager of block b writes its last three rows also into the front rows of block
-// b + 1, whose buffer was last read two blocks before.
-struct RowTiles {
-  float x[3][kKS + kRow][kRowChans + 1];
-  float z[2][kRow][kRowChans + 1];
-  float dt[2][kRow][kRowChans + 1];
-  float4 bc[2][2][4][kRow];
-  float y[2][kRow][kRowChans + 1];
+// A block's tiles sit in one of three slots: block b in slot b % 3.  [token][channel]
+// tiles are padded to 18 columns (no LDS bank conflicts for either the row or the
+// column access); the B/C tile is laid out [which][q][n] float4 holding tokens
+// 4q..4q+3, so lane n reads B (or C) of 4 tokens as one float4.  The x tile has three
+// more rows in front, the raw inputs of the three tokens before the block (the conv
+// window): the stager of block b also writes its last three rows there in block
+// b + 1's slot.
+constexpr int kTS = kRowChans + 2;  // tile row stride (floats)
+struct RowSlot {
+  float x[kKS + kRow][kTS];
+  float z[kRow][kTS];
+  float dt[kRow][kTS];
+  float4 bc[2][4][kRow];
 };
+struct RowTiles {
+  RowSlot slot[3];
+  float y[2][kRow][kTS];
+};
+constexpr uint32_t kSlotBytes = sizeof(RowSlot);
+
+__device__ __forceinline__ RowSlot& slot_at(RowTiles& L, uint32_t off) {
+  return *reinterpret_cast<RowSlot*>(reinterpret_cast<char*>(&L.slot[0]) + off);
+}
 
 // One thread's share of a block's global inputs: element (token i/16, channel i%16)
 // of the x/z/dt tiles, and element i of the contiguous [16][N] B and C tiles.
@@ -184,11 +194,17 @@ struct RowStage {
 template <typename IO>
 using gmem = __attribute__((address_space(1))) IO;
 
-template <typename IO>
-__device__ __forceinline__ gmem<IO>* sbase(IO* p) {
+// p as an opaque value: the compiler keeps it in scalar registers (it is wave-uniform)
+// and cannot reassociate it with a per-thread offset
+template <typename P>
+__device__ __forceinline__ P sreg(P p) {
   uint64_t v = reinterpret_cast<uint64_t>(p);
   asm volatile("" : "+s"(v));
-  return reinterpret_cast<gmem<IO>*>(v);
+  return reinterpret_cast<P>(v);
+}
+template <typename IO>
+__device__ __forceinline__ gmem<IO>* sbase(IO* p) {
+  return sreg(reinterpret_cast<gmem<IO>*>(reinterpret_cast<uint64_t>(p)));
 }
 template <typename IO>
 __device__ __forceinline__ IO ld_at(gmem<const IO>* p, uint32_t off) {
@@ -203,52 +219,55 @@ __device__ __forceinline__ void st_g(gmem<uint16_t>* p, float v) {
   *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
 }
 
-// Loads block tb's share of thread i (tb, T < 2^31).  xo / bco are the thread's byte
-// offsets in the [16][d] tiles (from the tile's first element, channel c0) and the
-// [16][N] B/C tiles; in the tensors' last block they are clamped to the last
-// element, so only valid memory is read (the clamped values only feed tokens past
-// the end of the chunk).
+// Global pointers of one staged block: the x/z/dt tiles from channel c0 of its first
+// token, the contiguous B/C tiles (wave-uniform, in scalar registers)
+template <typename IO>
+struct RowSrc {
+  gmem<const IO>*x, *z, *dt, *B, *C;
+};
+
+// Loads a block's share of this thread: its byte offsets o in the [16][d] x/z/dt
+// tiles and ob in the [16][N] B/C tiles (in the tensors' last block both are clamped
+// to the last element, so only valid memory is read; the clamped values only feed
+// tokens past the end of the chunk).
 template <typename IO, bool FINAL>
-__device__ __forceinline__ void row_stage_load(RowStage<IO>& r, const IO* __restrict__ x, const IO* __restrict__ z,
-                                               const IO* __restrict__ dt, const IO* __restrict__ B,
-                                               const IO* __restrict__ C, int tb, int T, int d, int N, int c0,
-                                               uint32_t xo, uint32_t bco) {
-  constexpr uint32_t es = sizeof(IO);
-  const int rem = T - tb;  // tokens left from tb, >= 1
-  uint32_t xl = rem >= kRow ? UINT32_MAX : static_cast<uint32_t>(rem * d - 1 - c0) * es;
-  uint32_t bl = rem >= kRow ? UINT32_MAX : static_cast<uint32_t>(rem * N - 1) * es;
-  asm volatile("" : "+s"(xl), "+s"(bl));  // one vector min each, not a min and a select
-  const uint32_t o = min(xo, xl), ob = min(bco, bl);
-  const int64_t e0 = static_cast<int64_t>(tb) * d + c0, b0 = static_cast<int64_t>(tb) * N;
-  r.x = ld_at(sbase(x + e0), o);
-  r.dt = ld_at(sbase(dt + e0), o);
-  if (FINAL) r.z = ld_at(sbase(z + e0), o);
-  r.B = ld_at(sbase(B + b0), ob);
-  if (FINAL) r.C = ld_at(sbase(C + b0), ob);
+__device__ __forceinline__ void row_stage_load(RowStage<IO>& r, const RowSrc<IO>& g, uint32_t o, uint32_t ob) {
+  r.x = ld_at(g.x, o);
+  r.dt = ld_at(g.dt, o);
+  if (FINAL) r.z = ld_at(g.z, o);
+  r.B = ld_at(g.B, ob);
+  if (FINAL) r.C = ld_at(g.C, ob);
 }
 
-// Writes a staged block into LDS: x into buffer xb (and, for the last three token rows,
-// into the front rows of buffer xn, the next block's), z/dt/B/C into buffer buf.
+// Writes a staged block into LDS: into the slot at byte offset sb, and the last three
+// token rows of x also into the front rows of the slot at sn (the next block's).
 template <typename IO, bool FINAL>
-__device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles& L, int xb, int xn, int buf, int N) {
+__device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles& L, uint32_t sb, uint32_t sn, int N) {
   const int i = threadIdx.x;
   const int tt = i >> 4, ch = i & (kRowChans - 1);
+  RowSlot& S = slot_at(L, sb);
   const float xv = io_f32(r.x);
-  L.x[xb][kKS + tt][ch] = xv;
-  if (tt >= kRow - kKS) L.x[xn][tt - (kRow - kKS)][ch] = xv;
-  L.dt[buf][tt][ch] = io_f32(r.dt);
-  if (FINAL) L.z[buf][tt][ch] = io_f32(r.z);
+  S.x[kKS + tt][ch] = xv;
+  if (tt >= kRow - kKS) slot_at(L, sn).x[tt - (kRow - kKS)][ch] = xv;
+  S.dt[tt][ch] = io_f32(r.dt);
+  if (FINAL) S.z[tt][ch] = io_f32(r.z);
   if (i < kRow * N) {
     const int t = i / N, n = i - t * N;
-    reinterpret_cast<float*>(&L.bc[buf][0][t >> 2][n])[t & 3] = io_f32(r.B);
-    if (FINAL) reinterpret_cast<float*>(&L.bc[buf][1][t >> 2][n])[t & 3] = io_f32(r.C);
+    reinterpret_cast<float*>(&S.bc[0][t >> 2][n])[t & 3] = io_f32(r.B);
+    if (FINAL) reinterpret_cast<float*>(&S.bc[1][t >> 2][n])[t & 3] = io_f32(r.C);
   }
 }
 
-// lanes j of every row with bit j of m16 set (a wave-uniform lane mask)
-__device__ __forceinline__ bool row_lanes(uint32_t m16) {
+// the lane mask that holds lanes j of every row with bit j of m16 set
+__device__ __forceinline__ uint64_t row_mask(uint32_t m16) {
   const uint32_t m32 = m16 | (m16 << 16);
-  return __builtin_amdgcn_inverse_ballot_w64((static_cast<uint64_t>(m32) << 32) | m32);
+  return (static_cast<uint64_t>(m32) << 32) | m32;
+}
+// tokens [lo, hi) of a 16-token block (lo <= 15, hi >= 1, either may lie outside 0..16)
+__device__ __forceinline__ uint32_t token_bits(int lo, int hi) {
+  const uint32_t mlo = lo <= 0 ? 0u : (1u << lo) - 1u;
+  const uint32_t mhi = hi >= kRow ? 0xFFFFu : (1u << hi) - 1u;
+  return mhi & ~mlo;
 }
 
 // Workgroup -> (chunk, 16-channel block).  Groups of kRowGroup consecutive channel
@@ -281,7 +300,6 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   constexpr int NMAX = kRow;
   constexpr int64_t kMask = ~static_cast<int64_t>(kRow - 1);
   constexpr uint32_t es = sizeof(IO);
-  constexpr int XS = kRowChans + 1;  // x tile row stride (floats)
   __shared__ RowTiles L;
   int64_t k;
   int cb;
@@ -355,17 +373,40 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const uint32_t bco = static_cast<uint32_t>(min(static_cast<int>(threadIdx.x), kRow * N - 1)) * es;
   const uint32_t yo = static_cast<uint32_t>(srow * d + sch) * es;  // the y element this thread stores
   const bool ych_ok = c0 + sch < d;
+  // the tensors' last block (T - Tl < 16 tokens): its loads are clamped to the last element
+  const int Tl = (T32 - 1) & ~(kRow - 1);
+  const uint32_t xlim = static_cast<uint32_t>((T32 - Tl) * d - 1 - c0) * es;
+  const uint32_t blim = static_cast<uint32_t>((T32 - Tl) * N - 1) * es;
+  auto lim_x = [&](int tb) { return tb == Tl ? xlim : UINT32_MAX; };
+  auto lim_b = [&](int tb) { return tb == Tl ? blim : UINT32_MAX; };
 
   // B/C entries past N stay zero: the staging only writes n < N
   if (N < kRow) {
-    float* bcf = reinterpret_cast<float*>(&L.bc[0][0][0][0]);
-    for (int i = threadIdx.x; i < 2 * 2 * 4 * kRow * 4; i += kRowThreads) bcf[i] = 0.0f;
+    for (int k = 0; k < 3; ++k) {
+      float* bcf = reinterpret_cast<float*>(&L.slot[k].bc[0][0][0]);
+      for (int i = threadIdx.x; i < 2 * 4 * kRow * 4; i += kRowThreads) bcf[i] = 0.0f;
+    }
     __syncthreads();
   }
 
+  const int64_t sx = static_cast<int64_t>(kRow) * d, sb = static_cast<int64_t>(kRow) * N;  // elements per block
+  RowSrc<IO> g;
+  auto set_src = [&](int tb) {
+    const int64_t e0 = static_cast<int64_t>(tb) * d + c0, b0 = static_cast<int64_t>(tb) * N;
+    g.x = sbase(x + e0);
+    g.dt = sbase(dt + e0);
+    if (FINAL) g.z = sbase(z + e0);
+    g.B = sbase(B + b0);
+    if (FINAL) g.C = sbase(C + b0);
+  };
+  auto load = [&](RowStage<IO>& r, int tb) {
+    row_stage_load<IO, FINAL>(r, g, min(xo, lim_x(tb)), min(bco, lim_b(tb)));
+  };
+  // blocks 0 and 1 staged, block 2 loaded
   RowStage<IO> stg{};
-  row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb0i, T32, d, N, c0, xo, bco);
-  row_stage_store<IO, FINAL>(stg, L, 0, 1, 0, N);
+  set_src(tb0i);
+  load(stg, tb0i);
+  row_stage_store<IO, FINAL>(stg, L, 0, kSlotBytes, N);
   {
     // raw input of token t for the staging channel; tokens before the sequence's start
     // come from its initial conv state (zero before that)
@@ -377,87 +418,131 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       const int64_t q = t - seq_start + kKS;
       return q >= 0 ? cs0[q] : 0.0f;
     };
-    if (srow < kKS) L.x[0][srow][sch] = hist(tb0 - kKS + srow);  // the window before the first block
+    if (srow < kKS) L.slot[0].x[srow][sch] = hist(tb0 - kKS + srow);  // the window before the first block
     const int64_t t = tb0 + srow;
     if (t < seq_start) {  // the first block starts in the sequence before: its tokens there are history
       const float v = hist(t);
-      L.x[0][kKS + srow][sch] = v;
-      if (srow >= kRow - kKS) L.x[1][srow - (kRow - kKS)][sch] = v;
+      L.slot[0].x[kKS + srow][sch] = v;
+      if (srow >= kRow - kKS) L.slot[1].x[srow - (kRow - kKS)][sch] = v;
     }
   }
-  if (nb > 1) row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb0i + kRow, T32, d, N, c0, xo, bco);
+  if (nb > 1) {
+    set_src(tb0i + kRow);
+    load(stg, tb0i + kRow);
+    row_stage_store<IO, FINAL>(stg, L, kSlotBytes, 2 * kSlotBytes, N);
+  }
+  if (nb > 2) {
+    set_src(tb0i + 2 * kRow);
+    load(stg, tb0i + 2 * kRow);
+  }
   __syncthreads();
+
+  // the lanes of the chunk's tokens in the first and the last block (all lanes between)
+  const uint64_t mfirst = row_mask(token_bits(rs - tb0i, re - tb0i));
+  const int tlasti = static_cast<int>(tlast);
+  const uint64_t mlast = row_mask(token_bits(rs - tlasti, re - tlasti));
+
+  // The per-token work of a block (conv, SiLU, softplus, SiLU(z)) runs one iteration
+  // ahead of its scan, so each iteration's scan and readout of block ib overlap the
+  // per-token work of block ib+1: two independent dependency chains.
+  struct Tok {
+    float delta, du, u, zs;
+  };
+  auto token_work = [&](float x3, float x2, float x1, float xv, float dtv, float zv, uint64_t m) -> Tok {
+    Tok o;
+    float xc = cbias;
+    xc = __builtin_fmaf(w0, x3, xc);
+    xc = __builtin_fmaf(w1, x2, xc);
+    xc = __builtin_fmaf(w2, x1, xc);
+    xc = __builtin_fmaf(w3, xv, xc);
+    o.u = silu(xc);
+    // tokens outside the chunk get delta = 0: their step is the identity
+    o.delta = softplus(dtv + dtb) * (__builtin_amdgcn_inverse_ballot_w64(m) ? 1.0f : 0.0f);
+    o.du = o.delta * o.u;
+    o.zs = FINAL ? silu(zv) : 0.0f;
+    return o;
+  };
+  Tok tk;
+  {
+    const float* xr = &L.slot[0].x[j][ch];
+    tk = token_work(xr[0], xr[kTS], xr[2 * kTS], xr[3 * kTS], L.slot[0].dt[j][ch], FINAL ? L.slot[0].z[j][ch] : 0.0f,
+                    mfirst);
+  }
 
   float p[kRow];
   float dsum = 0.0f;
   const uint32_t span = static_cast<uint32_t>(R.end - R.start);
-  const int64_t ckrow = CKPT ? static_cast<int64_t>(R.s) * d * NMAX : 0;
   const uint32_t cko = static_cast<uint32_t>(c * NMAX + j) * 4u;
-  int xb = 0;
+  // scalar loop state: the slots of blocks ib, ib+1, ib+2 (byte offsets), the block
+  // loaded next, and the y / checkpoint rows of the previous / this block
+  uint32_t scur = 0, snext = kSlotBytes, snn = 2 * kSlotBytes;
+  int tbl = tb0i + 3 * kRow;
+  set_src(tbl);
+  gmem<IO>* py = sbase(y + static_cast<int64_t>(tb0i - kRow) * d + c0);
+  gmem<float>* pck = CKPT ? sbase(ckpt + (static_cast<int64_t>(tb0 >> 4) + R.s) * d * NMAX) : nullptr;
+  int yrel = tb0i - kRow - rs;  // first token of the previous block relative to the chunk start
 
   for (int ib = 0; ib < nb; ++ib) {
     const int buf = ib & 1;
-    const int xn = xb == 2 ? 0 : xb + 1;
-    const int tb = tb0i + ib * kRow;
     if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0))  // the state before this block
-      *at(sbase(ckpt + ckrow + static_cast<int64_t>(tb >> 4) * d * NMAX), cko) = h;
+      *at(pck, cko) = h;
     {
-      // the conv window: inputs of tokens t-3 .. t from rows j .. j+3 of the x tile
-      const float* xr = &L.x[xb][j][ch];
-      const float x3 = xr[0], x2 = xr[XS], x1 = xr[2 * XS], xv = xr[3 * XS];
-      const float dtv = L.dt[buf][j][ch];
-      const float zv = FINAL ? L.z[buf][j][ch] : 0.0f;  // read ahead of the asm blocks below
+      const RowSlot& Sc = slot_at(L, scur);
+      const RowSlot& Sn = slot_at(L, snext);
       float4 Bq[4], Cq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        Bq[q] = L.bc[buf][0][q][j];
-        Cq[q] = FINAL ? L.bc[buf][1][q][j] : Bq[q];
+        Bq[q] = Sc.bc[0][q][j];
+        Cq[q] = FINAL ? Sc.bc[1][q][j] : Bq[q];
       }
-      // all of the block's LDS reads are in flight before the per-token work starts
+      // block ib+1's conv window (inputs of tokens t-3 .. t: rows j .. j+3), dt and z
+      // (past the last block these are stale values, computed on and not used)
+      const float* xr = &Sn.x[j][ch];
+      const float x3 = xr[0], x2 = xr[kTS], x1 = xr[2 * kTS], xv = xr[3 * kTS];
+      const float dtv = Sn.dt[j][ch];
+      const float zv = FINAL ? Sn.z[j][ch] : 0.0f;
+      // all of the block's LDS reads are in flight before the arithmetic starts
       __builtin_amdgcn_sched_barrier(0);
-      // tokens of the block inside the chunk: lanes [lo, hi) of every row
-      const int lo = rs - tb, hi = re - tb;
-      const uint32_t mlo = lo <= 0 ? 0u : (1u << lo) - 1u;
-      const uint32_t mhi = hi >= kRow ? 0xFFFFu : (1u << hi) - 1u;
-      const bool act = row_lanes(mhi & ~mlo);
-      float xc = cbias;
-      xc = __builtin_fmaf(w0, x3, xc);
-      xc = __builtin_fmaf(w1, x2, xc);
-      xc = __builtin_fmaf(w2, x1, xc);
-      xc = __builtin_fmaf(w3, xv, xc);
-      const float u = silu(xc);
-      // tokens outside the chunk get delta = 0: their step is the identity (softplus is
-      // computed in every lane and then selected, not branched around)
-      float sp = softplus(dtv + dtb);
-      asm volatile("" : "+v"(sp));
-      const float delta = act ? sp : 0.0f;
-      const float du = delta * u;
-      if (!FINAL) dsum += delta;
-      row_steps<FINAL>(std::make_integer_sequence<int, kRow>{}, delta, du, A2, Bq, Cq, h, p);
+      const Tok tn = token_work(x3, x2, x1, xv, dtv, zv, ib + 1 == nb - 1 ? mlast : ~0ull);
+      if (!FINAL) dsum += tk.delta;
+      row_steps<FINAL>(std::make_integer_sequence<int, kRow>{}, tk.delta, tk.du, A2, Bq, Cq, h, p);
       if (FINAL) {
         const float s = row_transpose_sum(p, j);
-        L.y[buf][j][ch] = __builtin_fmaf(Dc, u, s) * silu(zv);
+        L.y[buf][j][ch] = __builtin_fmaf(Dc, tk.u, s) * tk.zs;
       }
+      tk = tn;
     }
-    // stage block ib+1 (loaded one iteration ago), prefetch block ib+2, write y of block ib-1
-    if (ib + 1 < nb) row_stage_store<IO, FINAL>(stg, L, xn, xn == 2 ? 0 : xn + 1, buf ^ 1, N);
-    if (ib + 2 < nb) row_stage_load<IO, FINAL>(stg, x, z, dt, B, C, tb + 2 * kRow, T32, d, N, c0, xo, bco);
+    // stage block ib+2 (loaded one iteration ago), prefetch block ib+3, write y of block ib-1
+    if (ib + 2 < nb) row_stage_store<IO, FINAL>(stg, L, snn, scur, N);
+    if (ib + 3 < nb) load(stg, tbl);
     if (FINAL && ib > 0) {
-      const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(tb - kRow - rs);
+      const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(yrel);
       if (rel < span && ych_ok) {
         uint32_t o = yo;
         asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
-        st_g(at(sbase(y + static_cast<int64_t>(tb - kRow) * d + c0), o), L.y[buf ^ 1][srow][sch]);
+        st_g(at(py, o), L.y[buf ^ 1][srow][sch]);
       }
     }
-    xb = xn;
+    // advance the scalar state
+    const uint32_t st = scur;
+    scur = snext;
+    snext = snn;
+    snn = st;
+    tbl += kRow;
+    g.x = sreg(g.x + sx);
+    g.dt = sreg(g.dt + sx);
+    if (FINAL) g.z = sreg(g.z + sx);
+    g.B = sreg(g.B + sb);
+    if (FINAL) g.C = sreg(g.C + sb);
+    if (FINAL) py = sreg(py + sx);
+    if (CKPT) pck = sreg(pck + static_cast<int64_t>(d) * NMAX);
+    yrel += kRow;
     __syncthreads();
   }
-  const int xl = xb == 0 ? 2 : xb - 1;  // buffer of the last block
+  const uint32_t xl = snn;  // slot of the last block (the rotation has moved it two places on)
   if (FINAL) {
-    const int tb = tb0i + (nb - 1) * kRow;
-    const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(tb - rs);
-    if (rel < span && ych_ok) st_g(at(sbase(y + static_cast<int64_t>(tb) * d + c0), yo), L.y[(nb - 1) & 1][srow][sch]);
+    const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(yrel);
+    if (rel < span && ych_ok) st_g(at(py, yo), L.y[(nb - 1) & 1][srow][sch]);
   }
 
   if (CKPT && !FINAL) return;
@@ -471,7 +556,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   } else if (R.j == R.ns - 1 && cvalid) {
     if (j < N) ssm_state[sc * N + j] = h;
     const int jl = static_cast<int>((R.end - 1) & (kRow - 1));  // the lane of the sequence's last token
-    if (j < kKS) conv_state[sc * kKS + j] = L.x[xl][jl + 1 + j][ch];
+    if (j < kKS) conv_state[sc * kKS + j] = slot_at(L, xl).x[jl + 1 + j][ch];
   }
 }
 
