@@ -162,17 +162,19 @@ __device__ __forceinline__ float io_f32(uint16_t v) { return __uint_as_float(sta
 // 4q..4q+3, so lane n reads B (or C) of 4 tokens as one float4.  The x tile has three
 // more rows in front, the raw inputs of the three tokens before the block (the conv
 // window): the stager of block b also writes its last three rows there in block
-// b + 1's slot.
+// b + 1's slot.  With bf16 io the stager writes the 16 raw bits of dt, z, B and C into
+// the upper half of their float (the lower halves are zeroed once), which is the
+// float32 value without a conversion instruction.
 constexpr int kTS = kRowChans + 2;  // tile row stride (floats)
 struct RowSlot {
   float x[kKS + kRow][kTS];
   float z[kRow][kTS];
   float dt[kRow][kTS];
+  float y[kRow][kTS];  // the block's outputs, from its scan until they are stored
   float4 bc[2][4][kRow];
 };
 struct RowTiles {
   RowSlot slot[3];
-  float y[2][kRow][kTS];
 };
 constexpr uint32_t kSlotBytes = sizeof(RowSlot);
 
@@ -239,22 +241,37 @@ __device__ __forceinline__ void row_stage_load(RowStage<IO>& r, const RowSrc<IO>
   if (FINAL) r.C = ld_at(g.C, ob);
 }
 
+// A staging thread's byte offsets within a slot: element (token row tt, channel ch) of
+// the [token][channel] tiles (x from its first block row) and its element of the B/C
+// tile.
+struct RowStOff {
+  uint32_t tc;  // (tt * kTS + ch) * 4
+  uint32_t bc;  // of B; C is one [4][16] float4 tile further
+};
+
+__device__ __forceinline__ void st_lds(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
+__device__ __forceinline__ void st_lds(char* p, uint16_t v) { *reinterpret_cast<uint16_t*>(p + 2) = v; }
+
 // Writes a staged block into LDS: into the slot at byte offset sb, and the last three
 // token rows of x also into the front rows of the slot at sn (the next block's).
 template <typename IO, bool FINAL>
-__device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles& L, uint32_t sb, uint32_t sn, int N) {
-  const int i = threadIdx.x;
-  const int tt = i >> 4, ch = i & (kRowChans - 1);
-  RowSlot& S = slot_at(L, sb);
+__device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles& L, uint32_t sb, uint32_t sn,
+                                                const RowStOff& o, int N) {
+  constexpr uint32_t kX = offsetof(RowSlot, x) + kKS * kTS * 4, kZ = offsetof(RowSlot, z),
+                     kDt = offsetof(RowSlot, dt), kB = offsetof(RowSlot, bc), kC = kB + sizeof(float4) * 4 * kRow;
+  constexpr int kFront = static_cast<int>(offsetof(RowSlot, x)) - (kRow - kKS) * kTS * 4;  // row tt - 13, next slot
+  const int tt = threadIdx.x >> 4;
+  char* base = reinterpret_cast<char*>(&L.slot[0]);
+  char* t = base + sb + o.tc;
   const float xv = io_f32(r.x);
-  S.x[kKS + tt][ch] = xv;
-  if (tt >= kRow - kKS) slot_at(L, sn).x[tt - (kRow - kKS)][ch] = xv;
-  S.dt[tt][ch] = io_f32(r.dt);
-  if (FINAL) S.z[tt][ch] = io_f32(r.z);
-  if (i < kRow * N) {
-    const int t = i / N, n = i - t * N;
-    reinterpret_cast<float*>(&S.bc[0][t >> 2][n])[t & 3] = io_f32(r.B);
-    if (FINAL) reinterpret_cast<float*>(&S.bc[1][t >> 2][n])[t & 3] = io_f32(r.C);
+  st_lds(t + kX, xv);
+  if (tt >= kRow - kKS) st_lds(base + sn + (static_cast<int>(o.tc) + kFront), xv);
+  st_lds(t + kDt, r.dt);
+  if (FINAL) st_lds(t + kZ, r.z);
+  if (static_cast<int>(threadIdx.x) < kRow * N) {
+    char* b = base + sb + o.bc;
+    st_lds(b + kB, r.B);
+    if (FINAL) st_lds(b + kC, r.C);
   }
 }
 
@@ -372,7 +389,6 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const uint32_t xo = static_cast<uint32_t>(srow * d + schc) * es;
   const uint32_t bco = static_cast<uint32_t>(min(static_cast<int>(threadIdx.x), kRow * N - 1)) * es;
   const uint32_t yo = static_cast<uint32_t>(srow * d + sch) * es;  // the y element this thread stores
-  const bool ych_ok = c0 + sch < d;
   // the tensors' last block (T - Tl < 16 tokens): its loads are clamped to the last element
   const int Tl = (T32 - 1) & ~(kRow - 1);
   const uint32_t xlim = static_cast<uint32_t>((T32 - Tl) * d - 1 - c0) * es;
@@ -380,12 +396,18 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   auto lim_x = [&](int tb) { return tb == Tl ? xlim : UINT32_MAX; };
   auto lim_b = [&](int tb) { return tb == Tl ? blim : UINT32_MAX; };
 
-  // B/C entries past N stay zero: the staging only writes n < N
-  if (N < kRow) {
-    for (int k = 0; k < 3; ++k) {
-      float* bcf = reinterpret_cast<float*>(&L.slot[k].bc[0][0][0]);
-      for (int i = threadIdx.x; i < 2 * 4 * kRow * 4; i += kRowThreads) bcf[i] = 0.0f;
-    }
+  RowStOff so;
+  so.tc = static_cast<uint32_t>(srow * kTS + sch) * 4u;
+  {
+    const int i = min(static_cast<int>(threadIdx.x), kRow * N - 1), t = i / N, n = i - t * N;
+    so.bc = static_cast<uint32_t>(((t >> 2) * kRow + n) * 16 + (t & 3) * 4);
+  }
+  // B/C entries past N stay zero (the staging only writes n < N), and so do the lower
+  // halves of bf16 values
+  if (sizeof(IO) == 2 || N < kRow) {
+    float4* f = reinterpret_cast<float4*>(&L.slot[0]);
+    for (int i = threadIdx.x; i < static_cast<int>(sizeof(L) / sizeof(float4)); i += kRowThreads)
+      f[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     __syncthreads();
   }
 
@@ -406,7 +428,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   RowStage<IO> stg{};
   set_src(tb0i);
   load(stg, tb0i);
-  row_stage_store<IO, FINAL>(stg, L, 0, kSlotBytes, N);
+  row_stage_store<IO, FINAL>(stg, L, 0, kSlotBytes, so, N);
   {
     // raw input of token t for the staging channel; tokens before the sequence's start
     // come from its initial conv state (zero before that)
@@ -429,7 +451,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   if (nb > 1) {
     set_src(tb0i + kRow);
     load(stg, tb0i + kRow);
-    row_stage_store<IO, FINAL>(stg, L, kSlotBytes, 2 * kSlotBytes, N);
+    row_stage_store<IO, FINAL>(stg, L, kSlotBytes, 2 * kSlotBytes, so, N);
   }
   if (nb > 2) {
     set_src(tb0i + 2 * kRow);
@@ -481,9 +503,21 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   gmem<IO>* py = sbase(y + static_cast<int64_t>(tb0i - kRow) * d + c0);
   gmem<float>* pck = CKPT ? sbase(ckpt + (static_cast<int64_t>(tb0 >> 4) + R.s) * d * NMAX) : nullptr;
   int yrel = tb0i - kRow - rs;  // first token of the previous block relative to the chunk start
+  // The lanes of this wave that store y of a block whose first token is rel tokens past
+  // the chunk start: token rows srow = 4 w + r (lanes 16 r .. 16 r + 15) with
+  // 0 <= srow + rel < span, on channels below d.
+  const int w4 = 4 * __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const uint64_t ych_lanes = row_mask(d - c0 >= kRowChans ? 0xFFFFu : (1u << (d - c0)) - 1u);
+  auto y_lanes = [&](int rel) -> uint64_t {
+    const int lo = min(max(-rel - w4, 0), 4), hi = min(max(static_cast<int>(span) - rel - w4, 0), 4);
+    const uint64_t mhi = hi >= 4 ? ~0ull : (1ull << (16 * hi)) - 1ull;
+    const uint64_t mlo = lo >= 4 ? ~0ull : (1ull << (16 * lo)) - 1ull;
+    return mhi & ~mlo & ych_lanes;
+  };
+  // blocks between the first and the last are inside the chunk: all their rows store
+  const uint64_t yfirst = y_lanes(tb0i - rs);
 
   for (int ib = 0; ib < nb; ++ib) {
-    const int buf = ib & 1;
     if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0))  // the state before this block
       *at(pck, cko) = h;
     {
@@ -508,20 +542,17 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       row_steps<FINAL>(std::make_integer_sequence<int, kRow>{}, tk.delta, tk.du, A2, Bq, Cq, h, p);
       if (FINAL) {
         const float s = row_transpose_sum(p, j);
-        L.y[buf][j][ch] = __builtin_fmaf(Dc, tk.u, s) * tk.zs;
+        slot_at(L, scur).y[j][ch] = __builtin_fmaf(Dc, tk.u, s) * tk.zs;
       }
       tk = tn;
     }
     // stage block ib+2 (loaded one iteration ago), prefetch block ib+3, write y of block ib-1
-    if (ib + 2 < nb) row_stage_store<IO, FINAL>(stg, L, snn, scur, N);
+    if (ib + 2 < nb) row_stage_store<IO, FINAL>(stg, L, snn, scur, so, N);
     if (ib + 3 < nb) load(stg, tbl);
-    if (FINAL && ib > 0) {
-      const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(yrel);
-      if (rel < span && ych_ok) {
-        uint32_t o = yo;
-        asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
-        st_g(at(py, o), L.y[buf ^ 1][srow][sch]);
-      }
+    if (FINAL && ib > 0 && __builtin_amdgcn_inverse_ballot_w64(ib == 1 ? yfirst : ych_lanes)) {
+      uint32_t o = yo;
+      asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
+      st_g(at(py, o), *reinterpret_cast<const float*>(reinterpret_cast<const char*>(&L.slot[0].y[0][0]) + snn + so.tc));
     }
     // advance the scalar state
     const uint32_t st = scur;
@@ -540,10 +571,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     __syncthreads();
   }
   const uint32_t xl = snn;  // slot of the last block (the rotation has moved it two places on)
-  if (FINAL) {
-    const uint32_t rel = static_cast<uint32_t>(srow) + static_cast<uint32_t>(yrel);
-    if (rel < span && ych_ok) st_g(at(py, yo), L.y[(nb - 1) & 1][srow][sch]);
-  }
+  if (FINAL && __builtin_amdgcn_inverse_ballot_w64(y_lanes(yrel)))
+    st_g(at(py, yo), *reinterpret_cast<const float*>(reinterpret_cast<const char*>(&L.slot[0].y[0][0]) + xl + so.tc));
 
   if (CKPT && !FINAL) return;
   if (!FINAL) {
