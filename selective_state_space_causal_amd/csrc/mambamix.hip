@@ -15,6 +15,8 @@
 // mm_prefill.h, the decode kernels in mm_decode.h.
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include <stdint.h>
 #include <string.h>
 
@@ -185,6 +187,29 @@ struct PrefillArgs {
   int d, N;
 };
 
+// The row kernel stages with 4-element vector loads when N = 16, d % 4 == 0 and every io
+// tensor is aligned to 4 elements; otherwise element by element.
+template <typename IO>
+bool row_vec(int d, int N, std::initializer_list<const void*> io) {
+  if (N != kRow || d % 4 != 0) return false;
+  for (const void* q : io)
+    if (q != nullptr && !aligned(q, 4 * sizeof(IO))) return false;
+  return true;
+}
+
+template <typename IO, bool FINAL, bool CKPT>
+void launch_k_row(bool vec, dim3 grid, hipStream_t st, const PrefillArgs& a, const IO* x, const IO* z, const IO* dt,
+                  const IO* B, const IO* C, float* conv_state, float* ssm_state, IO* y, CarryWs cw, int64_t Lc,
+                  int whole, float* ckpt) {
+  const dim3 block(kRowThreads);
+  if (vec)
+    hipLaunchKernelGGL((k_row<IO, FINAL, CKPT, true>), grid, block, 0, st, x, z, dt, B, C, a.A_log, a.D, a.dt_bias,
+                       a.conv_w, a.conv_b, a.cu, conv_state, ssm_state, y, cw, a.S, a.T, a.d, a.N, Lc, whole, ckpt);
+  else
+    hipLaunchKernelGGL((k_row<IO, FINAL, CKPT, false>), grid, block, 0, st, x, z, dt, B, C, a.A_log, a.D, a.dt_bias,
+                       a.conv_w, a.conv_b, a.cu, conv_state, ssm_state, y, cw, a.S, a.T, a.d, a.N, Lc, whole, ckpt);
+}
+
 template <typename IO>
 void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st, StageEvents& evs, float* ckpt) {
   const IO* xi = static_cast<const IO*>(a.x);
@@ -193,32 +218,29 @@ void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st,
   const IO* Bi = static_cast<const IO*>(a.B);
   const IO* Ci = static_cast<const IO*>(a.C);
   const dim3 grid(static_cast<unsigned>(row_grid(p.whole ? a.S : p.Pmax, a.d)));
-  const dim3 block(kRowThreads);
   const int whole = p.whole ? 1 : 0;
+  const bool vec = row_vec<IO>(a.d, a.N, {a.x, a.z, a.dt, a.B, a.C, a.y});
+  IO* yo = static_cast<IO*>(a.y);
   if (!p.whole) {
     evs.mark(st);
     hipLaunchKernelGGL(k_chunk_plan, dim3(1), dim3(kPlanThreads), 0, st, a.cu, a.S, p.Lc, cw.off, cw.moff);
   }
   if (p.Mmax > 0) {
     evs.mark(st);
-    hipLaunchKernelGGL((k_row<IO, false>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias,
-                       a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d,
-                       a.N, p.Lc, whole, nullptr);
+    launch_k_row<IO, false, false>(vec, grid, st, a, xi, zi, di, Bi, Ci, a.conv_state, a.ssm_state, yo, cw, p.Lc,
+                                   whole, nullptr);
     evs.mark(st);
     const int64_t q = static_cast<int64_t>(a.d) * kRow;
     hipLaunchKernelGGL((k_carry<kRow>), dim3(static_cast<unsigned>(cdiv(q, kBlock))), dim3(kBlock), 0, st, cw,
                        a.A_log, a.S, a.d, a.N);
   }
   evs.mark(st);
-  if (ckpt != nullptr) {
-    hipLaunchKernelGGL((k_row<IO, true, true>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias,
-                       a.conv_w, a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d,
-                       a.N, p.Lc, whole, ckpt);
-  } else {
-    hipLaunchKernelGGL((k_row<IO, true>), grid, block, 0, st, xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w,
-                       a.conv_b, a.cu, a.conv_state, a.ssm_state, static_cast<IO*>(a.y), cw, a.S, a.T, a.d, a.N, p.Lc,
-                       whole, nullptr);
-  }
+  if (ckpt != nullptr)
+    launch_k_row<IO, true, true>(vec, grid, st, a, xi, zi, di, Bi, Ci, a.conv_state, a.ssm_state, yo, cw, p.Lc, whole,
+                                 ckpt);
+  else
+    launch_k_row<IO, true, false>(vec, grid, st, a, xi, zi, di, Bi, Ci, a.conv_state, a.ssm_state, yo, cw, p.Lc,
+                                  whole, nullptr);
 }
 
 template <typename IO, int NMAX>
@@ -430,10 +452,12 @@ int launch_backward(const BwdPlan& p, const BwdArgs& a, char* ws, hipStream_t st
     // 1. checkpoints: the forward's states before every 16-token block (unless given)
     if (a.ckpt == nullptr) {
       evs.mark(st);
-      hipLaunchKernelGGL((k_row<IO, false, true>), dim3(static_cast<unsigned>(row_grid(a.S, a.d))), block, 0, st,
-                         xi, zi, di, Bi, Ci, a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu,
-                         const_cast<float*>(a.conv_state), const_cast<float*>(a.ssm_state),
-                         static_cast<IO*>(nullptr), CarryWs{}, a.S, a.T, a.d, a.N, a.T + 1, 1, ckpt);
+      const PrefillArgs fa{a.x, a.z, a.dt, a.B, a.C, a.A_log, a.D, a.dt_bias, a.conv_w, a.conv_b, a.cu,
+                           nullptr, nullptr, nullptr, a.S, a.T, a.d, a.N};
+      launch_k_row<IO, false, true>(row_vec<IO>(a.d, a.N, {a.x, a.dt, a.B}), dim3(static_cast<unsigned>(row_grid(a.S, a.d))),
+                                    st, fa, xi, zi, di, Bi, Ci, const_cast<float*>(a.conv_state),
+                                    const_cast<float*>(a.ssm_state), static_cast<IO*>(nullptr), CarryWs{}, a.T + 1, 1,
+                                    ckpt);
     }
     // 2. the reverse pass
     evs.mark(st);

@@ -275,6 +275,80 @@ __device__ __forceinline__ void row_stage_store(const RowStage<IO>& r, RowTiles&
   }
 }
 
+// ---------------------------------------------------------------- vector staging
+// With N = 16, d % 4 == 0 and io aligned to 4 elements, a workgroup stages each tile
+// with one 4-element load per lane of one wave: wave 0 loads the x tile, wave 1 dt,
+// wave 2 z and wave 3 B and C (pass 2), or waves 0..2 x, dt and B (pass 1).  Lane l
+// takes row l / 4, channels 4 (l % 4) .. + 3 of a [16][d] tile, or elements 4 l .. 4 l + 3
+// (token l / 4, states 4 (l % 4) .. + 3) of the [16][16] B or C tile; wave 1 stores the
+// y tile the same way.  A block then costs 5 vector loads and one vector store per
+// workgroup instead of 5 loads and one store per wave.
+constexpr int kKindX = 0, kKindDt = 1, kKindZ = 2, kKindBC = 3, kKindNone = 4;
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <typename IO>
+struct Vec4T;
+template <>
+struct Vec4T<uint16_t> {
+  using T = u32x2_t;
+};
+template <>
+struct Vec4T<float> {
+  using T = f32x4_t;
+};
+template <typename IO>
+using Vec4 = typename Vec4T<IO>::T;
+
+template <typename IO>
+__device__ __forceinline__ Vec4<IO> ld4(gmem<const IO>* p, uint32_t off) {
+  return *reinterpret_cast<gmem<const Vec4<IO>>*>(reinterpret_cast<gmem<const char>*>(p) + off);
+}
+// the four elements into LDS floats S bytes apart (bf16: the raw bits into their upper halves)
+template <int S>
+__device__ __forceinline__ void st_lds4(char* p, const u32x2_t& v) {
+  *reinterpret_cast<uint16_t*>(p + 2) = static_cast<uint16_t>(v.x);
+  *reinterpret_cast<uint16_t*>(p + S + 2) = static_cast<uint16_t>(v.x >> 16);
+  *reinterpret_cast<uint16_t*>(p + 2 * S + 2) = static_cast<uint16_t>(v.y);
+  *reinterpret_cast<uint16_t*>(p + 3 * S + 2) = static_cast<uint16_t>(v.y >> 16);
+}
+template <int S>
+__device__ __forceinline__ void st_lds4(char* p, const f32x4_t& v) {
+  *reinterpret_cast<float*>(p) = v.x;
+  *reinterpret_cast<float*>(p + S) = v.y;
+  *reinterpret_cast<float*>(p + 2 * S) = v.z;
+  *reinterpret_cast<float*>(p + 3 * S) = v.w;
+}
+// the four elements as floats, into 16 contiguous 8-byte aligned LDS bytes
+__device__ __forceinline__ void st_lds4f(char* p, const u32x2_t& v) {
+  float2* q = reinterpret_cast<float2*>(p);
+  q[0] = make_float2(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u));
+  q[1] = make_float2(__uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+}
+__device__ __forceinline__ void st_lds4f(char* p, const f32x4_t& v) {
+  float2* q = reinterpret_cast<float2*>(p);
+  q[0] = make_float2(v.x, v.y);
+  q[1] = make_float2(v.z, v.w);
+}
+// four floats from 16 contiguous 8-byte aligned LDS bytes, stored as io
+__device__ __forceinline__ void st_g4(gmem<uint16_t>* p, uint32_t off, const char* src) {
+  const float2* q = reinterpret_cast<const float2*>(src);
+  const float2 a = q[0], b = q[1];
+  const f32x2_t fa = {a.x, a.y}, fb = {b.x, b.y};
+  const bf16x2_t ha = __builtin_convertvector(fa, bf16x2_t), hb = __builtin_convertvector(fb, bf16x2_t);
+  const u32x2_t v = {__builtin_bit_cast(uint32_t, ha), __builtin_bit_cast(uint32_t, hb)};
+  *reinterpret_cast<gmem<u32x2_t>*>(reinterpret_cast<gmem<char>*>(p) + off) = v;
+}
+__device__ __forceinline__ void st_g4(gmem<float>* p, uint32_t off, const char* src) {
+  const float2* q = reinterpret_cast<const float2*>(src);
+  const float2 a = q[0], b = q[1];
+  const f32x4_t v = {a.x, a.y, b.x, b.y};
+  *reinterpret_cast<gmem<f32x4_t>*>(reinterpret_cast<gmem<char>*>(p) + off) = v;
+}
+
 // the lane mask that holds lanes j of every row with bit j of m16 set
 __device__ __forceinline__ uint64_t row_mask(uint32_t m16) {
   const uint32_t m32 = m16 | (m16 << 16);
@@ -306,7 +380,8 @@ __device__ __forceinline__ void row_work(int64_t w, int ncg, int64_t& k, int& cb
 // chunk leaves a block it shares with the chunk before to that chunk.
 // whole != 0: one chunk per sequence, workgroup chunk index = sequence (no plan).
 // d <= kRowMaxD keeps every per-thread offset within a block's tiles below 2^32.
-template <typename IO, bool FINAL, bool CKPT = false>
+// VEC: vector staging (N = 16, d % 4 == 0, io aligned to 4 elements).
+template <typename IO, bool FINAL, bool CKPT, bool VEC>
 __global__ void __launch_bounds__(kRowThreads) k_row(
     const IO* __restrict__ x, const IO* __restrict__ z, const IO* __restrict__ dt, const IO* __restrict__ B,
     const IO* __restrict__ C, const float* __restrict__ A_log, const float* __restrict__ D,
@@ -389,10 +464,11 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const uint32_t xo = static_cast<uint32_t>(srow * d + schc) * es;
   const uint32_t bco = static_cast<uint32_t>(min(static_cast<int>(threadIdx.x), kRow * N - 1)) * es;
   const uint32_t yo = static_cast<uint32_t>(srow * d + sch) * es;  // the y element this thread stores
-  // the tensors' last block (T - Tl < 16 tokens): its loads are clamped to the last element
+  // the tensors' last block (T - Tl < 16 tokens): its loads are clamped to valid memory
   const int Tl = (T32 - 1) & ~(kRow - 1);
-  const uint32_t xlim = static_cast<uint32_t>((T32 - Tl) * d - 1 - c0) * es;
-  const uint32_t blim = static_cast<uint32_t>((T32 - Tl) * N - 1) * es;
+  const int remT = T32 - Tl;
+  const uint32_t xlim = static_cast<uint32_t>(remT * d - 1 - c0) * es;
+  const uint32_t blim = static_cast<uint32_t>(remT * N - 1) * es;
   auto lim_x = [&](int tb) { return tb == Tl ? xlim : UINT32_MAX; };
   auto lim_b = [&](int tb) { return tb == Tl ? blim : UINT32_MAX; };
 
@@ -402,6 +478,31 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     const int i = min(static_cast<int>(threadIdx.x), kRow * N - 1), t = i / N, n = i - t * N;
     so.bc = static_cast<uint32_t>(((t >> 2) * kRow + n) * 16 + (t & 3) * 4);
   }
+
+  // vector staging: this wave's tile kind and the lane's offsets (see above)
+  const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int kind = FINAL ? wv : (wv == 2 ? kKindBC : (wv == 3 ? kKindNone : wv));
+  const int vr = lane >> 2, vcg = lane & 3;
+  uint32_t vo = 0, vo_t = 0, vl = 0;
+  if (VEC) {
+    if (kind == kKindBC) {
+      vo = static_cast<uint32_t>(4 * lane) * es;
+      vo_t = static_cast<uint32_t>(min(4 * lane, remT * kRow - 4)) * es;
+      vl = static_cast<uint32_t>(offsetof(RowSlot, bc) + (((vr >> 2) * kRow + 4 * vcg) * 16 + (vr & 3) * 4));
+    } else {
+      vo = static_cast<uint32_t>(vr * d + 4 * vcg) * es;
+      vo_t = static_cast<uint32_t>(min(vr, remT - 1) * d + 4 * vcg) * es;
+      const uint32_t rc = static_cast<uint32_t>(vr * kTS + 4 * vcg) * 4u;
+      vl = rc + (kind == kKindX ? offsetof(RowSlot, x) + kKS * kTS * 4
+                                : (kind == kKindDt ? offsetof(RowSlot, dt) : offsetof(RowSlot, z)));
+    }
+  }
+  // x rows 13..15 also go to the next slot's front rows
+  const int vfront = static_cast<int>(offsetof(RowSlot, x)) + ((vr - (kRow - kKS)) * kTS + 4 * vcg) * 4;
+  const uint32_t vy = static_cast<uint32_t>(offsetof(RowSlot, y)) + static_cast<uint32_t>(vr * kTS + 4 * vcg) * 4u;
+  const uint32_t vyo = static_cast<uint32_t>(vr * d + 4 * vcg) * es;
+
   // B/C entries past N stay zero (the staging only writes n < N), and so do the lower
   // halves of bf16 values
   if (sizeof(IO) == 2 || N < kRow) {
@@ -413,22 +514,57 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
 
   const int64_t sx = static_cast<int64_t>(kRow) * d, sb = static_cast<int64_t>(kRow) * N;  // elements per block
   RowSrc<IO> g;
+  gmem<const IO>* gv = nullptr;  // vector staging: this wave's tensor at the block loaded next
   auto set_src = [&](int tb) {
     const int64_t e0 = static_cast<int64_t>(tb) * d + c0, b0 = static_cast<int64_t>(tb) * N;
-    g.x = sbase(x + e0);
-    g.dt = sbase(dt + e0);
-    if (FINAL) g.z = sbase(z + e0);
-    g.B = sbase(B + b0);
-    if (FINAL) g.C = sbase(C + b0);
+    if (VEC) {
+      const IO* t = kind == kKindX ? x + e0 : (kind == kKindDt ? dt + e0 : (kind == kKindZ ? z + e0 : B + b0));
+      gv = sbase(t);
+      if (FINAL) g.C = sbase(C + b0);
+    } else {
+      g.x = sbase(x + e0);
+      g.dt = sbase(dt + e0);
+      if (FINAL) g.z = sbase(z + e0);
+      g.B = sbase(B + b0);
+      if (FINAL) g.C = sbase(C + b0);
+    }
   };
-  auto load = [&](RowStage<IO>& r, int tb) {
-    row_stage_load<IO, FINAL>(r, g, min(xo, lim_x(tb)), min(bco, lim_b(tb)));
+  const int64_t vstride = kind == kKindBC ? sb : sx;
+  RowStage<IO> stg{};
+  Vec4<IO> va{}, vb{};
+  auto load = [&](int tb) {
+    if (VEC) {
+      if (kind != kKindNone) {
+        const uint32_t o = tb == Tl ? vo_t : vo;
+        va = ld4(gv, o);
+        if (FINAL && kind == kKindBC) vb = ld4(g.C, o);
+      }
+    } else {
+      row_stage_load<IO, FINAL>(stg, g, min(xo, lim_x(tb)), min(bco, lim_b(tb)));
+    }
+  };
+  // the staged block into the slot at byte offset sl; x rows 13..15 also into the slot at sn
+  auto store = [&](uint32_t sl, uint32_t sn) {
+    if (VEC) {
+      char* base = reinterpret_cast<char*>(&L.slot[0]);
+      if (kind == kKindX) {
+        st_lds4f(base + sl + vl, va);
+        if (vr >= kRow - kKS) st_lds4f(base + sn + vfront, va);
+      } else if (kind == kKindDt || kind == kKindZ) {
+        st_lds4<4>(base + sl + vl, va);
+      } else if (kind == kKindBC) {
+        st_lds4<16>(base + sl + vl, va);
+        if (FINAL) st_lds4<16>(base + sl + vl + sizeof(float4) * 4 * kRow, vb);
+      }
+    } else {
+      row_stage_store<IO, FINAL>(stg, L, sl, sn, so, N);
+    }
   };
   // blocks 0 and 1 staged, block 2 loaded
-  RowStage<IO> stg{};
   set_src(tb0i);
-  load(stg, tb0i);
-  row_stage_store<IO, FINAL>(stg, L, 0, kSlotBytes, so, N);
+  load(tb0i);
+  store(0, kSlotBytes);
+  if (VEC) __syncthreads();  // the history below overwrites x values other waves staged
   {
     // raw input of token t for the staging channel; tokens before the sequence's start
     // come from its initial conv state (zero before that)
@@ -450,12 +586,12 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   }
   if (nb > 1) {
     set_src(tb0i + kRow);
-    load(stg, tb0i + kRow);
-    row_stage_store<IO, FINAL>(stg, L, kSlotBytes, 2 * kSlotBytes, so, N);
+    load(tb0i + kRow);
+    store(kSlotBytes, 2 * kSlotBytes);
   }
   if (nb > 2) {
     set_src(tb0i + 2 * kRow);
-    load(stg, tb0i + 2 * kRow);
+    load(tb0i + 2 * kRow);
   }
   __syncthreads();
 
@@ -503,16 +639,38 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   gmem<IO>* py = sbase(y + static_cast<int64_t>(tb0i - kRow) * d + c0);
   gmem<float>* pck = CKPT ? sbase(ckpt + (static_cast<int64_t>(tb0 >> 4) + R.s) * d * NMAX) : nullptr;
   int yrel = tb0i - kRow - rs;  // first token of the previous block relative to the chunk start
-  // The lanes of this wave that store y of a block whose first token is rel tokens past
-  // the chunk start: token rows srow = 4 w + r (lanes 16 r .. 16 r + 15) with
-  // 0 <= srow + rel < span, on channels below d.
-  const int w4 = 4 * __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const uint64_t ych_lanes = row_mask(d - c0 >= kRowChans ? 0xFFFFu : (1u << (d - c0)) - 1u);
+  // The lanes that store y of a block whose first token is rel tokens past the chunk
+  // start: those of token rows t with 0 <= t + rel < span, on channels below d.  Element
+  // staging: every wave, token rows 4 w + r in lanes 16 r .. 16 r + 15.  Vector staging:
+  // wave 1, token row r in lanes 4 r .. 4 r + 3 (one lane per 4 channels).
+  const int w4 = 4 * wv;
+  const uint64_t ych_lanes = VEC ? 0x1111111111111111ull * ((1ull << min((d - c0) / 4, 4)) - 1ull)
+                                 : row_mask(d - c0 >= kRowChans ? 0xFFFFu : (1u << (d - c0)) - 1u);
   auto y_lanes = [&](int rel) -> uint64_t {
+    if (VEC) {
+      const int lo = min(max(-rel, 0), kRow), hi = min(max(static_cast<int>(span) - rel, 0), kRow);
+      const uint64_t mhi = hi >= kRow ? ~0ull : (1ull << (4 * hi)) - 1ull;
+      const uint64_t mlo = lo >= kRow ? ~0ull : (1ull << (4 * lo)) - 1ull;
+      return mhi & ~mlo & ych_lanes;
+    }
     const int lo = min(max(-rel - w4, 0), 4), hi = min(max(static_cast<int>(span) - rel - w4, 0), 4);
     const uint64_t mhi = hi >= 4 ? ~0ull : (1ull << (16 * hi)) - 1ull;
     const uint64_t mlo = lo >= 4 ? ~0ull : (1ull << (16 * lo)) - 1ull;
     return mhi & ~mlo & ych_lanes;
+  };
+  // y of the slot at sl, rows selected by the lane mask m
+  auto store_y = [&](uint32_t sl, uint64_t m) {
+    if (VEC) {
+      if (wv == kKindDt && __builtin_amdgcn_inverse_ballot_w64(m)) {
+        uint32_t o = vyo;
+        asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
+        st_g4(py, o, reinterpret_cast<const char*>(&L.slot[0]) + sl + vy);
+      }
+    } else if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      uint32_t o = yo;
+      asm volatile("" : "+v"(o));
+      st_g(at(py, o), *reinterpret_cast<const float*>(reinterpret_cast<const char*>(&L.slot[0].y[0][0]) + sl + so.tc));
+    }
   };
   // blocks between the first and the last are inside the chunk: all their rows store
   const uint64_t yfirst = y_lanes(tb0i - rs);
@@ -547,32 +705,32 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       tk = tn;
     }
     // stage block ib+2 (loaded one iteration ago), prefetch block ib+3, write y of block ib-1
-    if (ib + 2 < nb) row_stage_store<IO, FINAL>(stg, L, snn, scur, so, N);
-    if (ib + 3 < nb) load(stg, tbl);
-    if (FINAL && ib > 0 && __builtin_amdgcn_inverse_ballot_w64(ib == 1 ? yfirst : ych_lanes)) {
-      uint32_t o = yo;
-      asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
-      st_g(at(py, o), *reinterpret_cast<const float*>(reinterpret_cast<const char*>(&L.slot[0].y[0][0]) + snn + so.tc));
-    }
+    if (ib + 2 < nb) store(snn, scur);
+    if (ib + 3 < nb) load(tbl);
+    if (FINAL && ib > 0) store_y(snn, ib == 1 ? yfirst : ych_lanes);
     // advance the scalar state
     const uint32_t st = scur;
     scur = snext;
     snext = snn;
     snn = st;
     tbl += kRow;
-    g.x = sreg(g.x + sx);
-    g.dt = sreg(g.dt + sx);
-    if (FINAL) g.z = sreg(g.z + sx);
-    g.B = sreg(g.B + sb);
-    if (FINAL) g.C = sreg(g.C + sb);
+    if (VEC) {
+      gv = sreg(gv + vstride);
+      if (FINAL) g.C = sreg(g.C + sb);
+    } else {
+      g.x = sreg(g.x + sx);
+      g.dt = sreg(g.dt + sx);
+      if (FINAL) g.z = sreg(g.z + sx);
+      g.B = sreg(g.B + sb);
+      if (FINAL) g.C = sreg(g.C + sb);
+    }
     if (FINAL) py = sreg(py + sx);
     if (CKPT) pck = sreg(pck + static_cast<int64_t>(d) * NMAX);
     yrel += kRow;
     __syncthreads();
   }
   const uint32_t xl = snn;  // slot of the last block (the rotation has moved it two places on)
-  if (FINAL && __builtin_amdgcn_inverse_ballot_w64(y_lanes(yrel)))
-    st_g(at(py, yo), *reinterpret_cast<const float*>(reinterpret_cast<const char*>(&L.slot[0].y[0][0]) + xl + so.tc));
+  if (FINAL) store_y(xl, y_lanes(yrel));
 
   if (CKPT && !FINAL) return;
   if (!FINAL) {
