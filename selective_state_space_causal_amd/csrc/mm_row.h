@@ -333,19 +333,14 @@ __device__ __forceinline__ void st_lds4f(char* p, const f32x4_t& v) {
   q[0] = make_float2(v.x, v.y);
   q[1] = make_float2(v.z, v.w);
 }
-// four floats from 16 contiguous 8-byte aligned LDS bytes, stored as io
-__device__ __forceinline__ void st_g4(gmem<uint16_t>* p, uint32_t off, const char* src) {
-  const float2* q = reinterpret_cast<const float2*>(src);
-  const float2 a = q[0], b = q[1];
-  const f32x2_t fa = {a.x, a.y}, fb = {b.x, b.y};
+// four floats stored as io (bf16: rounded to nearest even)
+__device__ __forceinline__ void st_g4(gmem<uint16_t>* p, uint32_t off, const f32x4_t& v) {
+  const f32x2_t fa = {v.x, v.y}, fb = {v.z, v.w};
   const bf16x2_t ha = __builtin_convertvector(fa, bf16x2_t), hb = __builtin_convertvector(fb, bf16x2_t);
-  const u32x2_t v = {__builtin_bit_cast(uint32_t, ha), __builtin_bit_cast(uint32_t, hb)};
-  *reinterpret_cast<gmem<u32x2_t>*>(reinterpret_cast<gmem<char>*>(p) + off) = v;
+  const u32x2_t u = {__builtin_bit_cast(uint32_t, ha), __builtin_bit_cast(uint32_t, hb)};
+  *reinterpret_cast<gmem<u32x2_t>*>(reinterpret_cast<gmem<char>*>(p) + off) = u;
 }
-__device__ __forceinline__ void st_g4(gmem<float>* p, uint32_t off, const char* src) {
-  const float2* q = reinterpret_cast<const float2*>(src);
-  const float2 a = q[0], b = q[1];
-  const f32x4_t v = {a.x, a.y, b.x, b.y};
+__device__ __forceinline__ void st_g4(gmem<float>* p, uint32_t off, const f32x4_t& v) {
   *reinterpret_cast<gmem<f32x4_t>*>(reinterpret_cast<gmem<char>*>(p) + off) = v;
 }
 
@@ -626,6 +621,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     tk = token_work(xr[0], xr[kTS], xr[2 * kTS], xr[3 * kTS], L.slot[0].dt[j][ch], FINAL ? L.slot[0].z[j][ch] : 0.0f,
                     mfirst);
   }
+  __syncthreads();  // the first iteration's staging rewrites the front rows of slot 0 read just above
 
   float p[kRow];
   float dsum = 0.0f;
@@ -658,18 +654,33 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     const uint64_t mlo = lo >= 4 ? ~0ull : (1ull << (16 * lo)) - 1ull;
     return mhi & ~mlo & ych_lanes;
   };
-  // y of the slot at sl, rows selected by the lane mask m
-  auto store_y = [&](uint32_t sl, uint64_t m) {
+  // y of the slot at sl, read from LDS (vector staging: wave 1, four channels per lane)
+  // and then stored to the rows of the lane mask m
+  auto read_y = [&](uint32_t sl) -> f32x4_t {
+    const char* yb = reinterpret_cast<const char*>(&L.slot[0]) + sl;
+    f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (VEC) {
+      if (wv == kKindDt) {
+        const float2* q = reinterpret_cast<const float2*>(yb + vy);
+        const float2 a = q[0], b = q[1];
+        v = f32x4_t{a.x, a.y, b.x, b.y};
+      }
+    } else {
+      v.x = *reinterpret_cast<const float*>(yb + offsetof(RowSlot, y) + so.tc);
+    }
+    return v;
+  };
+  auto write_y = [&](const f32x4_t& v, uint64_t m) {
     if (VEC) {
       if (wv == kKindDt && __builtin_amdgcn_inverse_ballot_w64(m)) {
         uint32_t o = vyo;
         asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
-        st_g4(py, o, reinterpret_cast<const char*>(&L.slot[0]) + sl + vy);
+        st_g4(py, o, v);
       }
     } else if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       uint32_t o = yo;
       asm volatile("" : "+v"(o));
-      st_g(at(py, o), *reinterpret_cast<const float*>(reinterpret_cast<const char*>(&L.slot[0].y[0][0]) + sl + so.tc));
+      st_g(at(py, o), v.x);
     }
   };
   // blocks between the first and the last are inside the chunk: all their rows store
@@ -678,6 +689,14 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   for (int ib = 0; ib < nb; ++ib) {
     if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0))  // the state before this block
       *at(pck, cko) = h;
+    // First the staging: block ib+2 (loaded one iteration ago) into its slot, the loads of
+    // block ib+3, and y of block ib-1 out of LDS, so that their latencies run under the
+    // arithmetic below.  Block ib+2's slot last held block ib-1, whose tiles were last
+    // read in the iteration before (its y area is not written here); the front rows go to
+    // block ib+3's slot, block ib's, whose x was read in the iteration before as well.
+    if (ib + 2 < nb) store(snn, scur);
+    if (ib + 3 < nb) load(tbl);
+    const f32x4_t yv = FINAL ? read_y(snn) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     {
       const RowSlot& Sc = slot_at(L, scur);
       const RowSlot& Sn = slot_at(L, snext);
@@ -704,10 +723,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       }
       tk = tn;
     }
-    // stage block ib+2 (loaded one iteration ago), prefetch block ib+3, write y of block ib-1
-    if (ib + 2 < nb) store(snn, scur);
-    if (ib + 3 < nb) load(tbl);
-    if (FINAL && ib > 0) store_y(snn, ib == 1 ? yfirst : ych_lanes);
+    if (FINAL && ib > 0) write_y(yv, ib == 1 ? yfirst : ych_lanes);
     // advance the scalar state
     const uint32_t st = scur;
     scur = snext;
@@ -730,7 +746,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     __syncthreads();
   }
   const uint32_t xl = snn;  // slot of the last block (the rotation has moved it two places on)
-  if (FINAL) store_y(xl, y_lanes(yrel));
+  if (FINAL) write_y(read_y(xl), y_lanes(yrel));
 
   if (CKPT && !FINAL) return;
   if (!FINAL) {
