@@ -59,6 +59,41 @@ def test_state_sizes(N, engine):
     _check_prefill(case, 48, f"N={N}", engine)
 
 
+def _offset_copy(a: np.ndarray) -> torch.Tensor:
+    """a on the device, starting one element past an aligned allocation."""
+    t = dev(a)
+    buf = torch.zeros(t.numel() + 1, dtype=t.dtype, device="cuda")
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_row_staging_paths_agree(io, chunk):
+    """The row engine stages a block with one 4-element load per lane when N = 16, d % 4 == 0 and
+    the io tensors are aligned to 4 elements, and element by element otherwise.  The staging does
+    no arithmetic, so the same inputs placed one element past an aligned address (element path)
+    give bit-identical outputs; with d = 70 (not a multiple of 4) the element path matches the
+    oracle."""
+    row = mm.ENGINE_ROW
+    lens = [300, 17, 0, 211, 5, 64]
+    case = make_prefill(29, lens, 64, 16, io)
+    log(f"[staging] io={io} chunk={chunk} d=64 aligned vs offset by one element")
+    y, cs, ss = run_gpu_prefill(case, chunk, engine=row)
+    S = case["S"]
+    cs2, ss2 = dev(case["cs"][:S]), dev(case["ss"][:S])
+    y2 = _offset_copy(np.zeros_like(case["x"]))
+    mm.prefill(*(_offset_copy(case[k]) for k in ("x", "z", "dt", "B", "C")),
+               *(dev(case[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b", "cu")), cs2, ss2,
+               y=y2, chunk_len=chunk, engine=row)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y2), y), "element staging != vector staging (y)"
+    assert np.array_equal(host(ss2), ss) and np.array_equal(host(cs2), cs), "element staging != vector (states)"
+    case70 = make_prefill(31, lens, 70, 16, io)
+    _check_prefill(case70, chunk, f"d=70 io={io}", row)
+
+
 @pytest.mark.parametrize("engine", [0] + ENGINES)
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_many_short_sequences(io, engine):
