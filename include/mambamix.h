@@ -61,7 +61,7 @@ extern "C" {
 #define MM_OK               0
 #define MM_ERR_NULL        -1  /* a required pointer is NULL                                  */
 #define MM_ERR_DIM         -2  /* a negative size, T > INT32_MAX, S == 0 with T > 0, too few events */
-#define MM_ERR_UNSUPPORTED -3  /* K != 4, N outside 1..16, unknown io dtype or engine            */
+#define MM_ERR_UNSUPPORTED -3  /* K != 4, N outside 1..16, unknown io dtype or engine, d too large */
 #define MM_ERR_ALIGN       -4  /* a pointer not aligned to its element size                    */
 #define MM_ERR_WORKSPACE   -5  /* workspace smaller than the size query returns (or NULL)      */
 #define MM_ERR_ALIAS       -6  /* y overlaps an input, or conv_state overlaps ssm_state         */
@@ -110,6 +110,10 @@ size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int3
 #define MM_ENGINE_AUTO 0  /* the library picks from S, T and d                                        */
 #define MM_ENGINE_LANE 1  /* one lane per channel, all N state entries of it in registers             */
 #define MM_ENGINE_ROW  2  /* one channel per 16-lane row, one state entry per lane (for few sequences) */
+/* The row engine (also behind mamba_mixer_prefill_train and mamba_mixer_prefill_backward)
+ * takes d <= MM_ROW_MAX_D: with a larger d an explicit MM_ENGINE_ROW, the training forward
+ * and the backward return MM_ERR_UNSUPPORTED, and MM_ENGINE_AUTO uses the lane engine. */
+#define MM_ROW_MAX_D 4194304
 
 /*
  * mamba_mixer_prefill_chunked -- mamba_mixer_prefill with an explicit time-chunk

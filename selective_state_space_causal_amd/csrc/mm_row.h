@@ -41,7 +41,8 @@ constexpr int kRowThreads = kRowWaves * kWave;         // 256
 constexpr int kRowChans = kRowWaves * (kWave / kRow);  // 16 channels per workgroup
 constexpr int kRowGroup = 4;                           // workgroups sharing 128-byte lines of bf16 io
 constexpr int kXcds = 8;                               // MI355X: workgroup w runs on XCD w % 8
-constexpr int kRowMaxD = 1 << 22;                      // channel limit of the row layout (32-bit tile offsets)
+constexpr int kRowMaxD = MM_ROW_MAX_D;                 // channel limit of the row layout (32-bit tile offsets)
+static_assert(MM_ROW_MAX_D <= (1 << 22), "per-thread tile offsets must stay below 2^32");
 
 // ---------------------------------------------------------------- DPP helpers
 // DPP controls (gfx9 encoding): quad_perm 0x00-0xFF, row_shr:k 0x110+k,

@@ -323,3 +323,19 @@ def test_project_validation(lib):
     assert call(q) == MM_ERR_ALIAS
     assert call(p, wsb=need - 1) == MM_ERR_WORKSPACE
     assert call([ctypes.c_void_p(0)] * 10, T=0) == 0
+
+
+def test_row_engine_channel_limit(lib):
+    """The row layout keeps per-lane tile offsets in 32 bits up to MM_ROW_MAX_D channels: past it
+    the automatic plan takes the lane engine, and the row engine, the training forward and the
+    backward report MM_ERR_UNSUPPORTED."""
+    big = 4194304 + 16
+    assert mm.plan(1, 64, 4194304, 16, 4, 0, mm.ENGINE_ROW)["engine_name"] == "row"
+    assert mm.plan(1, 64, big, 16)["engine_name"] == "lane"
+    with pytest.raises(mm.MambaMixError) as e:
+        mm.plan(1, 64, big, 16, 4, 0, mm.ENGINE_ROW)
+    assert e.value.code == MM_ERR_UNSUPPORTED
+    with pytest.raises(mm.MambaMixError) as e:
+        mm.backward_plan(1, 64, big, 16)
+    assert e.value.code == MM_ERR_UNSUPPORTED
+    assert lib.mamba_mixer_prefill_backward_workspace_bytes(1, 64, big, 16, 4, 0) == 0
