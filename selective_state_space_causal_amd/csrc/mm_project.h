@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_
   const int Pp = NT * 16;
   const int dstride = Rp + 8;
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);  // wave-uniform
   auto xt = [&](int b) {  // staged x rows of buffer b, [kProjXRows][kProjXStride]
     return reinterpret_cast<uint16_t*>(smem + w * kProjWaveBytes + b * kProjStageBytes);
   };
