@@ -418,8 +418,19 @@ __global__ void __launch_bounds__(kBlock) k_bwd_sum_bc(const float* __restrict__
   if (i >= 2 * TN) return;
   const int q = i >= TN ? 1 : 0;
   const int64_t e = i - q * TN;
+  const float* p = pbc + q * TN + e;
+  const int64_t stride = 2 * TN;
+  // sixteen partials loaded at once, added in block order (the same order as one at a time)
   float s = 0.0f;
-  for (int b = 0; b < nchb; ++b) s += pbc[(static_cast<int64_t>(b) * 2 + q) * TN + e];
+  int b = 0;
+  for (; b + 16 <= nchb; b += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = p[(b + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += v[u];
+  }
+  for (; b < nchb; ++b) s += p[b * stride];
   st_io(q ? dC : dB, e, s);
 }
 
