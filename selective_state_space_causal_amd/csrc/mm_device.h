@@ -29,6 +29,39 @@ __device__ __forceinline__ void st_io(uint16_t* p, int64_t i, float v) {
   p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
+// ---------------------------------------------------------------- scalar-base access
+// Global-memory access from a wave-uniform base held as an opaque value in scalar
+// registers: the compiler can then neither fold a thread's offset into a 64-bit
+// vector address nor split the base into per-thread induction variables, so the
+// access takes the scalar-base plus 32-bit vector-offset form (off < 2^32).
+template <typename IO>
+using gmem = __attribute__((address_space(1))) IO;
+
+// p as an opaque value: the compiler keeps it in scalar registers (it is wave-uniform)
+// and cannot reassociate it with a per-thread offset
+template <typename P>
+__device__ __forceinline__ P sreg(P p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+s"(v));
+  return reinterpret_cast<P>(v);
+}
+template <typename IO>
+__device__ __forceinline__ gmem<IO>* sbase(IO* p) {
+  return sreg(reinterpret_cast<gmem<IO>*>(reinterpret_cast<uint64_t>(p)));
+}
+template <typename IO>
+__device__ __forceinline__ IO ld_at(gmem<const IO>* p, uint32_t off) {
+  return *reinterpret_cast<gmem<const IO>*>(reinterpret_cast<gmem<const char>*>(p) + off);
+}
+template <typename IO>
+__device__ __forceinline__ gmem<IO>* at(gmem<IO>* p, uint32_t off) {
+  return reinterpret_cast<gmem<IO>*>(reinterpret_cast<gmem<char>*>(p) + off);
+}
+__device__ __forceinline__ void st_g(gmem<float>* p, float v) { *p = v; }
+__device__ __forceinline__ void st_g(gmem<uint16_t>* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+}
+
 // ---------------------------------------------------------------- math
 // v_exp_f32 / v_log_f32 / v_rcp_f32 are the hardware base-2 exponential, base-2
 // logarithm and reciprocal (about 1 ulp).
