@@ -182,9 +182,10 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
     if y is None:
         y = torch.empty((T, d), dtype=io, device=x.device)
     _check(y, (T, d), io, "y")
-    need = workspace_bytes(S, T, d, N, CONV_K, chunk_len, engine) if T > 0 and d > 0 and S > 0 else 0
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is None:  # (a caller-provided workspace is size-checked by the library)
+        need = workspace_bytes(S, T, d, N, CONV_K, chunk_len, engine) if T > 0 and d > 0 and S > 0 else 0
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if events is None:
@@ -243,9 +244,10 @@ def prefill_train(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens,
     if ckpt is None:
         ckpt = torch.empty((rows, d, 16), dtype=torch.float32, device=x.device)
     _check(ckpt, (rows, d, 16), torch.float32, "ckpt")
-    need = workspace_bytes(S, T, d, N, CONV_K, chunk_len, ENGINE_ROW) if T > 0 and d > 0 and S > 0 else 0
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is None:  # (a caller-provided workspace is size-checked by the library)
+        need = workspace_bytes(S, T, d, N, CONV_K, chunk_len, ENGINE_ROW) if T > 0 and d > 0 and S > 0 else 0
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ev, nev = (None, 0) if events is None else ((ctypes.c_void_p * len(events))(*events), len(events))
@@ -299,9 +301,10 @@ def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqle
         if k not in g:
             g[k] = torch.empty(shape, dtype=dt_, device=x.device)
         _check(g[k], shape, dt_, k)
-    need = backward_plan(S, T, d, N, has_ckpt=ckpt is not None)["workspace"] if d > 0 else 0
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is None:  # (a caller-provided workspace is size-checked by the library)
+        need = backward_plan(S, T, d, N, has_ckpt=ckpt is not None)["workspace"] if d > 0 else 0
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if events is None:
@@ -351,8 +354,8 @@ def project(x, conv_w, conv_b, cu_seqlens, conv_state, w_x, w_dt, dt=None, B=Non
     _check(dt, (T, d), torch.bfloat16, "dt")
     _check(B, (T, N), torch.bfloat16, "B")
     _check(C, (T, N), torch.bfloat16, "C")
-    need = int(load().mamba_mixer_project_workspace_bytes(d, N, R))
-    if workspace is None:
+    if workspace is None:  # (a caller-provided workspace is size-checked by the library)
+        need = int(load().mamba_mixer_project_workspace_bytes(d, N, R))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     rc = load().mamba_mixer_project(
         _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(w_x), _ptr(w_dt), _ptr(dt),
