@@ -11,12 +11,13 @@
 // packed token stream.  Per block:
 //  * the workgroup stages the block's x, z, dt tiles ([16 tokens][16 channels])
 //    and the B, C tiles ([16 tokens][N], contiguous in memory) from HBM into LDS
-//    with coalesced loads, two blocks ahead of their use, and writes y back from
-//    an LDS tile one block behind -- every global access is a run of whole rows;
+//    with coalesced loads (issued for two blocks at a time, every second block, two
+//    blocks before their tiles go to LDS), and writes y back from an LDS tile one
+//    block behind -- every global access is a run of whole rows;
 //  * lane j of a row does the per-token work of token j for the row's channel:
-//    the causal conv (the three older inputs come from lanes j-1..j-3 or from the
-//    previous block by DPP row shifts), SiLU, softplus, delta * u, D * u and
-//    SiLU(z).  Tokens outside the chunk get delta = 0, which makes their step the
+//    the causal conv (its window of inputs t-3 .. t comes from the x tile, whose
+//    three front rows hold the previous block's last inputs), SiLU, softplus,
+//    delta * u, D * u and SiLU(z).  Tokens outside the chunk get delta = 0, which makes their step the
 //    identity (exp(0) = 1, nothing added);
 //  * the 16 recurrence steps: step i broadcasts delta and delta * u of token i from
 //    lane i to the row (DPP row_newbcast, folded into the multiply that uses it);
@@ -24,9 +25,15 @@
 //  * a 16x16 transposing butterfly over the row (DPP row rotations and quad
 //    permutes) sums C_n h_n over n for all 16 tokens at once and leaves token j's
 //    sum in lane j, which finishes y for its token.
-// One barrier per block.  The chunk plan, carries and stash are those of the
-// other engines (mm_prefill.h); with one chunk per sequence ("whole" mode) the
-// workgroup's chunk is simply its sequence and no plan is needed.
+// One barrier per block.  A block's four waves meet at that barrier, so a workgroup
+// advances at the pace of its slowest wave, and the waves that share a SIMD belong
+// to different workgroups.  Each wave therefore raises its issue priority step by
+// step as it works through the block's recurrence and drops it after the barrier:
+// the SIMD issues first for the wave nearest its barrier, and waves just past
+// theirs (staging, LDS reads) fill the gaps.
+// The chunk plan, carries and stash are those of the other engines (mm_prefill.h);
+// with one chunk per sequence ("whole" mode) the workgroup's chunk is simply its
+// sequence and no plan is needed.
 #pragma once
 
 #include <utility>
@@ -69,10 +76,14 @@ __device__ __forceinline__ float comp(const float4& v, int e) {
   return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
 }
 
-// One recurrence step: token I of the block.
+// One recurrence step: token I of the block.  Steps 2, 8 and 13 raise the wave's issue
+// priority to 1, 2 and 3 (k_row drops it to 0 after the block's barrier).
 template <int I, bool READOUT>
 __device__ __forceinline__ void row_step(float delta, float du, float A2, const float4 (&Bq)[4],
                                          const float4 (&Cq)[4], float& h, float (&p)[kRow]) {
+  if (I == 2) __builtin_amdgcn_s_setprio(1);
+  if (I == 8) __builtin_amdgcn_s_setprio(2);
+  if (I == 13) __builtin_amdgcn_s_setprio(3);
   const float a = exp2_hw(bcast<I>(delta) * A2);
   h = __builtin_fmaf(a, h, bcast<I>(du) * comp(Bq[I >> 2], I & 3));
   if (READOUT) p[I] = comp(Cq[I >> 2], I & 3) * h;
@@ -157,7 +168,7 @@ __device__ __forceinline__ float io_f32(float v) { return v; }
 __device__ __forceinline__ float io_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 
 // ---------------------------------------------------------------- LDS tiles
-// A block's tiles sit in one of three slots: block b in slot b % 3.  [token][channel]
+// A block's tiles sit in one of four slots: block b in slot b % 4.  [token][channel]
 // tiles are padded to 18 columns (no LDS bank conflicts for either the row or the
 // column access); the B/C tile is laid out [which][q][n] float4 holding tokens
 // 4q..4q+3, so lane n reads B (or C) of 4 tokens as one float4.  The x tile has three
@@ -174,8 +185,9 @@ struct RowSlot {
   float y[kRow][kTS];  // the block's outputs, from its scan until they are stored
   float4 bc[2][4][kRow];
 };
+constexpr int kSlots = 4;
 struct RowTiles {
-  RowSlot slot[3];
+  RowSlot slot[kSlots];
 };
 constexpr uint32_t kSlotBytes = sizeof(RowSlot);
 
@@ -494,40 +506,55 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     }
   };
   const int64_t vstride = kind == kKindBC ? sb : sx;
-  RowStage<IO> stg{};
-  Vec4<IO> va{}, vb{};
-  auto load = [&](int tb) {
+  // Two sets of staging registers, for a pair of blocks: blocks of even index (relative
+  // to the chunk's first block) go through the first, odd ones through the second.
+  struct StageRegs {
+    RowStage<IO> r;
+    Vec4<IO> a, b;
+  };
+  StageRegs q0{}, q1{};
+  // the loads of the block at token tb; `next` reads the block after the one the source
+  // pointers are at
+  auto load = [&](int tb, StageRegs& q, bool next) {
     if (VEC) {
       if (kind != kKindNone) {
         const uint32_t o = tb == Tl ? vo_t : vo;
-        va = ld4(gv, o);
-        if (FINAL && kind == kKindBC) vb = ld4(g.C, o);
+        q.a = ld4(next ? sreg(gv + vstride) : gv, o);
+        if (FINAL && kind == kKindBC) q.b = ld4(next ? sreg(g.C + sb) : g.C, o);
       }
     } else {
-      row_stage_load<IO, FINAL>(stg, g, min(xo, lim_x(tb)), min(bco, lim_b(tb)));
+      RowSrc<IO> gn = g;
+      if (next) {
+        gn.x = sreg(g.x + sx);
+        gn.dt = sreg(g.dt + sx);
+        if (FINAL) gn.z = sreg(g.z + sx);
+        gn.B = sreg(g.B + sb);
+        if (FINAL) gn.C = sreg(g.C + sb);
+      }
+      row_stage_load<IO, FINAL>(q.r, gn, min(xo, lim_x(tb)), min(bco, lim_b(tb)));
     }
   };
   // the staged block into the slot at byte offset sl; x rows 13..15 also into the slot at sn
-  auto store = [&](uint32_t sl, uint32_t sn) {
+  auto store = [&](uint32_t sl, uint32_t sn, const StageRegs& q) {
     if (VEC) {
       char* base = reinterpret_cast<char*>(&L.slot[0]);
       if (kind == kKindX) {
-        st_lds4f(base + sl + vl, va);
-        if (vr >= kRow - kKS) st_lds4f(base + sn + vfront, va);
+        st_lds4f(base + sl + vl, q.a);
+        if (vr >= kRow - kKS) st_lds4f(base + sn + vfront, q.a);
       } else if (kind == kKindDt || kind == kKindZ) {
-        st_lds4<4>(base + sl + vl, va);
+        st_lds4<4>(base + sl + vl, q.a);
       } else if (kind == kKindBC) {
-        st_lds4<16>(base + sl + vl, va);
-        if (FINAL) st_lds4<16>(base + sl + vl + sizeof(float4) * 4 * kRow, vb);
+        st_lds4<16>(base + sl + vl, q.a);
+        if (FINAL) st_lds4<16>(base + sl + vl + sizeof(float4) * 4 * kRow, q.b);
       }
     } else {
-      row_stage_store<IO, FINAL>(stg, L, sl, sn, so, N);
+      row_stage_store<IO, FINAL>(q.r, L, sl, sn, so, N);
     }
   };
-  // blocks 0 and 1 staged, block 2 loaded
+  // blocks 0 and 1 staged, blocks 2 and 3 loaded
   set_src(tb0i);
-  load(tb0i);
-  store(0, kSlotBytes);
+  load(tb0i, q0, false);
+  store(0, kSlotBytes, q0);
   if (VEC) __syncthreads();  // the history below overwrites x values other waves staged
   {
     // raw input of token t for the staging channel; tokens before the sequence's start
@@ -550,12 +577,16 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   }
   if (nb > 1) {
     set_src(tb0i + kRow);
-    load(tb0i + kRow);
-    store(kSlotBytes, 2 * kSlotBytes);
+    load(tb0i + kRow, q1, false);
+    store(kSlotBytes, 2 * kSlotBytes, q1);
   }
   if (nb > 2) {
     set_src(tb0i + 2 * kRow);
-    load(tb0i + 2 * kRow);
+    load(tb0i + 2 * kRow, q0, false);
+  }
+  if (nb > 3) {
+    set_src(tb0i + 3 * kRow);
+    load(tb0i + 3 * kRow, q1, false);
   }
   __syncthreads();
 
@@ -596,10 +627,10 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   float dsum = 0.0f;
   const uint32_t span = static_cast<uint32_t>(R.end - R.start);
   const uint32_t cko = static_cast<uint32_t>(c * NMAX + j) * 4u;
-  // scalar loop state: the slots of blocks ib, ib+1, ib+2 (byte offsets), the block
-  // loaded next, and the y / checkpoint rows of the previous / this block
-  uint32_t scur = 0, snext = kSlotBytes, snn = 2 * kSlotBytes;
-  int tbl = tb0i + 3 * kRow;
+  // scalar loop state: the slots of blocks ib .. ib+3 (byte offsets; block ib+3's is block
+  // ib-1's), the block loaded next, and the y / checkpoint rows of the previous / this block
+  uint32_t s0 = 0, s1 = kSlotBytes, s2 = 2 * kSlotBytes, s3 = 3 * kSlotBytes;
+  int tbl = tb0i + 4 * kRow;
   set_src(tbl);
   gmem<IO>* py = sbase(y + static_cast<int64_t>(tb0i - kRow) * d + c0);
   gmem<float>* pck = CKPT ? sbase(ckpt + (static_cast<int64_t>(tb0 >> 4) + R.s) * d * NMAX) : nullptr;
@@ -658,17 +689,25 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   for (int ib = 0; ib < nb; ++ib) {
     if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0))  // the state before this block
       *at(pck, cko) = h;
-    // First the staging: block ib+2 (loaded one iteration ago) into its slot, the loads of
-    // block ib+3, and y of block ib-1 out of LDS, so that their latencies run under the
-    // arithmetic below.  Block ib+2's slot last held block ib-1, whose tiles were last
-    // read in the iteration before (its y area is not written here); the front rows go to
-    // block ib+3's slot, block ib's, whose x was read in the iteration before as well.
-    if (ib + 2 < nb) store(snn, scur);
-    if (ib + 3 < nb) load(tbl);
-    const f32x4_t yv = FINAL ? read_y(snn) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // First the staging, every second block: blocks ib+2 and ib+3 (loaded two iterations
+    // ago) into their slots, then the loads of blocks ib+4 and ib+5 into the same registers;
+    // and y of block ib-1 out of LDS.  Their latencies run under the arithmetic below, and
+    // the loads have two blocks' arithmetic to arrive: the wait before the stores waits for
+    // every outstanding global access (loads and the y stores mixed), which are then all two
+    // iterations old.  Blocks ib+2 and ib+3 take the slots of blocks ib-2 and ib-1, whose
+    // tiles were last read in iterations ib-2 and ib-1 (their y areas are not written here);
+    // the front rows of ib+2 go to ib+3's slot before its own rows, those of ib+3 to block
+    // ib's slot, whose x rows were read in iteration ib-1.
+    if ((ib & 1) == 0) {
+      if (ib + 2 < nb) store(s2, s3, q0);
+      if (ib + 3 < nb) store(s3, s0, q1);
+      if (ib + 4 < nb) load(tbl, q0, false);
+      if (ib + 5 < nb) load(tbl + kRow, q1, true);
+    }
+    const f32x4_t yv = FINAL ? read_y(s3) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     {
-      const RowSlot& Sc = slot_at(L, scur);
-      const RowSlot& Sn = slot_at(L, snext);
+      const RowSlot& Sc = slot_at(L, s0);
+      const RowSlot& Sn = slot_at(L, s1);
       float4 Bq[4], Cq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -688,16 +727,17 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       row_steps<FINAL>(std::make_integer_sequence<int, kRow>{}, tk.delta, tk.du, A2, Bq, Cq, h, p);
       if (FINAL) {
         const float s = row_transpose_sum(p, j);
-        slot_at(L, scur).y[j][ch] = __builtin_fmaf(Dc, tk.u, s) * tk.zs;
+        slot_at(L, s0).y[j][ch] = __builtin_fmaf(Dc, tk.u, s) * tk.zs;
       }
       tk = tn;
     }
     if (FINAL && ib > 0) write_y(yv, ib == 1 ? yfirst : ych_lanes);
     // advance the scalar state
-    const uint32_t st = scur;
-    scur = snext;
-    snext = snn;
-    snn = st;
+    const uint32_t st = s0;
+    s0 = s1;
+    s1 = s2;
+    s2 = s3;
+    s3 = st;
     tbl += kRow;
     if (VEC) {
       gv = sreg(gv + vstride);
@@ -713,8 +753,9 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     if (CKPT) pck = sreg(pck + static_cast<int64_t>(d) * NMAX);
     yrel += kRow;
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
   }
-  const uint32_t xl = snn;  // slot of the last block (the rotation has moved it two places on)
+  const uint32_t xl = s3;  // slot of the last block (the rotation has moved it on once more)
   if (FINAL) write_y(read_y(xl), y_lanes(yrel));
 
   if (CKPT && !FINAL) return;
