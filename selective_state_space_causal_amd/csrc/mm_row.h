@@ -11,9 +11,9 @@
 // packed token stream.  Per block:
 //  * the workgroup stages the block's x, z, dt tiles ([16 tokens][16 channels])
 //    and the B, C tiles ([16 tokens][N], contiguous in memory) from HBM into LDS
-//    with coalesced loads (issued for two blocks at a time, every second block, two
-//    blocks before their tiles go to LDS), and writes y back from an LDS tile one
-//    block behind -- every global access is a run of whole rows;
+//    with coalesced loads issued two blocks before the tiles go to LDS (three
+//    blocks before their use), and writes y back from an LDS tile one block
+//    behind -- every global access is a run of whole rows;
 //  * lane j of a row does the per-token work of token j for the row's channel:
 //    the causal conv (its window of inputs t-3 .. t comes from the x tile, whose
 //    three front rows hold the previous block's last inputs), SiLU, softplus,
@@ -168,7 +168,7 @@ __device__ __forceinline__ float io_f32(float v) { return v; }
 __device__ __forceinline__ float io_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 
 // ---------------------------------------------------------------- LDS tiles
-// A block's tiles sit in one of four slots: block b in slot b % 4.  [token][channel]
+// A block's tiles sit in one of three slots: block b in slot b % 3.  [token][channel]
 // tiles are padded to 18 columns (no LDS bank conflicts for either the row or the
 // column access); the B/C tile is laid out [which][q][n] float4 holding tokens
 // 4q..4q+3, so lane n reads B (or C) of 4 tokens as one float4.  The x tile has three
@@ -185,7 +185,7 @@ struct RowSlot {
   float y[kRow][kTS];  // the block's outputs, from its scan until they are stored
   float4 bc[2][4][kRow];
 };
-constexpr int kSlots = 4;
+constexpr int kSlots = 3;
 struct RowTiles {
   RowSlot slot[kSlots];
 };
@@ -323,6 +323,26 @@ __device__ __forceinline__ void st_g4(gmem<uint16_t>* p, uint32_t off, const f32
 }
 __device__ __forceinline__ void st_g4(gmem<float>* p, uint32_t off, const f32x4_t& v) {
   *reinterpret_cast<gmem<f32x4_t>*>(reinterpret_cast<gmem<char>*>(p) + off) = v;
+}
+// The same stores, and a one-float store, written as assembly.  The compiler then does not
+// count them among the outstanding vector-memory operations: with stores among them it
+// takes the counter as unordered and waits for zero before using any loaded register,
+// which would drain the staging loads that are meant to stay in flight across two
+// blocks.  Not counting the stores only makes its waits longer than needed, never short:
+// loads complete in the order they were issued, so while a load is outstanding so are
+// the loads after it.  The stores' addresses and data are read at issue; a store of
+// more than 8 bytes needs one wait state before its data registers are written again.
+__device__ __forceinline__ void st_g4_uncounted(gmem<uint16_t>* p, uint32_t off, const f32x4_t& v) {
+  const f32x2_t fa = {v.x, v.y}, fb = {v.z, v.w};
+  const bf16x2_t ha = __builtin_convertvector(fa, bf16x2_t), hb = __builtin_convertvector(fb, bf16x2_t);
+  const u32x2_t u = {__builtin_bit_cast(uint32_t, ha), __builtin_bit_cast(uint32_t, hb)};
+  asm volatile("global_store_dwordx2 %0, %1, %2" ::"v"(off), "v"(u), "s"(p) : "memory");
+}
+__device__ __forceinline__ void st_g4_uncounted(gmem<float>* p, uint32_t off, const f32x4_t& v) {
+  asm volatile("global_store_dwordx4 %0, %1, %2\n\ts_nop 0" ::"v"(off), "v"(v), "s"(p) : "memory");
+}
+__device__ __forceinline__ void st_g_uncounted(gmem<float>* p, uint32_t off, float v) {
+  asm volatile("global_store_dword %0, %1, %2" ::"v"(off), "v"(v), "s"(p) : "memory");
 }
 
 // the lane mask that holds lanes j of every row with bit j of m16 set
@@ -462,7 +482,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const int vr = lane >> 2, vcg = lane & 3;
   uint32_t vo = 0, vo_t = 0, vl = 0;
   if (VEC) {
-    if (kind == kKindBC) {
+    if (kind == kKindBC || kind == kKindNone) {
       vo = static_cast<uint32_t>(4 * lane) * es;
       vo_t = static_cast<uint32_t>(min(4 * lane, remT * kRow - 4)) * es;
       vl = static_cast<uint32_t>(offsetof(RowSlot, bc) + (((vr >> 2) * kRow + 4 * vcg) * 16 + (vr & 3) * 4));
@@ -491,6 +511,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const int64_t sx = static_cast<int64_t>(kRow) * d, sb = static_cast<int64_t>(kRow) * N;  // elements per block
   RowSrc<IO> g;
   gmem<const IO>* gv = nullptr;  // vector staging: this wave's tensor at the block loaded next
+  gmem<const IO>* gv_last = nullptr;
   auto set_src = [&](int tb) {
     const int64_t e0 = static_cast<int64_t>(tb) * d + c0, b0 = static_cast<int64_t>(tb) * N;
     if (VEC) {
@@ -505,33 +526,28 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       if (FINAL) g.C = sbase(C + b0);
     }
   };
-  const int64_t vstride = kind == kKindBC ? sb : sx;
-  // Two sets of staging registers, for a pair of blocks: blocks of even index (relative
-  // to the chunk's first block) go through the first, odd ones through the second.
+  const int64_t vstride = (kind == kKindBC || kind == kKindNone) ? sb : sx;
+  // Two sets of staging registers: a block's loads are issued two iterations before its
+  // tiles go to LDS, blocks of even index (relative to the chunk's first block) through
+  // the first set, odd ones through the second; the loop body is written out twice, so
+  // that no registers move between the sets.  With vector staging every wave issues the
+  // same two loads per block, whatever its tile kind and whether the block exists (the
+  // second is C for the B/C wave and a repeat of the first for the others; past the
+  // chunk's last block both re-read that block), so that the compiler's count of
+  // outstanding loads is the same on every path and its waits only drain the loads of
+  // the block being stored.
   struct StageRegs {
     RowStage<IO> r;
     Vec4<IO> a, b;
   };
   StageRegs q0{}, q1{};
-  // the loads of the block at token tb; `next` reads the block after the one the source
-  // pointers are at
-  auto load = [&](int tb, StageRegs& q, bool next) {
+  auto load = [&](int tb, StageRegs& q) {
     if (VEC) {
-      if (kind != kKindNone) {
-        const uint32_t o = tb == Tl ? vo_t : vo;
-        q.a = ld4(next ? sreg(gv + vstride) : gv, o);
-        if (FINAL && kind == kKindBC) q.b = ld4(next ? sreg(g.C + sb) : g.C, o);
-      }
+      const uint32_t o = tb == Tl ? vo_t : vo;
+      q.a = ld4(gv, o);
+      q.b = ld4(FINAL && kind == kKindBC ? g.C : gv, o);
     } else {
-      RowSrc<IO> gn = g;
-      if (next) {
-        gn.x = sreg(g.x + sx);
-        gn.dt = sreg(g.dt + sx);
-        if (FINAL) gn.z = sreg(g.z + sx);
-        gn.B = sreg(g.B + sb);
-        if (FINAL) gn.C = sreg(g.C + sb);
-      }
-      row_stage_load<IO, FINAL>(q.r, gn, min(xo, lim_x(tb)), min(bco, lim_b(tb)));
+      row_stage_load<IO, FINAL>(q.r, g, min(xo, lim_x(tb)), min(bco, lim_b(tb)));
     }
   };
   // the staged block into the slot at byte offset sl; x rows 13..15 also into the slot at sn
@@ -553,7 +569,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   };
   // blocks 0 and 1 staged, blocks 2 and 3 loaded
   set_src(tb0i);
-  load(tb0i, q0, false);
+  load(tb0i, q0);
   store(0, kSlotBytes, q0);
   if (VEC) __syncthreads();  // the history below overwrites x values other waves staged
   {
@@ -577,22 +593,19 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   }
   if (nb > 1) {
     set_src(tb0i + kRow);
-    load(tb0i + kRow, q1, false);
+    load(tb0i + kRow, q1);
     store(kSlotBytes, 2 * kSlotBytes, q1);
   }
-  if (nb > 2) {
-    set_src(tb0i + 2 * kRow);
-    load(tb0i + 2 * kRow, q0, false);
-  }
-  if (nb > 3) {
-    set_src(tb0i + 3 * kRow);
-    load(tb0i + 3 * kRow, q1, false);
-  }
+  // blocks 2 and 3 (or the last block again), loaded
+  const int tlasti = static_cast<int>(tlast);
+  set_src(min(tb0i + 2 * kRow, tlasti));
+  load(min(tb0i + 2 * kRow, tlasti), q0);
+  set_src(min(tb0i + 3 * kRow, tlasti));
+  load(min(tb0i + 3 * kRow, tlasti), q1);
   __syncthreads();
 
   // the lanes of the chunk's tokens in the first and the last block (all lanes between)
   const uint64_t mfirst = row_mask(token_bits(rs - tb0i, re - tb0i));
-  const int tlasti = static_cast<int>(tlast);
   const uint64_t mlast = row_mask(token_bits(rs - tlasti, re - tlasti));
 
   // The per-token work of a block (conv, SiLU, softplus, SiLU(z)) runs one iteration
@@ -627,11 +640,22 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   float dsum = 0.0f;
   const uint32_t span = static_cast<uint32_t>(R.end - R.start);
   const uint32_t cko = static_cast<uint32_t>(c * NMAX + j) * 4u;
-  // scalar loop state: the slots of blocks ib .. ib+3 (byte offsets; block ib+3's is block
-  // ib-1's), the block loaded next, and the y / checkpoint rows of the previous / this block
-  uint32_t s0 = 0, s1 = kSlotBytes, s2 = 2 * kSlotBytes, s3 = 3 * kSlotBytes;
+  // scalar loop state: the slots of blocks ib, ib+1, ib+2 (byte offsets), the block
+  // loaded next, and the y / checkpoint rows of the previous / this block
+  uint32_t s0 = 0, s1 = kSlotBytes, s2 = 2 * kSlotBytes;
   int tbl = tb0i + 4 * kRow;
-  set_src(tbl);
+  set_src(min(tbl, tlasti));
+  // the source pointers of the chunk's last block (the loads past it re-read it)
+  const RowSrc<IO> g_last = [&] {
+    const RowSrc<IO> gs = g;
+    gmem<const IO>* const gvs = gv;
+    set_src(tlasti);
+    const RowSrc<IO> gl = g;
+    gv_last = gv;
+    g = gs;
+    gv = gvs;
+    return gl;
+  }();
   gmem<IO>* py = sbase(y + static_cast<int64_t>(tb0i - kRow) * d + c0);
   gmem<float>* pck = CKPT ? sbase(ckpt + (static_cast<int64_t>(tb0 >> 4) + R.s) * d * NMAX) : nullptr;
   int yrel = tb0i - kRow - rs;  // first token of the previous block relative to the chunk start
@@ -674,8 +698,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     if (VEC) {
       if (wv == kKindDt && __builtin_amdgcn_inverse_ballot_w64(m)) {
         uint32_t o = vyo;
-        asm volatile("" : "+v"(o));  // keeps the offset 32-bit at the store (scalar-base form)
-        st_g4(py, o, v);
+        asm volatile("" : "+v"(o));
+        st_g4_uncounted(py, o, v);
       }
     } else if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       uint32_t o = yo;
@@ -686,25 +710,32 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   // blocks between the first and the last are inside the chunk: all their rows store
   const uint64_t yfirst = y_lanes(tb0i - rs);
 
-  for (int ib = 0; ib < nb; ++ib) {
-    if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0))  // the state before this block
-      *at(pck, cko) = h;
-    // First the staging, every second block: blocks ib+2 and ib+3 (loaded two iterations
-    // ago) into their slots, then the loads of blocks ib+4 and ib+5 into the same registers;
-    // and y of block ib-1 out of LDS.  Their latencies run under the arithmetic below, and
-    // the loads have two blocks' arithmetic to arrive: the wait before the stores waits for
-    // every outstanding global access (loads and the y stores mixed), which are then all two
-    // iterations old.  Blocks ib+2 and ib+3 take the slots of blocks ib-2 and ib-1, whose
-    // tiles were last read in iterations ib-2 and ib-1 (their y areas are not written here);
-    // the front rows of ib+2 go to ib+3's slot before its own rows, those of ib+3 to block
-    // ib's slot, whose x rows were read in iteration ib-1.
-    if ((ib & 1) == 0) {
-      if (ib + 2 < nb) store(s2, s3, q0);
-      if (ib + 3 < nb) store(s3, s0, q1);
-      if (ib + 4 < nb) load(tbl, q0, false);
-      if (ib + 5 < nb) load(tbl + kRow, q1, true);
+  auto block = [&](int ib, StageRegs& q) {
+    if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0)) {  // the state before this block
+      uint32_t o = cko;
+      asm volatile("" : "+v"(o));
+      st_g_uncounted(pck, o, h);
     }
-    const f32x4_t yv = FINAL ? read_y(s3) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // First the staging: block ib+2 (loaded two iterations ago) into its slot, the loads of
+    // block ib+4 into the registers that held it, and y of block ib-1 out of LDS, so that
+    // their latencies run under the arithmetic below.  Block ib+2's slot last held block
+    // ib-1, whose tiles were last read in the iteration before (its y area is not written
+    // here); the front rows go to block ib+3's slot, block ib's, whose x was read in the
+    // iteration before as well.
+    if (ib + 2 < nb) store(s2, s0, q);
+    if (VEC || ib + 4 < nb) {
+      const bool past = ib + 4 >= nb;
+      const RowSrc<IO> gn = g;
+      gmem<const IO>* const gvn = gv;
+      if (past) {
+        g = g_last;
+        gv = gv_last;
+      }
+      load(past ? tlasti : tbl, q);
+      g = gn;
+      gv = gvn;
+    }
+    const f32x4_t yv = FINAL ? read_y(s2) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     {
       const RowSlot& Sc = slot_at(L, s0);
       const RowSlot& Sn = slot_at(L, s1);
@@ -736,8 +767,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     const uint32_t st = s0;
     s0 = s1;
     s1 = s2;
-    s2 = s3;
-    s3 = st;
+    s2 = st;
     tbl += kRow;
     if (VEC) {
       gv = sreg(gv + vstride);
@@ -754,8 +784,12 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     yrel += kRow;
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
+  };
+  for (int ib = 0; ib < nb; ib += 2) {
+    block(ib, q0);
+    if (ib + 1 < nb) block(ib + 1, q1);
   }
-  const uint32_t xl = s3;  // slot of the last block (the rotation has moved it on once more)
+  const uint32_t xl = s2;  // slot of the last block (the rotation has moved it two places on)
   if (FINAL) write_y(read_y(xl), y_lanes(yrel));
 
   if (CKPT && !FINAL) return;
