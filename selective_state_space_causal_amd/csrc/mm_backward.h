@@ -288,6 +288,10 @@ __global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_e
 
       __builtin_amdgcn_sched_barrier(0);
       // the block's states from its checkpoint, and the readout p
+      // issue priority rises through the block (forward recompute 1, adjoint 2, tail 3) and
+      // drops after the block's last barrier: the SIMD issues first for the wave nearest the
+      // barriers its workgroup waits at (the waves sharing a SIMD belong to other workgroups)
+      __builtin_amdgcn_s_setprio(1);
       float pr[kRow];
       float h = h0;
       bwd_fwd_steps(std::make_integer_sequence<int, kRow>{}, delta, du, A2, Bq, Cq, h, &L.red[1][ch].v[0][j],
@@ -316,6 +320,7 @@ __global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_e
       }
       float(&rB)[kRow][kRow] = L.red[0][ch].v;
       float(&rC)[kRow][kRow] = L.red[1][ch].v;
+      __builtin_amdgcn_s_setprio(2);
       bwd_rev_steps(std::make_integer_sequence<int, kRow>{}, dp_r, du_r, delta_r, An, Br, Cr, lam, anext,
                     accA, s1, s2, rB, rC, jz);
       __builtin_amdgcn_sched_barrier(0);
@@ -324,6 +329,7 @@ __global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_e
 
       __builtin_amdgcn_sched_barrier(0);
       // per-token tail
+      __builtin_amdgcn_s_setprio(3);
       const float dut = __builtin_fmaf(dp, Dc, delta * S1);
       const float ddel = __builtin_fmaf(u, S1, S2);
       const float dv = act ? ddel * sigmoid_hw(v) : 0.0f;
@@ -378,6 +384,7 @@ __global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_e
         }
       }
       __syncthreads();
+      __builtin_amdgcn_s_setprio(0);
     }
 
     // gradient of the initial SSM state: the adjoint carried through the block's first token
