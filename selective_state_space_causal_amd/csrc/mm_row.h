@@ -622,8 +622,13 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     xc = __builtin_fmaf(w2, x1, xc);
     xc = __builtin_fmaf(w3, xv, xc);
     o.u = silu(xc);
-    // tokens outside the chunk get delta = 0: their step is the identity
-    o.delta = softplus(dtv + dtb) * (__builtin_amdgcn_inverse_ballot_w64(m) ? 1.0f : 0.0f);
+    // tokens outside the chunk get delta = 0: their step is the identity.  softplus is
+    // computed on every lane (the empty asm keeps the select from becoming a branch around
+    // it), then selected: one instruction, and a non-finite dt of a token outside the
+    // chunk cannot reach the chunk's state through a multiply by zero
+    float sp = softplus(dtv + dtb);
+    asm volatile("" : "+v"(sp));
+    o.delta = __builtin_amdgcn_inverse_ballot_w64(m) ? sp : 0.0f;
     o.du = o.delta * o.u;
     o.zs = FINAL ? silu(zv) : 0.0f;
     return o;
