@@ -255,12 +255,22 @@ __global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_e
       const int64_t tb = tb0 + static_cast<int64_t>(ib) * kRow;
       const int64_t t = tb + j;
       const bool act = t >= start && t < end;
-      // the next (earlier) block's checkpoint and conv look-back, loaded a block ahead
-      float h0n = 0.0f, prevn = 0.0f;
-      if (ib > 0) {
-        h0n = ckpt[((crow0 + ib - 1) * d64 + cc) * kRow + j];
-        if (j >= kRow - kKS) prevn = hist(tb - 2 * kRow + j);
-      }
+      // Staging and loads, at the top of the block so that they have its whole arithmetic
+      // to arrive: block ib-1 (loaded an iteration ago) into the other buffer, whose block
+      // ib+1 was last read before the previous iteration's barriers; the next (earlier)
+      // block's checkpoint and conv look-back, loaded as raw values whatever the lane and
+      // block (the indices clamped into range) and resolved at the end of the block; then
+      // the loads of block ib-2.  The first use of any of them is then past the block's
+      // arithmetic: the compiler waits for every outstanding load at a use (the stores in
+      // the loop make it treat the counter as unordered), and an early use would stall on
+      // the staging loads.
+      if (ib >= 1) bwd_stage_store<IO>(stg, L, buf ^ 1, N);
+      const float h0n = ckpt[((crow0 + (ib > 0 ? ib - 1 : 0)) * d64 + cc) * kRow + j];
+      // look-back token of lane j >= 13, relative to the sequence start (chunks < 2^31 tokens)
+      const int prel = static_cast<int>(tb - start) - 2 * kRow + j;
+      const IO praw = x[(start + (prel > 0 ? prel : 0)) * d64 + cc];
+      const float pcs = cs0[min(max(prel + kKS, 0), kKS - 1)];
+      if (ib >= 2) bwd_stage_load<IO>(stg, x, z, dt, dy, B, C, tb - 2 * kRow, T32, d, N, c0);
 
       // per-token forward quantities (lane j = token j)
       const float xv = (t < start) ? hist0 : L.x[buf][j][ch];
@@ -355,11 +365,9 @@ __global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_e
       L.o[1][j][ch] = dzv;
       L.o[2][j][ch] = dv;
       h0 = h0n;
-      prev = prevn;
+      prev = (ib > 0 && j >= kRow - kKS) ? (prel >= 0 ? io_f32(praw) : (prel + kKS >= 0 ? pcs : 0.0f)) : 0.0f;
 
       __builtin_amdgcn_sched_barrier(0);
-      if (ib >= 1) bwd_stage_store<IO>(stg, L, buf ^ 1, N);
-      if (ib >= 2) bwd_stage_load<IO>(stg, x, z, dt, dy, B, C, tb - 2 * kRow, T32, d, N, c0);
       __syncthreads();
       {  // sums over the workgroup's 16 channels, and the io outputs of the block
         const int tt = threadIdx.x >> 4, n = threadIdx.x & (kRow - 1);
