@@ -106,13 +106,13 @@ def test_many_short_sequences(io, engine):
 
 
 def test_auto_plan_picks_lane_engine_for_many_sequences():
-    """4096 sequences x 64 channels reach the lane engine's wave threshold: the automatic plan
+    """8192 sequences x 64 channels reach the lane engine's wave threshold: the automatic plan
     uses it, and the result matches the oracle."""
     rng = np.random.default_rng(23)
-    lens = rng.integers(1, 9, size=4096).tolist()
+    lens = rng.integers(1, 9, size=8192).tolist()
     case = make_prefill(23, lens, 64, 16, "bf16")
     assert mm.plan(case["S"], case["T"], 64, 16)["engine_name"] == "lane"
-    _check_prefill(case, 0, "4096 sequences (auto -> lane)", 0)
+    _check_prefill(case, 0, "8192 sequences (auto -> lane)", 0)
 
 
 @pytest.mark.parametrize("engine", ENGINES)
