@@ -716,11 +716,6 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   const uint64_t yfirst = y_lanes(tb0i - rs);
 
   auto block = [&](int ib, StageRegs& q) {
-    if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0)) {  // the state before this block
-      uint32_t o = cko;
-      asm volatile("" : "+v"(o));
-      st_g_uncounted(pck, o, h);
-    }
     // First the staging: block ib+2 (loaded two iterations ago) into its slot, the loads of
     // block ib+4 into the registers that held it, and y of block ib-1 out of LDS, so that
     // their latencies run under the arithmetic below.  Block ib+2's slot last held block
@@ -739,6 +734,14 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       load(past ? tlasti : tbl, q);
       g = gn;
       gv = gvn;
+    }
+    // the state before this block, stored after the staging: the hardware counts the store
+    // among the outstanding accesses, so issued before the staging's waits it would make
+    // them wait for it too
+    if (CKPT && cvalid && (ib > 0 || tb0 == R.start || R.j == 0)) {
+      uint32_t o = cko;
+      asm volatile("" : "+v"(o));
+      st_g_uncounted(pck, o, h);
     }
     const f32x4_t yv = FINAL ? read_y(s2) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     {
