@@ -136,28 +136,34 @@ __device__ __forceinline__ void bwd_fwd_steps(std::integer_sequence<int, I...>, 
 
 // adjoint step, token I of the block (called for I = 15 down to 0).  lam holds
 // lambda of token I+1 on entry and of token I on exit; anext the decay of token I+1
-// on entry and of token I on exit.  The forward phase left the state h_I in rC[I]
-// and the decay a_I in rB[I]; each is read before the slot is overwritten with the
-// dC or dB term.  lambda h_{I-1} a_I = lambda (h_I - du_I B_I).
+// on entry and of token I on exit; hcur the state after token I on entry and the
+// state before it on exit.  The forward phase left the state h_I in rC[I] and the
+// decay a_I in rB[I]; each slot is read before it is overwritten with the dC or dB
+// term (slot I-1 is read at step I, one step before step I-1 overwrites it).
+// lambda a_I h_{I-1} is formed as a product of the three: the equal difference
+// lambda (h_I - du_I B_I) cancels where a_I h_{I-1} is small beside du_I B_I (large
+// delta |A|), and that error is then scaled by delta A.
 template <int I>
 __device__ __forceinline__ void bwd_rev_step(float dp, float du, float delta, float An,
                                              const float4 (&Bq)[4], const float4 (&Cq)[4],
                                              float& lam, float& anext, float& accA,
                                              float (&s1)[kRow], float (&s2)[kRow], float (&rB)[kRow][kRow],
-                                             float (&rC)[kRow][kRow], int j) {
+                                             float (&rC)[kRow][kRow], int j, float& hcur, float h0) {
   const float dpi = bcast<I>(dp);
   lam = __builtin_fmaf(anext, lam, dpi * comp(Cq[I >> 2], I & 3));
-  const float hI = rC[I][j];  // the state after token I, left here by the forward phase
+  const float hI = hcur;                            // the state after token I
+  const float hprev = I > 0 ? rC[I - 1][j] : h0;    // the state before token I
   rC[I][j] = dpi * hI;
   const float dui = bcast<I>(du);
   const float aI = rB[I][j];
   rB[I][j] = lam * dui;
   const float sb = lam * comp(Bq[I >> 2], I & 3);
   s1[I] = sb;
-  const float q = __builtin_fmaf(-dui, sb, lam * hI);
+  const float q = lam * (aI * hprev);
   s2[I] = q * An;
   accA = __builtin_fmaf(bcast<I>(delta), q, accA);
   anext = aI;
+  hcur = hprev;
 }
 
 template <int... I>
@@ -165,8 +171,9 @@ __device__ __forceinline__ void bwd_rev_steps(std::integer_sequence<int, I...>, 
                                               float An, const float4 (&Bq)[4], const float4 (&Cq)[4],
                                               float& lam,
                                               float& anext, float& accA, float (&s1)[kRow], float (&s2)[kRow],
-                                              float (&rB)[kRow][kRow], float (&rC)[kRow][kRow], int j) {
-  (bwd_rev_step<kRow - 1 - I>(dp, du, delta, An, Bq, Cq, lam, anext, accA, s1, s2, rB, rC, j), ...);
+                                              float (&rB)[kRow][kRow], float (&rC)[kRow][kRow], int j, float h0) {
+  float hcur = rC[kRow - 1][j];  // the state after the block's last token
+  (bwd_rev_step<kRow - 1 - I>(dp, du, delta, An, Bq, Cq, lam, anext, accA, s1, s2, rB, rC, j, hcur, h0), ...);
 }
 
 // The reverse pass.  Workgroup (k, cb) takes channels 16 cb .. 16 cb + 15 of
@@ -332,7 +339,7 @@ __global__ void __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_e
       float(&rC)[kRow][kRow] = L.red[1][ch].v;
       __builtin_amdgcn_s_setprio(2);
       bwd_rev_steps(std::make_integer_sequence<int, kRow>{}, dp_r, du_r, delta_r, An, Br, Cr, lam, anext,
-                    accA, s1, s2, rB, rC, jz);
+                    accA, s1, s2, rB, rC, jz, h0);
       __builtin_amdgcn_sched_barrier(0);
       const float S1 = row_transpose_sum(s1, j);
       const float S2 = row_transpose_sum(s2, j);

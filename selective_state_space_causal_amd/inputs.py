@@ -15,7 +15,10 @@ Recipe (all draws from numpy's PCG64 via ``SeedSequence(seed, spawn_key=...)``):
   sub-stream per (tensor, row block).
 * Parameters, per channel: ``A_log[c, n] = ln(n + 1)`` (so A = -(n + 1)),
   ``D = 1``, ``dt_bias = softplus^-1(dt0)`` with ``dt0 = exp(U[ln 1e-3, ln 0.1])``,
-  ``conv_w[c, k], conv_b[c] ~ U(-0.5, 0.5)``.
+  ``conv_w[c, k], conv_b[c] ~ U(-0.5, 0.5)``.  This is the recipe of the measured
+  workloads.  ``params_per_channel`` draws parameters that differ in every channel
+  as a trained layer's do: ``A_log[c, n] = ln U[0.5, 16]`` independently per (c, n)
+  and ``D[c] ~ N(0, 1)``, the rest as above (parity tests only).
 * bf16 tensors are the float32 draws rounded to nearest-even bf16, stored as
   raw ``uint16`` bit patterns.
 * Packed variable lengths: integers uniform on [lo, hi] drawn until the running
@@ -34,6 +37,7 @@ COL_BLOCK = 64
 # sub-stream tags
 TAG_X, TAG_Z, TAG_DT, TAG_B, TAG_C, TAG_PARAMS, TAG_LENS = 1, 2, 3, 4, 5, 6, 7
 TAG_DY = 8
+TAG_PARAMS_VAR = 9
 TAG_STEP = 100  # decode step k uses tags TAG_STEP * (k + 1) + {TAG_X, ...}
 
 
@@ -119,6 +123,18 @@ def params(seed: int, d: int, N: int, K: int) -> dict[str, np.ndarray]:
     A_log = np.tile(np.log(np.arange(1, N + 1, dtype=np.float64)), (d, 1)).astype(np.float32)
     D = np.ones(d, dtype=np.float32)
     return dict(A_log=A_log, D=D, dt_bias=dt_bias, conv_w=conv_w, conv_b=conv_b)
+
+
+def params_per_channel(seed: int, d: int, N: int, K: int) -> dict[str, np.ndarray]:
+    """Parameters that vary in every channel (and A_log in every state entry): A_log[c, n] =
+    ln U[0.5, 16] drawn independently per (c, n), D[c] ~ N(0, 1); dt_bias, conv_w, conv_b as in
+    ``params``.  A kernel that took A_log or D of the wrong channel or state entry would not
+    match the oracle on these."""
+    p = params(seed, d, N, K)
+    rng = _rng(seed, TAG_PARAMS_VAR, d, N, K)
+    p["A_log"] = np.log(rng.uniform(0.5, 16.0, size=(d, N))).astype(np.float32)
+    p["D"] = rng.standard_normal(d).astype(np.float32)
+    return p
 
 
 def packed_lengths(seed: int, total: int, lo: int, hi: int) -> np.ndarray:

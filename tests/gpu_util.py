@@ -66,13 +66,14 @@ def assert_within(g, r, io, what):
     return msg
 
 
-def make_prefill(seed, lens, d, N, io, nonzero_state=True, extra_slots=0):
-    """Seeded inputs for a packed prefill (numpy).  Returns dict with cu, tokens, params, states."""
+def make_prefill(seed, lens, d, N, io, nonzero_state=True, extra_slots=0, varied=False):
+    """Seeded inputs for a packed prefill (numpy).  Returns dict with cu, tokens, params, states.
+    varied=True draws parameters that differ in every channel (inputs.params_per_channel)."""
     from selective_state_space_causal_amd import inputs
 
     T = int(np.sum(lens))
     tok = inputs.prefill_inputs(seed, T, d, N, io)
-    p = inputs.params(seed, d, N, 4)
+    p = (inputs.params_per_channel if varied else inputs.params)(seed, d, N, 4)
     S = len(lens)
     rng = np.random.default_rng(seed + 1000)
     if nonzero_state:

@@ -96,7 +96,8 @@ def test_m1p4b_packed_full_size():
 
 
 def test_m7b_decode_full_size():
-    """256 rows, d_inner 8192: states from a 512-token prefill, then 128 decode steps."""
+    """256 rows, d_inner 8192: states from a 512-token prefill, then 128 decode steps, y of every
+    step checked on the sampled channels."""
     Bs, L, d, N, steps = 256, 512, 8192, 16, 128
     T = Bs * L
     log(f"[workload] m7b init prefill T={T} d={d} chunk={mm.chunk_len(Bs, T, d, N)}")
@@ -121,8 +122,7 @@ def test_m7b_decode_full_size():
         ydr, cs_o, ss_o = oracle.decode(dt_["x"][:, ch], dt_["z"][:, ch], dt_["dt"][:, ch], dt_["B"], dt_["C"],
                                         p["A_log"][ch], p["D"][ch], p["dt_bias"][ch], p["conv_w"][ch],
                                         p["conv_b"][ch], cs_o, ss_o)
-        if s % 16 == 0 or s == steps - 1:
-            assert_within(_y_cols(yd, ch), ydr, "bf16", f"m7b decode step {s} y")
+        assert_within(_y_cols(yd, ch), ydr, "bf16", f"m7b decode step {s} y")
     assert_within(host(ssd)[:, ch], ss_o, "bf16", "m7b decode final ssm_state")
     assert np.array_equal(host(csd)[:, ch], cs_o)
 
