@@ -1,14 +1,20 @@
 """Benchmark of the selective-SSM mixer core on one MI355X.
 
-One step = one prefill call over the Mamba-130m-shaped layer workload (8 packed
-sequences of 2048 tokens, d_inner 1536, N 16, bf16 io, fp32 state): conv + SiLU,
-softplus, discretisation, the segmented selective scan, readout and gate, and the
-final-state write-back.  `value` is prefill tokens/s with all inputs resident in
-HBM.  The same JSON line also carries the batch-256 decode measurement (Falcon-
-Mamba-7B-shaped: d_inner 8192, N 16, state initialised by a 512-token prefill,
-then 128 single-token steps), the per-kernel times measured with HIP events on
-the launch stream, the roofline of the dominant kernel, and the fp64 CPU oracle
-timed on this host as a baseline.
+One step = one prefill call over the 1.4B-shaped packed workload (PackMamba-style packing:
+sequence lengths uniform on [128, 4096] drawn until 16384 tokens, d_inner 4096, N 16, bf16 io,
+fp32 state): conv + SiLU, softplus, discretisation, the segmented selective scan, readout and
+gate, and the final-state write-back.  `value` is prefill tokens/s with all inputs resident in
+HBM.  The same JSON line also carries:
+  * the 130m-shaped prefill (8 x 2048 tokens, d_inner 1536) and the 2.8B-shaped long prefill
+    (131072 tokens in 16 state-carrying calls of 8192, d_inner 5120), each with its own roofline;
+  * packed vs one call per sequence on the 1.4B-shaped stream (PackMamba's comparison, context);
+  * the batch-256 decode (Falcon-Mamba-7B-shaped: d_inner 8192, N 16, state initialised by a
+    512-token prefill, then 128 single-token steps) and its replay variant;
+  * the prefill backward and the dt/B/C projections;
+  * per-kernel times measured with HIP events on the launch stream inside the timed steps, the
+    roofline of each dominant kernel (algorithmic FLOP and bytes per launch over its time, HBM
+    traffic and VALU issue fraction from the committed rocprofv3 summaries under profiles/);
+  * the fp64 CPU oracle timed on this host as a baseline.
 
 Every timed measurement follows an untimed settle phase (--settle-ms, default 100 ms of
 back-to-back calls of the measured workload): under sustained load the GPU raises its clocks
@@ -34,11 +40,10 @@ if ROOT not in sys.path:
 
 METRIC = "prefill tokens/s + decode steps/s (B=256); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-# FP32 vector peak 157.3 TFLOP/s = 256 CUs x 2.4 GHz x 128 FMA lanes/clk x 2; one issue slot = one
-# plain fp32 op (an FMA counts 2 flops), a transcendental (exp2/log2/rcp) issues at a quarter of the
-# rate and counts 4 slots.
+# FP32 vector peak (AMD's published figure): 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 2.4 GHz x 64 FMA
+# lanes per clock x 2 FLOP; reaching it takes packed fp32 (two fp32 operations per lane and
+# instruction), which this build does not generate.  The rooflines count algorithmic FLOP against it.
 ALU_PEAK_TFLOPS = 157.3
-TRANS_SLOTS = 4
 
 
 def log(msg):
@@ -112,7 +117,6 @@ def kernel_source_sha256():
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
-PREFILL_PROFILE_SUFFIX = "__m130_prefill_8x2048_d1536_N16_bf16.txt"  # profiles/<final kernel><suffix>
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d8192_N16_bf16.txt")
 PROFILE_REPLAY = os.path.join(ROOT, "profiles", "k_decode_replay__m7b_decode_b256_d8192_N16_W4_bf16.txt")
 PROFILE_BACKWARD = os.path.join(ROOT, "profiles", "k_row_bwd__m130_backward_8x2048_d1536_N16_bf16.txt")
@@ -172,29 +176,29 @@ def replay_alg_bytes(Bs, d, N, K, s_io, W):
     return total / W
 
 
-def alu_slots_per_token_channel(N):
-    """Issue slots of the method's fp32 arithmetic per (token, channel), transcendentals weighted x4.
+def alg_flop_per_token_channel(N):
+    """Algorithmic FLOP of the method per (token, channel): an FMA counts 2, an add or multiply 1,
+    a transcendental (exp, log, reciprocal) 1.
 
-    conv 4 FMA; SiLU(xc) = xc / (1 + exp(-xc)): add, mul + exp, rcp; softplus = log(1 + exp(v)):
-    2 adds + exp, log; delta*u 1; per state index: delta*A, delta*u*B, the state FMA, the readout FMA
-    (4) + 1 exp; D*u 1; SiLU(z) 2 + exp, rcp; gating multiply 1.
+    conv: 4 FMA (8); SiLU(xc) = xc / (1 + e^-xc): add, multiply + exp, rcp (2 + 2); softplus(v) =
+    log(1 + e^v), v = dt + dt_bias: 2 adds + exp, log (2 + 2); delta * u (1); per state entry:
+    delta * A (1) + exp, (delta u) * B (1), the state FMA (2), the readout FMA (2) -- 6 + 1 each;
+    + D u (2); SiLU(z): add, multiply + exp, rcp (2 + 2); the gate multiply (1).
+    At N = 16: 114 + 22 = 136.
     """
-    plain = 4 + 2 + 2 + 1 + 4 * N + 1 + 2 + 1
+    plain = 8 + 2 + 2 + 1 + 6 * N + 2 + 2 + 1
     trans = 2 + 2 + N + 2
-    return plain + TRANS_SLOTS * trans, plain, trans
+    return plain + trans
 
 
-def alu_slots_backward(N):
-    """Issue slots of the backward's fp32 arithmetic per (token, channel): the forward's (its
-    per-token quantities and states are recomputed, not stored) plus the adjoint's.  Adjoint per
-    state index: the lambda update 2, the dC term 1, the dB term 1, the S1 term and sum 2, the S2
-    term lambda h a A and sum 4, the dA term 1 (11); per token: dp 1, dz 3, du 2, d(delta) 2,
-    d(dt) 1 + sigmoid (add + exp, rcp), d(xc) 4 + sigmoid (add + exp, rcp), dconv_w 4, dconv_b 1,
-    dx 4, dD 1, ddt_bias 1, dt + dt_bias and masks 3 (29 plain + 4 transcendentals)."""
-    f_slots, f_plain, f_trans = alu_slots_per_token_channel(N)
-    plain = f_plain + 11 * N + 29
-    trans = f_trans + 4
-    return plain + TRANS_SLOTS * trans, plain, trans
+def alg_flop_backward(N):
+    """Algorithmic FLOP of the backward per (token, channel), counted as alg_flop_per_token_channel:
+    the forward's (the states and per-token quantities are recomputed, not stored) plus the
+    adjoint's.  Per state entry: the lambda FMA (2), the dC and dB terms (2), the S1 term and its
+    sum (2), lambda a h_prev (2) times A and its sum (2), the dA FMA (2) -- 12 each.  Per token:
+    dp 1, dz 4, du 2, d(delta) 2, d(dt) = d(delta) sigmoid(v) 3 + 2 transcendentals, d(xc) 4 + 2
+    transcendentals, dconv_w 4 FMA (8), dconv_b 1, dx 4 FMA (8), dD FMA (2), ddt_bias 1 -- 36 + 4."""
+    return alg_flop_per_token_channel(N) + 12 * N + 36 + 4
 
 
 def make_prefill_set(seed, lens, d, N, io):
@@ -208,156 +212,251 @@ def make_prefill_set(seed, lens, d, N, io):
     return tok, p, cs, ss, cu
 
 
-def bench_prefill(args):
+def prefill_workloads():
+    """The prefill workloads: packed lengths and d_inner of each (N 16, conv 4, bf16 io, fp32 state).
+
+    m1p4b_packed -- the headline: PackMamba-style packing of sequences with lengths uniform on
+                    [128, 4096] until 16384 tokens, d_inner 4096 (1.4B-shaped layer); one call.
+    m130_prefill -- 8 sequences x 2048 tokens, d_inner 1536 (130m-shaped layer); one call.
+    m2p8b_long   -- one 131072-token sequence, d_inner 5120 (2.8B-shaped layer), in 16 calls of
+                    8192 tokens that carry the conv/SSM state from call to call (the state cache).
+    """
+    from selective_state_space_causal_amd import inputs
+
+    lens = [int(v) for v in inputs.packed_lengths(0, 16384, 128, 4096)]
+    return {
+        "m1p4b_packed": dict(lens=lens, d=4096, calls=1,
+                             workload=f"1.4B-shaped packed prefill: {len(lens)} sequences, lengths U[128,4096] to "
+                                      f"T=16384 ({lens}), d_inner 4096, d_state 16, conv 4, bf16 io, fp32 state"),
+        "m130_prefill": dict(lens=[2048] * 8, d=1536, calls=1,
+                             workload="mamba-130m-shaped layer prefill: 8 packed sequences x 2048 tokens, "
+                                      "d_inner 1536, d_state 16, conv 4, bf16 io, fp32 state"),
+        "m2p8b_long": dict(lens=[131072], d=5120, calls=16,
+                           workload="2.8B-shaped long prefill: 1 sequence of 131072 tokens in 16 calls of 8192 "
+                                    "tokens carrying the conv/SSM state, d_inner 5120, d_state 16, conv 4, bf16 io, "
+                                    "fp32 state"),
+    }
+
+
+def profile_path(kernel, name):
+    """profiles/<kernel>__<workload>.txt: the committed rocprofv3 summary of one kernel on one workload."""
+    tags = {"m1p4b_packed": "m1p4b_packed_T16384_d4096_N16_bf16", "m130_prefill": "m130_prefill_8x2048_d1536_N16_bf16",
+            "m2p8b_long": "m2p8b_long_16x8192_d5120_N16_bf16"}
+    return os.path.join(ROOT, "profiles", f"{kernel}__{tags[name]}.txt")
+
+
+def profile_field(path, field):
+    """A numeric field of a committed profile summary ("<field>: <value>"), or None when the summary
+    is missing or was taken on a different kernel source than the one built now."""
+    try:
+        text = open(path).read()
+        src = kernel_source_sha256()
+    except OSError:
+        return None
+    sha = val = None
+    for line in text.splitlines():
+        if line.startswith("kernel source sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        if line.startswith(field + ":"):
+            val = float(line.split(":", 1)[1].split()[0])
+    return val if sha == src else None
+
+
+def bench_prefill_workload(name, steps, warmup):
+    """Time `steps` steps of one prefill workload (a step = all its calls) on resident inputs.
+
+    Inputs, workspaces, plans and the HIP events are set up before anything is timed.  Calls-1
+    workloads alternate between two resident input sets (seeds 0 and 1), so that the 256 MB
+    Infinity Cache cannot hold a step's inputs.  The 16-call workload runs over the 131072 tokens
+    of one resident set; its state slots are not reset between steps (a step continues the state
+    of the step before: the same work on nonzero initial states).  After the warm-up steps an
+    untimed settle phase of back-to-back steps lets the clocks ramp.  The timed steps run back to
+    back, and the per-kernel times come from HIP events the library records on its launch stream
+    inside them (see below)."""
     import torch
 
     import selective_state_space_causal_amd as mm
 
-    S, L, d, N, K, io = 8, 2048, 1536, 16, 4, "bf16"
-    T = S * L
-    lens = [L] * S
-    names = mm.kernel_names(S, T, d, N, K)
+    wl = prefill_workloads()[name]
+    lens, d, calls = wl["lens"], wl["d"], wl["calls"]
+    N, K = 16, 4
+    T = int(sum(lens))
+    S = len(lens)
+    Tc, cl = (T // calls, [T // calls]) if calls > 1 else (T, lens)  # tokens and lengths of one call
+    Sc = len(cl)
+    plan = mm.plan(Sc, Tc, d, N, K)
+    names = plan["kernels"]
     nk = len(names)
-    # two resident input sets, used alternately, so the 256 MB Infinity Cache cannot hold a whole step
     sets = []
-    for seed in (0, 1):
-        tok, p, cs, ss, cu = make_prefill_set(seed, lens, d, N, io)
-        st = dict(x=dev(tok["x"]), z=dev(tok["z"]), dt=dev(tok["dt"]), B=dev(tok["B"]), C=dev(tok["C"]),
-                  A_log=dev(p["A_log"]), D=dev(p["D"]), dt_bias=dev(p["dt_bias"]), conv_w=dev(p["conv_w"]),
-                  conv_b=dev(p["conv_b"]), cu=dev(cu), cs=dev(cs), ss=dev(ss))
+    t0 = time.perf_counter()
+    for seed in ((0,) if calls > 1 else (0, 1)):
+        tok, p, cs, ss, cu = make_prefill_set(seed, lens, d, N, "bf16")
+        st = {k: dev(v) for k, v in tok.items()}
+        del tok
+        st.update({k: dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")})
+        st.update(cu=dev(inputs_cu(cl)), cs=dev(cs), ss=dev(ss))
         st["y"] = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
-        st["ws"] = torch.empty(mm.workspace_bytes(S, T, d, N), dtype=torch.uint8, device="cuda")
+        # at least 256 bytes: with a workspace given, the binding makes no plan query of its own
+        st["ws"] = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
         sets.append(st)
     torch.cuda.synchronize()
+    log(f"[bench] {name}: inputs resident ({time.perf_counter() - t0:.1f} s), plan {names}, "
+        f"chunk {plan['chunk_len']}, workspace {plan['workspace_bytes']} B")
+    views = []  # per call: the io slices of each set
+    for st in sets:
+        vs = []
+        for c in range(calls):
+            sl = slice(c * Tc, (c + 1) * Tc)
+            vs.append([st[k][sl] for k in ("x", "z", "dt", "B", "C")] + [st["y"][sl]])
+        views.append(vs)
 
-    def step(i, events=None):
-        st = sets[i % 2]
-        mm.prefill(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"], st["dt_bias"],
-                   st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], y=st["y"], workspace=st["ws"],
-                   events=events)
+    def step(i, ev=None):
+        st = sets[i % len(sets)]
+        for c, v in enumerate(views[i % len(sets)]):
+            e = None if ev is None else ev[c * (nk + 1):(c + 1) * (nk + 1)]
+            mm.prefill(*v[:5], st["A_log"], st["D"], st["dt_bias"], st["conv_w"], st["conv_b"], st["cu"], st["cs"],
+                       st["ss"], y=v[5], workspace=st["ws"], events=e)
 
-    ev = HipEvents(args.steps * (nk + 1))  # created before the timed steps: no idle time between them
-    for i in range(args.warmup):
+    # One kernel per step: one event before the first timed step's kernel and one after the last
+    # step's (the library records them on its launch stream), so the steps run unperturbed and the
+    # kernel's mean launch time is the span over the steps (launch gaps included).  Several kernels
+    # per call: an event before each kernel and after the last, in every timed call.
+    span = calls == 1 and nk == 1
+    per_step_ev = calls * (nk + 1)
+    hev = HipEvents(4 if span else steps * per_step_ev)
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     n_settle = settle(step)
-    # the timed steps, back to back, without instrumentation
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for i in range(steps):
+        if span:
+            first, last = i == 0, i == steps - 1
+            step(i, [hev.ev[0], hev.ev[1]] if first and last else
+                 ([hev.ev[0], hev.ev[2]] if first else ([hev.ev[3], hev.ev[1]] if last else None)))
+        else:
+            step(i, hev.ev[i * per_step_ev:(i + 1) * per_step_ev])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the same steps again with HIP events around each kernel, for the per-kernel times
-    for i in range(args.steps):
-        step(i, ev.ev[i * (nk + 1):(i + 1) * (nk + 1)])
-    torch.cuda.synchronize()
-    per_kernel = {n: [] for n in names}
-    for i in range(args.steps):
-        b = i * (nk + 1)
-        for k, n in enumerate(names):
-            per_kernel[n].append(ev.ms(b + k, b + k + 1))
-    ev.close()
-    kern_ms = {n: float(np.mean(v)) for n, v in per_kernel.items()}
-    plan = mm.plan(S, T, d, N, K)
-    return dict(S=S, L=L, T=T, d=d, N=N, K=K, wall_s=wall, kern_ms=kern_ms, names=names,
-                chunk_len=plan["chunk_len"], engine=plan["engine_name"], settle_steps=n_settle)
+    kern = {n: [] for n in names}
+    if span:
+        kern[names[0]].append(hev.ms(0, 1) / steps)
+    else:
+        for i in range(steps):
+            for c in range(calls):
+                b = i * per_step_ev + c * (nk + 1)
+                for k, n in enumerate(names):
+                    kern[n].append(hev.ms(b + k, b + k + 1))
+    hev.close()
+    del sets, views
+    torch.cuda.empty_cache()
+    return dict(name=name, workload=wl["workload"], S=S, T=T, d=d, N=N, K=K, calls=calls, call_T=Tc, call_S=Sc,
+                wall_s=wall, steps=steps, settle_steps=n_settle, names=names, chunk_len=plan["chunk_len"],
+                kernel_timing="span of the timed steps / steps" if span else "events around every kernel",
+                engine=plan["engine_name"], kern_ms={n: float(np.mean(v)) for n, v in kern.items()})
 
 
-def _time_prefill_call(mm, st, lens, d, N, reps, chunk_len=0, events=True):
-    """Mean event time (ms) of whole prefill calls on resident inputs (the library launches on torch's
-    current stream), states zeroed before each call; the first call is a warm-up."""
-    import torch
+def inputs_cu(lens):
+    from selective_state_space_causal_amd import inputs
 
-    times = []
-
-    def call(i):
-        mm.prefill(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"], st["dt_bias"],
-                   st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], y=st["y"], chunk_len=chunk_len)
-
-    settle(call)
-    for r in range(reps + 1):
-        st["cs"].zero_()
-        st["ss"].zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        mm.prefill(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"], st["dt_bias"],
-                   st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], y=st["y"], chunk_len=chunk_len)
-        e1.record()
-        torch.cuda.synchronize()
-        if r > 0:
-            times.append(e0.elapsed_time(e1))
-    return float(np.mean(times))
+    return inputs.cu_from_lengths(lens)
 
 
-def bench_other_prefills(args):
-    """Prefill rates of the other configurations (context; the headline is the 130m step):
-    the packed 1.4B-shaped stream, the same sequences one call each (PackMamba's comparison),
-    one 8192-token chunk of the 2.8B-shaped long sequence, and that sequence's 16 chunk calls."""
+def prefill_line(pf):
+    """Throughput, per-kernel times and the roofline of one timed prefill workload."""
+    T, d, N, K, calls = pf["T"], pf["d"], pf["N"], pf["K"], pf["calls"]
+    ms_per_step = pf["wall_s"] / pf["steps"] * 1e3
+    kern = pf["kern_ms"]
+    # the final pass runs every token of a call through the whole method: the dominant kernel
+    dom = pf["names"][-1]
+    dom_ms = kern[dom]
+    Tc, Sc = pf["call_T"], pf["call_S"]
+    flop = alg_flop_per_token_channel(N)
+    alg_flop = flop * Tc * d
+    alg_bytes = prefill_alg_bytes(Tc, Sc, d, N, K, 2)
+    tflops = alg_flop / (dom_ms * 1e-3) / 1e12
+    gbs = alg_bytes / (dom_ms * 1e-3) / 1e9
+    prof = profile_path(dom, pf["name"])
+    issue = profile_field(prof, "valu_issue_frac")
+    roof = dict(bound="alu", achieved=round(tflops, 2), peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(tflops / ALU_PEAK_TFLOPS, 4), traffic=_int_or_none(profile_field(prof, "traffic_bytes_per_launch")),
+                kernel=dom, kernel_ms=round(dom_ms, 4), alg_flop_per_launch=alg_flop,
+                per_unit=f"{flop} algorithmic FLOP per (token, channel) at N={N} (an FMA 2, an add or multiply 1, "
+                         f"a transcendental 1); {Tc} tokens x {d} channels per launch",
+                hbm_view=dict(alg_bytes_per_launch=alg_bytes, achieved_GBs=round(gbs, 1), peak_GBs=HBM_PEAK_GBS,
+                              frac=round(gbs / HBM_PEAK_GBS, 4)),
+                issue_view=dict(valu_issue_frac=issue,
+                                source=os.path.relpath(prof, ROOT),
+                                note="fraction of the SIMDs' VALU issue cycles the kernel kept busy, from the "
+                                     "committed rocprofv3 counters of this kernel (null when the summary is missing "
+                                     "or stale); without packed fp32 the 157.3 TFLOP/s peak is out of reach, so "
+                                     "this is the kernel's headroom against its own instruction stream"))
+    call_ms = sum(kern.values())
+    return dict(workload=pf["workload"], tokens_per_s=round(T * pf["steps"] / pf["wall_s"], 1),
+                ms_per_step=round(ms_per_step, 4), steps=pf["steps"], settle_steps=pf["settle_steps"],
+                kernel_timing=pf["kernel_timing"],
+                calls_per_step=calls, engine=pf["engine"], chunk_len=pf["chunk_len"],
+                kernels_ms={k: round(v, 4) for k, v in kern.items()},
+                kernels_ms_per_step=round(call_ms * calls, 4),
+                hbm_view_step=dict(alg_bytes_per_step=prefill_alg_bytes(Tc, Sc, d, N, K, 2) * calls,
+                                   achieved_GBs=round(prefill_alg_bytes(Tc, Sc, d, N, K, 2) * calls
+                                                      / (ms_per_step * 1e-3) / 1e9, 1)),
+                roofline=roof)
+
+
+def _int_or_none(v):
+    return None if v is None else int(v)
+
+
+def bench_packed_vs_separate():
+    """Context for PackMamba's comparison: the 1.4B-shaped packed stream in one call against one call
+    per sequence on the same resident inputs (each call timed with events after a settle phase;
+    workspaces preallocated)."""
     import torch
 
     import selective_state_space_causal_amd as mm
-    from selective_state_space_causal_amd import inputs
+
+    wl = prefill_workloads()["m1p4b_packed"]
+    lens, d, N = wl["lens"], wl["d"], 16
+    tok, p, cs, ss, cu = make_prefill_set(0, lens, d, N, "bf16")
+    st = {k: dev(v) for k, v in tok.items()}
+    prm = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    T = int(sum(lens))
+    y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(mm.workspace_bytes(len(lens), T, d, N), 256), dtype=torch.uint8, device="cuda")
+    css, sss = dev(cs), dev(ss)
+    calls = [([st[k] for k in ("x", "z", "dt", "B", "C")], dev(cu), css, sss, y)]
+    sep = []
+    off = 0
+    for L in lens:
+        sl = slice(off, off + L)
+        sep.append(([st[k][sl] for k in ("x", "z", "dt", "B", "C")], dev(np.array([0, L], np.int32)),
+                    css[:1].clone(), sss[:1].clone(), y[sl]))
+        off += L
+    wss = [torch.empty(max(mm.workspace_bytes(1, L, d, N), 256), dtype=torch.uint8, device="cuda") for L in lens]
+
+    def run(cs_, ws_):
+        for (io, cu_, c_, s_, y_), w in zip(cs_, ws_):
+            mm.prefill(*io, *prm, cu_, c_, s_, y=y_, workspace=w)
 
     out = {}
-
-    def resident(lens, d, N, seed=0):
-        tok, p, cs, ss, cu = make_prefill_set(seed, lens, d, N, "bf16")
-        st = {k: dev(v) for k, v in tok.items()}
-        st.update({k: dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")})
-        st.update(cu=dev(cu), cs=dev(cs), ss=dev(ss))
-        st["y"] = torch.empty((int(sum(lens)), d), dtype=torch.bfloat16, device="cuda")
-        return st
-
-    # 1.4B-shaped packed stream, and the same sequences one call each
-    lens = inputs.packed_lengths(0, 16384, 128, 4096).tolist()
-    d = 4096
-    st = resident(lens, d, 16)
-    T = int(sum(lens))
-    ms = _time_prefill_call(mm, st, lens, d, 16, reps=5)
-    plan = mm.plan(len(lens), T, d, 16)
-    sep_ms = 0.0
-    off = 0
-    for L in lens:  # one call per sequence, each on its own slice of the same inputs
-        sub = dict(st)
-        for k in ("x", "z", "dt", "B", "C", "y"):
-            sub[k] = st[k][off:off + L]
-        sub["cu"] = torch.tensor([0, L], dtype=torch.int32, device="cuda")
-        sub["cs"], sub["ss"] = st["cs"][:1].clone(), st["ss"][:1].clone()
-        sep_ms += _time_prefill_call(mm, sub, [L], d, 16, reps=3)
-        off += L
-    out["m1p4b_packed"] = dict(
-        workload=f"1.4B-shaped packed prefill: {len(lens)} sequences, lengths U[128,4096] to T={T}, d_inner {d}",
-        tokens_per_s=round(T / (ms * 1e-3), 1), ms=round(ms, 4), engine=plan["engine_name"],
-        chunk_len=plan["chunk_len"], kernels=plan["kernels"],
-        separate_calls_ms=round(sep_ms, 4), packed_speedup_over_separate=round(sep_ms / ms, 3))
-    del st
-    # 2.8B-shaped long sequence: 16 chunk calls of 8192 tokens carrying the state (for timing,
-    # every call takes the same 8192 resident input tokens; the parity tests use distinct ones)
-    d, L, nch = 5120, 8192, 16
-    st = resident([L], d, 16)
-    plan = mm.plan(1, L, d, 16)
-    times = []
-    st["cs"].zero_()
-    st["ss"].zero_()
-    for k in range(nch + 1):
+    for key, cs_, ws_ in (("packed", calls, [ws]), ("separate", sep, wss)):
+        settle(lambda i: run(cs_, ws_))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        mm.prefill(st["x"], st["z"], st["dt"], st["B"], st["C"], st["A_log"], st["D"], st["dt_bias"],
-                   st["conv_w"], st["conv_b"], st["cu"], st["cs"], st["ss"], y=st["y"])
-        e1.record()
-        torch.cuda.synchronize()
-        if k > 0:  # the first call is a warm-up
+        times = []
+        for _ in range(5):
+            e0.record()
+            run(cs_, ws_)
+            e1.record()
+            torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
-    tot = float(np.sum(times))
-    out["m2p8b_long_chunked"] = dict(
-        workload=f"2.8B-shaped long prefill: 1 sequence of {L * nch} tokens in {nch} calls of {L}, d_inner {d}, "
-                 "state carried between calls",
-        tokens_per_s=round(L * nch / (tot * 1e-3), 1), ms_total=round(tot, 3),
-        ms_per_chunk_call=round(tot / nch, 4), engine=plan["engine_name"], chunk_len=plan["chunk_len"],
-        kernels=plan["kernels"])
-    del st
+        out[key] = float(np.mean(times))
+    del st, y, ws, wss, calls, sep
     torch.cuda.empty_cache()
-    return out
+    return dict(what="the 1.4B-shaped packed stream in one call vs one call per sequence (PackMamba's comparison; "
+                     "context only)", packed_ms=round(out["packed"], 4), separate_ms=round(out["separate"], 4),
+                packed_speedup=round(out["separate"] / out["packed"], 3))
 
 
 def _time_calls(fn, n_kernels, names, reps=10):
@@ -433,9 +532,9 @@ def bench_backward(args):
     del st, bws, fws, out, ck, y
     torch.cuda.empty_cache()
     step_ms = ms_f + ms_bc
-    slots, plain, trans = alu_slots_backward(N)
+    flop = alg_flop_backward(N)
     kb = k_bc["k_row_bwd"]
-    ach = T * d * slots * 2 / (kb * 1e-3) / 1e12
+    ach = T * d * flop / (kb * 1e-3) / 1e12
     return dict(
         workload=f"mamba-130m-shaped layer backward: {S} packed sequences x {L} tokens, d_inner {d}, d_state {N}, "
                  "conv 4, bf16 io, fp32 state; gradients of all inputs, parameters and initial states",
@@ -452,9 +551,11 @@ def bench_backward(args):
         roofline=dict(bound="alu", achieved=round(ach, 2), peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(ach / ALU_PEAK_TFLOPS, 4), traffic=counted_traffic(PROFILE_BACKWARD),
                       kernel="k_row_bwd", kernel_ms=round(kb, 4),
-                      per_unit=f"{slots} issue slots per (token, channel) = {plain} plain fp32 ops + {trans} "
-                               f"transcendentals x {TRANS_SLOTS} (the forward's, recomputed, and the adjoint's); "
-                               "FLOP = 2 x slots", note="the reverse kernel of the training step's backward"),
+                      per_unit=f"{flop} algorithmic FLOP per (token, channel) (the forward's, recomputed, and the "
+                               "adjoint's; an FMA 2, an add or multiply 1, a transcendental 1)",
+                      issue_view=dict(valu_issue_frac=profile_field(PROFILE_BACKWARD, "valu_issue_frac"),
+                                      source=os.path.relpath(PROFILE_BACKWARD, ROOT)),
+                      note="the reverse kernel of the training step's backward"),
         io_bytes=io_bytes, io_GBs_standalone=round(io_bytes / (ms_b * 1e-3) / 1e9, 1))
 
 
@@ -676,8 +777,9 @@ def bench_decode(args):
 
 
 def cpu_baseline(lens, d, N, io):
-    """The fp64 oracle on this host's cores: full prefills of the bench workload (all tokens, all
-    channels), repeated until about 12 s of CPU time have been spent (at most 8 runs)."""
+    """The fp64 oracle on this host's cores: full prefills of the headline workload (all tokens, all
+    channels), repeated until about 12 s of CPU time have been spent (at most 8 runs), and one
+    thread on its first sequence."""
     import oracle
 
     oracle.build(force=False)
@@ -712,8 +814,9 @@ def cpu_baseline(lens, d, N, io):
     except OSError:
         pass
     return dict(value=round(runs * T / el, 1), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{runs} full prefills of the bench workload ({len(lens)} x {lens[0]} tokens, d={d}, N={N}), "
-                       f"fp64, {el:.2f} s wall, {cpu:.1f} s CPU on {threads} threads (input widening to fp64 included)",
+                sample=f"{runs} full prefills of the headline workload ({len(lens)} packed sequences, T={T}, d={d}, "
+                       f"N={N}), fp64, {el:.2f} s wall, {cpu:.1f} s CPU on {threads} threads (input widening to "
+                       "fp64 included)",
                 single_thread=dict(value=round(L0 / el1, 1), unit="tokens/s",
                                    sample=f"one sequence of {L0} tokens, d={d}, N={N}, {el1:.2f} s"),
                 cpu_model=model)
@@ -759,24 +862,27 @@ def summarize_rocprof(path):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="untimed back-to-back calls before each timed measurement (the clocks' ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="decode measurement only (for profiling)")
     ap.add_argument("--no-other-prefills", action="store_true",
-                    help="skip the context prefill rates of the other configurations")
+                    help="skip the other prefill workloads (130m-shaped, 2.8B-shaped long) and packed vs separate")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward timing")
     ap.add_argument("--no-project", action="store_true", help="skip the projection timing")
+    ap.add_argument("--only-prefill", metavar="WORKLOAD",
+                    help="only this prefill workload (m1p4b_packed, m130_prefill, m2p8b_long): the kernel-trace "
+                         "and counter runs of its profile")
     ap.add_argument("--only-project", action="store_true",
                     help="only the projection timing at the 130m shape (the kernel-trace and counter runs of its "
                          "profile)")
     ap.add_argument("--only-backward", action="store_true",
                     help="only the backward timing (the kernel-trace and counter runs of its profile)")
+    ap.add_argument("--only-decode", action="store_true", help="only the decode measurements")
     ap.add_argument("--decode-flushed-only", action="store_true",
-                    help="with --no-prefill: only the flushed-cache eager and replay decode dispatches "
+                    help="with --only-decode: only the flushed-cache eager and replay decode dispatches "
                          "(the kernel-trace and counter runs of the profiles)")
     ap.add_argument("--summarize-rocprof", metavar="CSV",
                     help="print a per-kernel table of a rocprofv3 kernel_stats.csv or counter_collection.csv "
@@ -790,9 +896,6 @@ def main():
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
         return
-    if args.copy_calibration:
-        copy_calibration()
-        return
     if args.source_sha:
         print(kernel_source_sha256())
         return
@@ -801,6 +904,9 @@ def main():
               "(the mixer core shards by channel or sequence with no communication; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -809,66 +915,48 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     mm.load()
     log(f"[bench] {mm.version()} on {torch.cuda.get_device_name(0)}")
+    diag = dict(metric=METRIC, note="diagnostic run (profiling); no headline value")
+    if args.only_prefill:
+        pf = bench_prefill_workload(args.only_prefill, args.steps, args.warmup)
+        print(json.dumps(dict(diag, prefill={args.only_prefill: prefill_line(pf)})), flush=True)
+        return
     if args.only_project:
-        print(json.dumps(dict(metric=METRIC, note="projection-only diagnostic run (--only-project); no headline value",
-                              project=bench_project(args, only_m130=True))), flush=True)
+        print(json.dumps(dict(diag, project=bench_project(args, only_m130=True))), flush=True)
         return
     if args.only_backward:
-        print(json.dumps(dict(metric=METRIC, note="backward-only diagnostic run (--only-backward); no headline value",
-                              backward=bench_backward(args))), flush=True)
+        print(json.dumps(dict(diag, backward=bench_backward(args))), flush=True)
+        return
+    if args.only_decode:
+        out = decode_result(args) if not args.decode_flushed_only else bench_decode(args)
+        print(json.dumps(dict(diag, decode=out)), flush=True)
         return
 
-    if args.no_prefill:
-        args.no_cpu_baseline = True
-        out = dict(metric=METRIC, note="decode-only diagnostic run (--no-prefill); no headline value")
-    else:
-        out = prefill_result(args)
-    if not args.no_prefill and not args.no_other_prefills:
-        out["other_prefills"] = bench_other_prefills(args)
-    if not args.no_prefill and not args.no_backward:
+    head = prefill_line(bench_prefill_workload("m1p4b_packed", args.steps, args.warmup))
+    out = dict(metric=METRIC, value=head["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup,
+               settle=dict(ms=args.settle_ms, steps=head["settle_steps"],
+                           note="untimed back-to-back steps after the warmup, before the timed ones (the GPU's "
+                                "clocks ramp over ~20 ms of load)"),
+               ms_per_step=head["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="f32", io_dtype="bf16", data="synthetic",
+               config=dict(workload=head["workload"], T=16384, S=len(prefill_workloads()["m1p4b_packed"]["lens"]),
+                           d_inner=4096, d_state=16, d_conv=4, chunk_len=head["chunk_len"], engine=head["engine"]),
+               roofline=head["roofline"], kernels_ms=head["kernels_ms"],
+               dtype_note="the path computes in fp32 (fp32 state); x, z, dt, B, C and y are bf16 in HBM")
+    if not args.no_other_prefills:
+        out["other_prefills"] = {n: prefill_line(bench_prefill_workload(n, args.steps, args.warmup))
+                                 for n in ("m130_prefill", "m2p8b_long")}
+        out["packed_vs_separate"] = bench_packed_vs_separate()
+    if not args.no_backward:
         out["backward"] = bench_backward(args)
-    if not args.no_prefill and not args.no_project:
+    if not args.no_project:
         out["project"] = bench_project(args)
     if not args.no_decode:
-        out["decode"] = decode_result(args) if not args.decode_flushed_only else bench_decode(args)
+        out["decode"] = decode_result(args)
     if not args.no_cpu_baseline:
-        c = out["config"]
-        out["cpu_baseline"] = cpu_baseline([c["L"]] * c["S"], c["d_inner"], c["d_state"], "bf16")
+        wl = prefill_workloads()["m1p4b_packed"]
+        out["cpu_baseline"] = cpu_baseline(wl["lens"], wl["d"], 16, "bf16")
     print(json.dumps(out), flush=True)
-
-
-def prefill_result(args):
-    pf = bench_prefill(args)
-    T, d, N, K = pf["T"], pf["d"], pf["N"], pf["K"]
-    ms_per_step = pf["wall_s"] / args.steps * 1e3
-    tokens_per_s = T * args.steps / pf["wall_s"]
-    step_bytes = prefill_alg_bytes(T, pf["S"], d, N, K, 2)
-    dom = pf["names"][-1]  # the final pass: the dominant kernel
-    dom_ms = pf["kern_ms"][dom]
-    slots, plain, trans = alu_slots_per_token_channel(N)
-    achieved_tflops = T * d * slots * 2 / (dom_ms * 1e-3) / 1e12
-    roofline = dict(bound="alu", achieved=round(achieved_tflops, 2), peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved_tflops / ALU_PEAK_TFLOPS, 4), traffic=counted_traffic(os.path.join(ROOT, "profiles", dom + PREFILL_PROFILE_SUFFIX)),
-                    kernel=dom, kernel_ms=round(dom_ms, 4),
-                    per_unit=f"{slots} issue slots per (token, channel) = {plain} plain fp32 ops + "
-                             f"{trans} transcendentals x {TRANS_SLOTS}; FLOP = 2 x slots")
-    out = dict(metric=METRIC, value=round(tokens_per_s, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
-               warmup=args.warmup, settle=dict(ms=args.settle_ms, steps=pf["settle_steps"],
-                                               note="untimed back-to-back steps after the warmup, before the "
-                                                    "timed ones (the GPU's clocks ramp over ~20 ms of load)"),
-               ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak",
-               vs_baseline=None, dtype="f32", io_dtype="bf16", data="synthetic",
-               config=dict(workload="mamba-130m-shaped layer prefill: 8 packed sequences x 2048 tokens, "
-                                    "d_inner 1536, d_state 16, conv 4, bf16 io, fp32 state",
-                           S=pf["S"], L=pf["L"], T=T, d_inner=d, d_state=N, d_conv=K,
-                           chunk_len=pf["chunk_len"], engine=pf["engine"]),
-               roofline=roofline,
-               kernels_ms={k: round(v, 4) for k, v in pf["kern_ms"].items()},
-               hbm_view=dict(alg_bytes_per_step=step_bytes,
-                             achieved_GBs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-                             peak_GBs=HBM_PEAK_GBS,
-                             frac=round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)))
-    return out
 
 
 def replay_result(dc):
