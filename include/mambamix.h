@@ -35,9 +35,11 @@
  *    (bfloat16 bit patterns, 2 bytes) elements; parameters and states are
  *    always float32.  bf16 outputs are rounded to nearest even.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
- *    null stream).  The library allocates no memory, keeps no pointer and no
- *    global mutable state; calls on different streams may run concurrently
- *    provided their output buffers do not overlap.
+ *    null stream).  The library allocates no memory and keeps no caller
+ *    pointer; its one piece of global state is the per-device address of the
+ *    fixed scratch behind mamba_mixer_prefill_noalloc.  Calls on different
+ *    streams may run concurrently provided their output buffers (and, for
+ *    mamba_mixer_prefill_noalloc, their device) do not overlap.
  *  - The caller owns every buffer.  The states are read as the initial state
  *    and overwritten in place with the final state.
  *  - Return value: MM_OK (0) or a negative MM_ERR_* code.  Argument errors are
@@ -105,6 +107,30 @@ int mamba_mixer_prefill(const void* x, const void* z, const void* dt, const void
 
 /* Workspace bytes mamba_mixer_prefill needs for these sizes (0 is possible).  Host only. */
 size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K);
+
+/*
+ * mamba_mixer_prefill_noalloc -- mamba_mixer_prefill for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid it): the same
+ * computation, plan and kernels, with no workspace argument.  The carries of a chunked plan go
+ * to a fixed scratch array in the library's device code, MM_NOALLOC_SCRATCH_BYTES per GPU, which
+ * each GPU the library runs on holds until the process ends.  The call allocates and frees
+ * nothing.
+ *   Arguments, layouts and results: those of mamba_mixer_prefill.
+ *   A plan whose workspace (mamba_mixer_prefill_workspace_bytes) exceeds
+ *   MM_NOALLOC_SCRATCH_BYTES is MM_ERR_WORKSPACE, returned before anything is enqueued.
+ *   The scratch is found for the current device (hipGetDevice) on the first call that needs it
+ *   there; `stream` must belong to that device.  MM_ERR_HIP if it cannot be resolved.
+ *   Every call on one GPU uses the same scratch, and nothing in it needs to start at any value:
+ *   calls that may overlap on one GPU (concurrent streams, or threads) race on it and must be
+ *   serialised by the caller; calls ordered on one stream are safe.
+ */
+#define MM_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mamba_mixer_prefill_noalloc(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                const float* A_log, const float* D, const float* dt_bias,
+                                const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                                float* conv_state, float* ssm_state, void* y,
+                                int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                                void* stream);
 
 /* Prefill engines (see mamba_mixer_prefill_ex). */
 #define MM_ENGINE_AUTO 0  /* the library picks from S, T and d                                        */

@@ -45,6 +45,8 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_prefill.restype = ctypes.c_int
     lib.mamba_mixer_prefill_chunked.argtypes = [P] * 14 + [i32, i64, i32, i32, i32, i32, i64, P, sz, P]
     lib.mamba_mixer_prefill_chunked.restype = ctypes.c_int
+    lib.mamba_mixer_prefill_noalloc.argtypes = [P] * 14 + [i32, i64, i32, i32, i32, i32, P]
+    lib.mamba_mixer_prefill_noalloc.restype = ctypes.c_int
     lib.mamba_mixer_prefill_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
     lib.mamba_mixer_prefill_workspace_bytes.restype = sz
     lib.mamba_mixer_prefill_workspace_bytes_chunked.argtypes = [i32, i64, i32, i32, i32, i64]
@@ -199,6 +201,44 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
         S, T, d, N, CONV_K, _io_code(x), int(chunk_len), int(engine), wptr, wbytes, _stream(stream), ev, nev)
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_prefill")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MM_NOALLOC_SCRATCH_BYTES
+
+
+def prefill_noalloc(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, y=None,
+                    stream=None):
+    """``prefill`` through mamba_mixer_prefill_noalloc: the automatic plan with its workspace in the
+    library's fixed per-GPU scratch (at most NOALLOC_SCRATCH_BYTES), so the call allocates no
+    workspace; y is allocated here only when not given.  Calls that overlap on one GPU race on the
+    scratch."""
+    import torch
+
+    T, d = x.shape
+    N = B.shape[1]
+    S = cu_seqlens.shape[0] - 1
+    io = x.dtype
+    for t, n in ((x, "x"), (z, "z"), (dt, "dt")):
+        _check(t, (T, d), io, n)
+    for t, n in ((B, "B"), (C, "C")):
+        _check(t, (T, N), io, n)
+    _check(A_log, (d, N), torch.float32, "A_log")
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (conv_b, "conv_b")):
+        _check(t, (d,), torch.float32, n)
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
+    if y is None:
+        y = torch.empty((T, d), dtype=io, device=x.device)
+    _check(y, (T, d), io, "y")
+    rc = load().mamba_mixer_prefill_noalloc(
+        _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(conv_w),
+        _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(ssm_state), _ptr(y),
+        S, T, d, N, CONV_K, _io_code(x), _stream(stream))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_prefill_noalloc")
     return y
 
 

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include <stdint.h>
 #include <string.h>
@@ -514,6 +515,34 @@ int check_proj_sizes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t R, int3
   return MM_OK;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+
+// The workspace of mamba_mixer_prefill_noalloc: a file-scope device array that every GPU the
+// library runs on holds from the loading of the library's code until the process ends.  Host
+// code never passes the array's name to a kernel or a copy (on the host it names a stand-in,
+// not device memory): it passes the device address hipGetSymbolAddress returns, looked up once
+// per device with that device current and kept per device.
+static __device__ __align__(256) unsigned char scratch[MM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (MM_OK), or MM_ERR_HIP when the device or the
+// symbol cannot be resolved.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MM_OK;
+}
+
 }  // namespace
 }  // namespace mm
 
@@ -576,12 +605,15 @@ size_t mamba_mixer_prefill_workspace_bytes(int32_t S, int64_t T, int32_t d, int3
 
 // The prefill call; with ckpt != NULL (row engine only) the final pass also stores the
 // state before every 16-token block.
+// use_scratch: the workspace is the library's fixed device scratch (mamba_mixer_prefill_noalloc);
+// a plan that needs more than it holds is MM_ERR_WORKSPACE, found before anything is enqueued.
 static int prefill_call(const void* x, const void* z, const void* dt, const void* B, const void* C,
                         const float* A_log, const float* D, const float* dt_bias, const float* conv_w,
                         const float* conv_b, const int32_t* cu_seqlens, float* conv_state, float* ssm_state,
                         void* y, float* ckpt, int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
                         int32_t io_dtype, int64_t chunk_len, int32_t engine, void* workspace,
-                        size_t workspace_bytes, void* stream, void* const* events, int32_t n_events) {
+                        size_t workspace_bytes, void* stream, void* const* events, int32_t n_events,
+                        bool use_scratch = false) {
   int rc = check_prefill_sizes(S, T, d, N, K, io_dtype);
   if (rc != MM_OK) return rc;
   if (T == 0 || d == 0 || S == 0) return MM_OK;
@@ -613,6 +645,16 @@ static int prefill_call(const void* x, const void* z, const void* dt, const void
   Plan p{};
   rc = make_plan(p, S, T, d, N, chunk_len, engine);
   if (rc != MM_OK) return rc;
+  if (use_scratch) {
+    if (p.total > MM_NOALLOC_SCRATCH_BYTES) return MM_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (p.total > 0) {
+      rc = scratch_address(&workspace);
+      if (rc != MM_OK) return rc;
+      workspace_bytes = MM_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (p.total > 0 && (workspace == nullptr || workspace_bytes < p.total)) return MM_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MM_ERR_ALIGN;
   if (events != nullptr && n_events < p.kernels + 1) return MM_ERR_DIM;
@@ -684,6 +726,16 @@ int mamba_mixer_prefill(const void* x, const void* z, const void* dt, const void
                         void* workspace, size_t workspace_bytes, void* stream) {
   return mamba_mixer_prefill_chunked(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state,
                                      ssm_state, y, S, T, d, N, K, io_dtype, 0, workspace, workspace_bytes, stream);
+}
+
+int mamba_mixer_prefill_noalloc(const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                const float* A_log, const float* D, const float* dt_bias,
+                                const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
+                                float* conv_state, float* ssm_state, void* y,
+                                int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int32_t io_dtype,
+                                void* stream) {
+  return prefill_call(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_state, ssm_state, y,
+                      nullptr, S, T, d, N, K, io_dtype, 0, MM_ENGINE_AUTO, nullptr, 0, stream, nullptr, 0, true);
 }
 
 int mamba_mixer_decode(const void* x, const void* z, const void* dt, const void* B, const void* C,

@@ -339,3 +339,20 @@ def test_row_engine_channel_limit(lib):
         mm.backward_plan(1, 64, big, 16)
     assert e.value.code == MM_ERR_UNSUPPORTED
     assert lib.mamba_mixer_prefill_backward_workspace_bytes(1, 64, big, 16, 4, 0) == 0
+
+
+def test_noalloc_prefill_rejects_plans_beyond_its_scratch(lib):
+    """A plan whose workspace exceeds the fixed scratch (here 65.6 MB of lane-engine carries and
+    packed B/C) is MM_ERR_WORKSPACE, found on the host before any device call; argument errors
+    come first."""
+    S, T, d, N = 8192, 327680, 256, 16
+    need = mm.workspace_bytes(S, T, d, N)
+    assert need > mm.NOALLOC_SCRATCH_BYTES
+    big = 0x100000000  # fake device addresses 4 GiB apart: no two arrays overlap
+    ptrs = [ctypes.c_void_p(0x1000000000 + i * big) for i in range(14)]
+    assert lib.mamba_mixer_prefill_noalloc(*ptrs, S, T, d, N, 4, 1, None) == MM_ERR_WORKSPACE
+    ptrs[3] = None
+    assert lib.mamba_mixer_prefill_noalloc(*ptrs, S, T, d, N, 4, 1, None) == MM_ERR_NULL
+    assert lib.mamba_mixer_prefill_noalloc(*ptrs, S, T, d, 17, 4, 1, None) == MM_ERR_UNSUPPORTED
+    # nothing to do: success without touching a device
+    assert lib.mamba_mixer_prefill_noalloc(*ptrs, S, 0, d, N, 4, 1, None) == 0
