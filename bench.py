@@ -320,10 +320,13 @@ def bench_prefill_workload(name, steps, warmup):
     # One kernel per step: one event before the first timed step's kernel and one after the last
     # step's (the library records them on its launch stream), so the steps run unperturbed and the
     # kernel's mean launch time is the span over the steps (launch gaps included).  Several kernels
-    # per call: an event before each kernel and after the last, in every timed call.
+    # per call: an event before each kernel and after the last, in every call of the first and the
+    # last timed step (events between kernels cost several microseconds each, so the steps between
+    # run uninstrumented).
     span = calls == 1 and nk == 1
     per_step_ev = calls * (nk + 1)
-    hev = HipEvents(4 if span else steps * per_step_ev)
+    inst = sorted({0, steps - 1})  # the instrumented steps
+    hev = HipEvents(4 if span else len(inst) * per_step_ev)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -336,16 +339,16 @@ def bench_prefill_workload(name, steps, warmup):
             step(i, [hev.ev[0], hev.ev[1]] if first and last else
                  ([hev.ev[0], hev.ev[2]] if first else ([hev.ev[3], hev.ev[1]] if last else None)))
         else:
-            step(i, hev.ev[i * per_step_ev:(i + 1) * per_step_ev])
+            step(i, hev.ev[inst.index(i) * per_step_ev:(inst.index(i) + 1) * per_step_ev] if i in inst else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern = {n: [] for n in names}
     if span:
         kern[names[0]].append(hev.ms(0, 1) / steps)
     else:
-        for i in range(steps):
+        for q in range(len(inst)):
             for c in range(calls):
-                b = i * per_step_ev + c * (nk + 1)
+                b = q * per_step_ev + c * (nk + 1)
                 for k, n in enumerate(names):
                     kern[n].append(hev.ms(b + k, b + k + 1))
     hev.close()
@@ -353,7 +356,8 @@ def bench_prefill_workload(name, steps, warmup):
     torch.cuda.empty_cache()
     return dict(name=name, workload=wl["workload"], S=S, T=T, d=d, N=N, K=K, calls=calls, call_T=Tc, call_S=Sc,
                 wall_s=wall, steps=steps, settle_steps=n_settle, names=names, chunk_len=plan["chunk_len"],
-                kernel_timing="span of the timed steps / steps" if span else "events around every kernel",
+                kernel_timing="span of the timed steps / steps" if span else
+                "events around every kernel of the first and the last timed step",
                 engine=plan["engine_name"], kern_ms={n: float(np.mean(v)) for n, v in kern.items()})
 
 

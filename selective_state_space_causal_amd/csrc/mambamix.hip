@@ -15,6 +15,7 @@
 // mm_prefill.h, the decode kernels in mm_decode.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <initializer_list>
 #include <mutex>
 
@@ -56,31 +57,49 @@ struct Plan {
   int nmax;
   int64_t Lc;    // chunk length
   int64_t Pmax;  // chunk grid bound: ceil(T / Lc) + S
-  int64_t Mmax;  // carry-slot bound: floor(T / Lc) (every non-last chunk holds Lc tokens)
+  int64_t Mmax;  // non-last-chunk bound: floor(T / Lc) (every non-last chunk holds Lc tokens)
+  int ksub;      // row engine: pass 1 scans a non-last chunk as ksub pieces (carry slots: Mmax * ksub)
+  bool inl;      // row engine: the kernels compute the chunk plan themselves (S <= kPlanInline)
   int64_t Tpad;  // B/C rows incl. zero padding past T
   size_t off_off, off_moff, off_bc, off_a, off_b, off_stash, total;
   int kernels;   // kernels one call enqueues
   bool whole;    // row engine with one chunk per sequence: no plan, no carries
 };
 
-// Modelled time (microseconds) of the row engine with P chunks per (average)
-// sequence, fitted to measurements on MI355X.  A pass is as slow as its busiest
-// CU: with g = workgroups / 256, some CU runs ceil(g) workgroups of W / wgs
-// (token, channel) pairs each, at a per-CU rate of ~575 M pairs/s with >= 4
-// workgroups (16 waves) on the CU, ~500 M/s with 2-3 and less with 1.  Pass 1
-// runs ~1.33x faster (no readout); chunking adds the plan and carry kernels
-// (~13 us).
-double row_pass_us(double W, double wgs, double speed) {
+// Pieces per non-last chunk in the row engine's pass 1: the smallest power of two that gives
+// the pass about 8 workgroups per CU (it only has the non-last chunks to work on), keeping
+// pieces at >= 128 tokens.  Chunk lengths are rounded to multiples of 16 * ksub.
+int row_pieces(int64_t Lc, double nonlast_chunks, int64_t nchb) {
+  int k = 1;
+  while (k < 16 && nonlast_chunks * k * nchb < 8.0 * kCUs && Lc / (2 * k) >= 128) k *= 2;
+  return k;
+}
+
+// Modelled time (microseconds) of the row engine with P chunks per (average) sequence,
+// fitted to measurements on MI355X.  A pass is as slow as its busiest CU: with
+// g = workgroups / 256, some CU runs ceil(g) workgroups, each taking (its W / wgs
+// (token, channel) pairs) / rate + a fixed cost per workgroup.  Final pass: ~996 pairs per
+// us per CU with >= 3 workgroups on the CU, x 0.82 with 2, less with 1, plus 7.8 us per
+// workgroup (staging fill and drain, carry fold, final states).  Pass 1: 1.54x the rate,
+// 1.5 us per workgroup.  Fitted to: the 130m-shaped call (3 per CU, 0.117 ms), and one
+// 8192-token call at d_inner 5120 in whole-sequence mode (0.338 ms), in two chunks (pass 1
+// in 8 pieces: 0.070 + 0.221 ms) and in four (pass 1 in 4 pieces: 0.100 + 0.204 ms).
+// Chunking adds the plan (inside the kernels for S <= kPlanInline) and a launch (~3 us).
+double row_pass_us(double W, double wgs, double speed, double per_wg) {
   if (wgs <= 0) return 0.0;
   const double g = std::ceil(wgs / kCUs);
-  const double rate = 575.0 * (g >= 4 ? 1.0 : (g >= 2 ? 0.88 : 0.6)) * speed;  // pairs per us per CU
-  return g * (W / wgs) / rate;
+  const double rate = 996.0 * (g >= 3 ? 1.0 : (g >= 2 ? 0.82 : 0.55)) * speed;  // pairs per us per CU
+  return g * ((W / wgs) / rate + per_wg);
 }
 double row_cost(int64_t S, int64_t T, int d, int64_t P) {
   const double W = static_cast<double>(T) * d;
-  const double wgs = static_cast<double>(S) * cdiv(d, kRowChans);
-  double t = row_pass_us(W, wgs * P, 1.0);
-  if (P > 1) t += row_pass_us(W * (P - 1) / P, wgs * (P - 1), 1.33) + 13.0;
+  const int64_t nchb = cdiv(d, kRowChans);
+  const double wgs = static_cast<double>(S) * nchb;
+  double t = row_pass_us(W, wgs * P, 1.0, 7.8);
+  if (P > 1) {
+    const int k = row_pieces(cdiv(cdiv(T, S), P), static_cast<double>(S) * (P - 1), nchb);
+    t += row_pass_us(W * (P - 1) / P, wgs * (P - 1) * k, 1.54, 1.5) + (S <= kPlanInline ? 3.0 : 8.0);
+  }
   return t;
 }
 
@@ -117,6 +136,15 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   }
   if (p.Lc < 16) p.Lc = 16;  // >= 3 keeps a continuing chunk's conv window inside its sequence
   p.Lc = (p.Lc + 15) / 16 * 16;
+  p.ksub = 1;
+  if (engine == MM_ENGINE_ROW && p.Lc <= T) {
+    // pass 1 in pieces; the chunk length a multiple of 16 pieces' worth of tokens
+    const int64_t nchb = cdiv(d, kRowChans);
+    // at least T / Lc - S non-last chunks (sequences longer than Lc have all but one)
+    p.ksub = row_pieces(p.Lc, static_cast<double>(std::max<int64_t>(T / p.Lc - S, 1)), nchb);
+    while (p.ksub > 1 && p.Lc % (16 * p.ksub) != 0) p.ksub /= 2;
+    p.inl = S <= kPlanInline;
+  }
   p.Pmax = cdiv(T, p.Lc) + S;
   p.Mmax = T / p.Lc;
   p.Tpad = T + 16;
@@ -129,14 +157,17 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   p.off_bc = off; off += align256(nbc * sizeof(float));
   if (p.whole) off = 0;  // nothing in the workspace is used
   if (p.Mmax > 0) {
-    p.off_a = off; off += align256(static_cast<size_t>(p.Mmax) * d * sizeof(float));
-    p.off_b = off; off += align256(static_cast<size_t>(p.Mmax) * d * p.nmax * sizeof(float));
+    const size_t m1 = static_cast<size_t>(p.Mmax) * p.ksub;  // carry slots (pass-1 pieces)
+    p.off_a = off; off += align256(m1 * d * sizeof(float));
+    p.off_b = off; off += align256(m1 * d * p.nmax * sizeof(float));
     p.off_stash = off; off += align256(static_cast<size_t>(p.Mmax) * d * (p.nmax + kKS) * sizeof(float));
   }
   p.total = off;
   p.kernels = p.Mmax > 0 ? 5 : 3;
-  if (engine == MM_ENGINE_ROW) p.kernels = p.whole ? 1 : (p.Mmax > 0 ? 4 : 2);
-  const int64_t wgs = engine == MM_ENGINE_LANE ? p.Pmax * cdiv(d, kBlock) : row_grid(p.whole ? S : p.Pmax, d);
+  // row engine: [k_chunk_plan unless the kernels compute it], [pass 1], pass 2
+  if (engine == MM_ENGINE_ROW) p.kernels = p.whole ? 1 : (p.inl ? 0 : 1) + (p.Mmax > 0 ? 1 : 0) + 1;
+  const int64_t wgs = engine == MM_ENGINE_LANE ? p.Pmax * cdiv(d, kBlock)
+                                               : row_grid(p.whole ? S : std::max(p.Pmax, p.Mmax * p.ksub), d);
   if (wgs > INT32_MAX || p.Pmax > INT32_MAX) return MM_ERR_DIM;
   return MM_OK;
 }
@@ -144,10 +175,14 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
 const char* kernel_name(const Plan& p, int i) {
   const char* agg = p.engine == MM_ENGINE_LANE ? "k_lane_agg" : "k_row_agg";
   const char* fin = p.engine == MM_ENGINE_LANE ? "k_lane_final" : "k_row_final";
-  if (p.engine == MM_ENGINE_ROW) {  // stages B/C itself: no packing kernel
+  if (p.engine == MM_ENGINE_ROW) {  // stages B/C itself: no packing kernel; carries folded in pass 2
     if (p.whole) return i == 0 ? fin : "";
-    const char* names[4] = {"k_chunk_plan", p.Mmax > 0 ? agg : fin, "k_carry", fin};
-    return i < p.kernels ? names[i] : "";
+    const char* names[3];
+    int n = 0;
+    if (!p.inl) names[n++] = "k_chunk_plan";
+    if (p.Mmax > 0) names[n++] = agg;
+    names[n++] = fin;
+    return i >= 0 && i < n ? names[i] : "";
   }
   if (i == 0) return "k_chunk_plan";
   if (i == 1) return "k_pack_bc";
@@ -225,18 +260,15 @@ void launch_row(const Plan& p, const PrefillArgs& a, CarryWs cw, hipStream_t st,
   const int whole = p.whole ? 1 : 0;
   const bool vec = row_vec<IO>(a.d, a.N, {a.x, a.z, a.dt, a.B, a.C, a.y});
   IO* yo = static_cast<IO*>(a.y);
-  if (!p.whole) {
+  if (!p.whole && !p.inl) {
     evs.mark(st);
     hipLaunchKernelGGL(k_chunk_plan, dim3(1), dim3(kPlanThreads), 0, st, a.cu, a.S, p.Lc, cw.off, cw.moff);
   }
-  if (p.Mmax > 0) {
+  if (!p.whole && p.Mmax > 0) {
     evs.mark(st);
-    launch_k_row<IO, false, false>(vec, grid, st, a, xi, zi, di, Bi, Ci, a.conv_state, a.ssm_state, yo, cw, p.Lc,
+    const dim3 grid1(static_cast<unsigned>(row_grid(p.Mmax * p.ksub, a.d)));  // pass-1 pieces
+    launch_k_row<IO, false, false>(vec, grid1, st, a, xi, zi, di, Bi, Ci, a.conv_state, a.ssm_state, yo, cw, p.Lc,
                                    whole, nullptr);
-    evs.mark(st);
-    const int64_t q = static_cast<int64_t>(a.d) * kRow;
-    hipLaunchKernelGGL((k_carry<kRow>), dim3(static_cast<unsigned>(cdiv(q, kBlock))), dim3(kBlock), 0, st, cw,
-                       a.A_log, a.S, a.d, a.N);
   }
   evs.mark(st);
   if (ckpt != nullptr)
@@ -253,6 +285,8 @@ int launch_prefill(const Plan& p, const PrefillArgs& a, char* ws, hipStream_t st
   CarryWs cw{};
   cw.off = reinterpret_cast<int32_t*>(ws + p.off_off);
   cw.moff = reinterpret_cast<int32_t*>(ws + p.off_moff);
+  cw.ksub = p.ksub;
+  cw.inl = p.inl ? 1 : 0;
   if (p.Mmax > 0) {
     cw.a = reinterpret_cast<float*>(ws + p.off_a);
     cw.b = reinterpret_cast<float*>(ws + p.off_b);

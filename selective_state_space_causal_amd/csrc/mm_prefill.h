@@ -131,10 +131,55 @@ __device__ __forceinline__ ChunkRef chunk_ref(const int32_t* __restrict__ cu, co
 struct CarryWs {
   int32_t* off;    // [S+1]
   int32_t* moff;   // [S+1]
-  float* a;        // [M][d]         sum(delta) of a non-last chunk, -1 for a sequence's first chunk
-  float* b;        // [M][d][NMAX]   chunk-end state (local after pass 1, true after k_carry)
+  float* a;        // [M*ksub][d]    sum(delta) of a pass-1 piece, -1 for a sequence's first piece
+  float* b;        // [M*ksub][d][NMAX] piece-end state (local after pass 1; the lane engine's k_carry makes it true)
   float* stash;    // [M][d][NMAX+3] initial ssm then conv state of a multi-chunk sequence (at its first slot)
+  int ksub;        // row engine: pass 1 scans each non-last chunk as ksub pieces of Lc / ksub tokens
+  int inl;         // row engine: off / moff are computed by every workgroup (S <= kPlanInline), not read
 };
+
+// The chunk plan of at most kPlanInline sequences, computed by one 256-thread workgroup into
+// its LDS arrays off[0..S], moff[0..S]: the sums of k_chunk_plan.  Saves that kernel's launch
+// where every workgroup can afford S loads of cu_seqlens.
+constexpr int kPlanInline = 256;
+__device__ __forceinline__ void chunk_plan_inline(const int32_t* __restrict__ cu, int S, int64_t Lc, int32_t* off,
+                                                  int32_t* moff, int32_t (&wsum)[2][kPlanInline / kWave]) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wv = t / kWave;
+  int n = 0;
+  if (t < S) {
+    const int64_t L = static_cast<int64_t>(cu[t + 1]) - cu[t];
+    n = static_cast<int>((L + Lc - 1) / Lc);
+  }
+  int m = n > 0 ? n - 1 : 0;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {  // inclusive scan within the wave
+    const int tn = __shfl_up(n, o, kWave);
+    const int tm = __shfl_up(m, o, kWave);
+    if (lane >= o) {
+      n += tn;
+      m += tm;
+    }
+  }
+  if (lane == kWave - 1) {
+    wsum[0][wv] = n;
+    wsum[1][wv] = m;
+  }
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) {
+    n += wsum[0][w];
+    m += wsum[1][w];
+  }
+  if (t < S) {
+    off[t + 1] = n;
+    moff[t + 1] = m;
+  }
+  if (t == 0) {
+    off[0] = 0;
+    moff[0] = 0;
+  }
+  __syncthreads();
+}
 
 // ---------------------------------------------------------------- B/C packing
 

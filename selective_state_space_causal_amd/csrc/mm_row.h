@@ -345,6 +345,13 @@ __device__ __forceinline__ void st_g_uncounted(gmem<float>* p, uint32_t off, flo
   asm volatile("global_store_dword %0, %1, %2" ::"v"(off), "v"(v), "s"(p) : "memory");
 }
 
+// a workgroup-uniform 64-bit value held in vector registers, moved to scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // the lane mask that holds lanes j of every row with bit j of m16 set
 __device__ __forceinline__ uint64_t row_mask(uint32_t m16) {
   const uint32_t m32 = m16 | (m16 << 16);
@@ -367,8 +374,12 @@ __device__ __forceinline__ void row_work(int64_t w, int ncg, int64_t& k, int& cb
   cb = static_cast<int>(item % ncg) * kRowGroup + m;
 }
 
-// FINAL = false: pass 1 (sum(delta) and local end state of every non-last chunk).
-// FINAL = true: pass 2 (y, and the final states at a sequence's last chunk).
+// FINAL = false: pass 1 (sum(delta) and local end state of every piece of a non-last
+// chunk: each such chunk is scanned as ws.ksub pieces of Lc / ksub tokens, so that the
+// pass has enough workgroups; a sequence's first piece starts from its slot).
+// FINAL = true: pass 2 (y, and the final states at a sequence's last chunk); a chunk's
+// carry-in is the fold of the pieces before it, done by the chunk's own workgroup.
+// With ws.inl every workgroup computes the chunk plan itself (no k_chunk_plan launch).
 // CKPT = true: also write the state before every 16-token block to ckpt, [rows][d][16],
 // the block starting at token tb of sequence s at row s + tb / 16.  With FINAL = false
 // (whole sequences only) that is all the pass writes: the checkpoint pass of the
@@ -389,12 +400,18 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   constexpr int64_t kMask = ~static_cast<int64_t>(kRow - 1);
   constexpr uint32_t es = sizeof(IO);
   __shared__ RowTiles L;
+  __shared__ int32_t plan_l[2][kPlanInline + 1];
+  __shared__ int32_t plan_w[2][kPlanInline / kWave];
   int64_t k;
   int cb;
   const int nchb = (d + kRowChans - 1) / kRowChans;
   row_work(blockIdx.x, (nchb + kRowGroup - 1) / kRowGroup, k, cb);
-  if (cb >= nchb) return;
+  if (cb >= nchb) return;  // (uniform over the workgroup)
   ChunkRef R;
+  int64_t slot = 0;  // pass 1: this piece's carry slot
+  int stash_i = 0;   // the sequence's stash slot (multi-chunk sequences)
+  const int32_t* offp = ws.off;
+  const int32_t* moffp = ws.moff;
   if (whole) {
     if (k >= S) return;
     R.ok = true;
@@ -405,11 +422,45 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     R.end = cu[R.s + 1];
     if (R.end <= R.start) return;  // empty sequence: its slot stays as it is
     R.cidx = R.pidx = 0;
+    if (!FINAL && !CKPT) return;
   } else {
-    R = chunk_ref(cu, ws.off, ws.moff, S, k, Lc);
-    if (!R.ok) return;
+    if (ws.inl) {  // (uniform)
+      chunk_plan_inline(cu, S, Lc, plan_l[0], plan_l[1], plan_w);
+      offp = plan_l[0];
+      moffp = plan_l[1];
+    }
+    if (!FINAL && !CKPT) {
+      // pass 1: piece k of the non-last chunks, each chunk scanned as ksub pieces of Lc / ksub
+      // tokens (pieces of non-last chunks are full); its sequence is the largest s with
+      // moff[s] <= k / ksub
+      const int64_t q = k / ws.ksub;
+      if (q >= moffp[S]) return;
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(moffp[mid]) <= q) lo = mid; else hi = mid - 1;
+      }
+      R.ok = true;
+      R.s = lo;
+      R.j = static_cast<int>(k - static_cast<int64_t>(ws.ksub) * moffp[lo]);  // piece within the sequence
+      R.ns = offp[lo + 1] - offp[lo];
+      R.start = cu[lo] + static_cast<int64_t>(R.j) * (Lc / ws.ksub);
+      R.end = R.start + Lc / ws.ksub;
+      R.cidx = R.pidx = 0;
+      slot = k;
+    } else {
+      R = chunk_ref(cu, offp, moffp, S, k, Lc);
+      if (!R.ok) return;
+    }
+    stash_i = moffp[R.s];
+    // read from LDS, these workgroup-uniform values sit in vector registers: into scalar ones
+    R.s = __builtin_amdgcn_readfirstlane(R.s);
+    R.j = __builtin_amdgcn_readfirstlane(R.j);
+    R.ns = __builtin_amdgcn_readfirstlane(R.ns);
+    R.start = uniform64(R.start);
+    R.end = uniform64(R.end);
+    stash_i = __builtin_amdgcn_readfirstlane(stash_i);
   }
-  if (!FINAL && !CKPT && R.j == R.ns - 1) return;
 
   const int j = threadIdx.x & (kRow - 1);             // state entry in the scan; token of the block in the per-token work
   const int ch = static_cast<int>(threadIdx.x >> 4);  // row = channel within the workgroup
@@ -435,16 +486,38 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     if (R.j == 0) {
       h = (j < N) ? ssm_state[sc * N + j] : 0.0f;
       if (cvalid) {
-        float* stash = ws.stash + (static_cast<int64_t>(R.cidx) * d + c) * (NMAX + kKS);
+        float* stash = ws.stash + (static_cast<int64_t>(stash_i) * d + c) * (NMAX + kKS);
         stash[j] = h;
         if (j < kKS) stash[NMAX + j] = conv_state[sc * kKS + j];
       }
     }
   } else if (R.j == 0) {
-    h = from_stash ? ws.stash[(static_cast<int64_t>(ws.moff[R.s]) * d + cc) * (NMAX + kKS) + j]
+    h = from_stash ? ws.stash[(static_cast<int64_t>(stash_i) * d + cc) * (NMAX + kKS) + j]
                    : ((j < N) ? ssm_state[sc * N + j] : 0.0f);
   } else {
-    h = ws.b[(static_cast<int64_t>(R.pidx) * d + cc) * NMAX + j];
+    // the carry-in: pass 1's pieces of the chunks before this one, folded in order with
+    // (a, b) o (a', b') = (a a', a' b + b'), a piece's decay product being exp(A sum(delta)).
+    // The first piece started from the slot, so its state is already true.  The loads of a
+    // group of eight pieces are issued before their arithmetic.
+    const int64_t m0 = static_cast<int64_t>(ws.ksub) * stash_i;
+    const int64_t m1 = m0 + static_cast<int64_t>(R.j) * ws.ksub;
+    const float* pa = ws.a + cc;
+    const float* pb = ws.b + static_cast<int64_t>(cc) * NMAX + j;
+    const int64_t sa = d, sb = static_cast<int64_t>(d) * NMAX;
+    float cur = pb[m0 * sb];
+    for (int64_t i = m0 + 1; i < m1; i += 8) {
+      float av[8], bv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t iu = i + u < m1 ? i + u : m1 - 1;
+        av[u] = pa[iu * sa];
+        bv[u] = pb[iu * sb];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i + u < m1) cur = __builtin_fmaf(exp2_hw(A2 * av[u]), cur, bv[u]);
+    }
+    h = cur;
   }
 
   const int64_t tb0 = R.start & kMask;
@@ -576,7 +649,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     // raw input of token t for the staging channel; tokens before the sequence's start
     // come from its initial conv state (zero before that)
     const int cs = c0 + schc;
-    const float* cs0 = from_stash ? ws.stash + (static_cast<int64_t>(ws.moff[R.s]) * d + cs) * (NMAX + kKS) + NMAX
+    const float* cs0 = from_stash ? ws.stash + (static_cast<int64_t>(stash_i) * d + cs) * (NMAX + kKS) + NMAX
                                   : conv_state + (static_cast<int64_t>(R.s) * d + cs) * kKS;
     auto hist = [&](int64_t t) -> float {
       if (t >= seq_start) return io_f32(x[t * d + cs]);
@@ -804,7 +877,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
   if (!FINAL) {
     const float ds = row_sum(dsum);
     if (cvalid) {
-      const int64_t pc = static_cast<int64_t>(R.cidx) * d + c;
+      const int64_t pc = slot * d + c;
       if (j == 0) ws.a[pc] = (R.j == 0) ? -1.0f : ds;
       ws.b[pc * NMAX + j] = h;
     }

@@ -145,10 +145,21 @@ def test_workspace_query_and_plan(lib):
     # many sequences -> the lane engine; sequences of the mean length are not split
     q = mm.plan(256, 131072, 8192, 16)
     assert q["engine_name"] == "lane" and q["chunk_len"] >= 512 and q["kernels"][-1] == "k_lane_final"
-    # a single long sequence is split into chunks to fill the GPU
+    # a single long sequence is split into chunks to fill the GPU: pass 1 over the pieces of the
+    # non-last chunks, then the final pass, which folds the carries itself; with few sequences
+    # the kernels compute the chunk plan themselves
     r = mm.plan(1, 131072, 5120, 16)
     assert r["engine_name"] == "row" and r["chunk_len"] < 131072
-    assert r["kernels"] == ["k_chunk_plan", "k_row_agg", "k_carry", "k_row_final"]
+    assert r["kernels"] == ["k_row_agg", "k_row_final"]
+    r2 = mm.plan(300, 300 * 2048, 64, 16, chunk_len=512, engine=2)
+    assert r2["kernels"] == ["k_chunk_plan", "k_row_agg", "k_row_final"]
+    # pass-1 pieces have their own carry slots: one sequence of 8192 tokens in 2048-token
+    # chunks (3 non-last chunks) with 320 channel blocks takes 4 pieces per chunk to give
+    # pass 1 about 8 workgroups per CU.  Workspace: the chunk offsets, then sum(delta) and the
+    # end state per slot (slots for the 4-chunk bound x 4 pieces), the stash per chunk
+    d = 5120
+    assert mm.workspace_bytes(1, 8192, d, 16, chunk_len=2048, engine=2) == \
+        2 * 256 + 4 * 4 * d * 4 + 4 * 4 * d * 16 * 4 + 4 * d * 19 * 4
     # explicit engines and chunk lengths are honoured (chunk lengths round up to 16)
     for e, name in ((1, "lane"), (2, "row")):
         pe = mm.plan(3, 500, 100, 16, chunk_len=40, engine=e)

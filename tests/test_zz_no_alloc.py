@@ -1,7 +1,7 @@
 """mamba_mixer_prefill_noalloc, the prefill for callers that cannot allocate (its carries live in the
 library's fixed per-GPU scratch), through the C ABI: three calls in a row, each smaller than the one
-before (a lane-engine plan with 1.9 MB of carries and packed B/C, a chunked row-engine plan with
-92 KB, a whole-sequence plan with none), each equal bit for bit to mamba_mixer_prefill with a
+before (a lane-engine plan with about 1.9 MB of carries and packed B/C, a chunked row-engine plan
+with about 0.1 MB, a whole-sequence plan with none), each equal bit for bit to mamba_mixer_prefill with a
 caller-allocated workspace on the same inputs (the same plan and kernels) and within the bf16
 tolerance of the oracle.  Needs an MI355X."""
 from __future__ import annotations
@@ -41,22 +41,23 @@ def _run(case, noalloc):
     return host(y), host(cs), host(ss)
 
 
-CASES = [  # (lengths, d, expected engine, expected workspace bytes)
-    ([3, 1, 0, 2] * 2048 + [5], 64, "lane", 1862912),
-    ([3000], 64, "row", 92672),
-    ([300, 1, 0, 499], 80, "row", 0),
+CASES = [  # (lengths, d, expected engine): workspace from the plan query, falling from call to call
+    ([3, 1, 0, 2] * 2048 + [5], 64, "lane"),
+    ([3000], 64, "row"),
+    ([300, 1, 0, 499], 80, "row"),
 ]
 
 
 def test_noalloc_prefill_equals_workspace_prefill():
     assert torch.cuda.is_available(), "needs a GPU"
     prev = None
-    for i, (lens, d, engine, need) in enumerate(CASES):
+    for i, (lens, d, engine) in enumerate(CASES):
         case = make_prefill(700 + i, lens, d, 16, "bf16", varied=True)
         p = mm.plan(case["S"], case["T"], d, 16)
-        log(f"[noalloc] call {i}: S={case['S']} T={case['T']} d={d} plan {p['kernels']} workspace "
-            f"{p['workspace_bytes']}")
-        assert p["engine_name"] == engine and p["workspace_bytes"] == need
+        need = p["workspace_bytes"]
+        log(f"[noalloc] call {i}: S={case['S']} T={case['T']} d={d} plan {p['kernels']} workspace {need}")
+        assert p["engine_name"] == engine
+        assert (need == 0) == (i == len(CASES) - 1), "the last call needs no workspace, the others do"
         assert need <= mm.NOALLOC_SCRATCH_BYTES
         if prev is not None:
             assert need < prev, "each call needs less scratch than the one before"
