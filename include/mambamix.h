@@ -62,7 +62,8 @@ extern "C" {
 /* status codes */
 #define MM_OK               0
 #define MM_ERR_NULL        -1  /* a required pointer is NULL                                  */
-#define MM_ERR_DIM         -2  /* a negative size, T > INT32_MAX, S == 0 with T > 0, too few events */
+#define MM_ERR_DIM         -2  /* a negative size, T > INT32_MAX, S == 0 with T > 0, too few events,
+                                  an array of more than MM_MAX_ROWS_X_D rows x channels        */
 #define MM_ERR_UNSUPPORTED -3  /* K != 4, N outside 1..16, unknown io dtype or engine, d too large */
 #define MM_ERR_ALIGN       -4  /* a pointer not aligned to its element size                    */
 #define MM_ERR_WORKSPACE   -5  /* workspace smaller than the size query returns (or NULL)      */
@@ -76,6 +77,9 @@ extern "C" {
 /* limits of this build */
 #define MM_MAX_N 16
 #define MM_CONV_K 4
+/* Largest rows x channels of any array (tokens x d, sequences x d, batch x d): 2^36, far more
+ * than one GPU's memory holds, and small enough that every byte extent fits in 64 bits. */
+#define MM_MAX_ROWS_X_D (1ull << 36)
 
 /*
  * mamba_mixer_prefill -- run the mixer over S packed sequences.
@@ -244,6 +248,35 @@ int mamba_mixer_decode_replay(const void* x_ring, const void* dt_ring, const voi
                               int32_t k, int32_t commit, void* stream);
 
 /*
+ * mamba_mixer_decode_replay_dual -- mamba_mixer_decode_replay with the dual-precision
+ * checkpoint of the ReplaySSM page (abstract: a low-precision checkpoint serves the output
+ * computation on most steps, a higher-precision checkpoint the recurrent updates).  Beside the
+ * fp32 checkpoint (conv_state, ssm_state) the caller keeps its bf16 copy:
+ *   conv_lo   [Bs, d, 4]  bf16   conv_state rounded to nearest even; entry 3 is zero
+ *   ssm_lo    [Bs, d, N]  bf16   ssm_state rounded to nearest even
+ * A call that does not commit reads only the copy (40 bytes per (row, channel) instead of 76):
+ * its output is that of the window step from the rounded checkpoint.  A committing call
+ * (commit != 0 or k == W - 1) reads the fp32 checkpoint: its output and the state it commits
+ * equal, bit for bit, those of the eager decode, and it rewrites both checkpoints.  Fill the
+ * copy once with mamba_mixer_replay_checkpoint_lo (e.g. after the prefill that initialises the
+ * state).  Everything else, the ring layouts and the limits are those of
+ * mamba_mixer_decode_replay; io must be MM_IO_BF16 (else MM_ERR_UNSUPPORTED); ssm_lo must be
+ * 16-byte and conv_lo 8-byte aligned (MM_ERR_ALIGN); the copies may not overlap any other
+ * array (MM_ERR_ALIAS).
+ */
+int mamba_mixer_decode_replay_dual(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z,
+                                   const void* C, const float* A_log, const float* D, const float* dt_bias,
+                                   const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
+                                   void* conv_lo, void* ssm_lo, void* y, int32_t Bs, int32_t d, int32_t N, int32_t K,
+                                   int32_t io_dtype, int32_t W, int32_t k, int32_t commit, void* stream);
+
+/* The bf16 copy (conv_lo [Bs, d, 4], ssm_lo [Bs, d, N], rounded to nearest even, conv entry 3
+ * zero) of an fp32 replay checkpoint, for mamba_mixer_decode_replay_dual.  N must be 16;
+ * alignment and overlap rules as there. */
+int mamba_mixer_replay_checkpoint_lo(const float* conv_state, const float* ssm_state, void* conv_lo, void* ssm_lo,
+                                     int32_t Bs, int32_t d, int32_t N, int32_t K, void* stream);
+
+/*
  * mamba_mixer_decode_replay_multi -- several steps of a replay window in one call, for
  * speculative decoding (the ReplaySSM page, abstract: with the recent inputs kept,
  * rolling back a speculation is a buffer-pointer move, and outputs of draft tokens can be
@@ -339,7 +372,8 @@ int mamba_mixer_prefill_train(const void* x, const void* z, const void* dt, cons
                               void* y, float* ckpt, int32_t S, int64_t T, int32_t d, int32_t N, int32_t K,
                               int32_t io_dtype, int64_t chunk_len, void* workspace, size_t workspace_bytes,
                               void* stream, void* const* events, int32_t n_events);
-/* Bytes of the checkpoints of a prefill of S sequences and T tokens with d channels. */
+/* Bytes of the checkpoints of a prefill of S sequences and T tokens with d channels (0 for sizes
+ * the calls reject). */
 size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d);
 /*
  * mamba_mixer_project -- the input-dependent projections that produce the scan's dt, B and C

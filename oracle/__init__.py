@@ -170,6 +170,26 @@ def decode_replay(x_ring, dt_ring, B_ring, k, z, C, A_log, D, dt_bias, conv_w, c
     return decode(x_ring[k], z, dt_ring[k], B_ring[k], C, A_log, D, dt_bias, conv_w, conv_b, cs, ss, nthreads)
 
 
+def bf16_round(a):
+    """Values rounded to the nearest bfloat16 (8 significant bits), ties to even, as float64.
+    With a = m 2^e, 0.5 <= |m| < 1 (frexp), the bf16 value is round(256 m) / 256 * 2^e, where
+    round takes halves to the even neighbour (numpy's round); a carry to 256 gives 2^e exactly."""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def decode_replay_lo(x_ring, dt_ring, B_ring, k, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
+                     nthreads: int = 0):
+    """Output of window step k with the dual-precision checkpoint ("ReplaySSM: Cache SSM Inputs,
+    Not State", abstract: a low-precision checkpoint serves the output computation of most steps,
+    a higher-precision one the recurrent updates): ``decode_replay`` from the checkpoint (conv and
+    SSM state) rounded to bfloat16.  Returns (y_k, conv_state, ssm_state) as decode_replay does
+    (the states after step k from the rounded checkpoint; a committing step uses the full one)."""
+    return decode_replay(x_ring, dt_ring, B_ring, k, z, C, A_log, D, dt_bias, conv_w, conv_b,
+                         bf16_round(conv_state), bf16_round(ssm_state), nthreads)
+
+
 def project(x, conv_w, conv_b, cu_seqlens, conv_state, w_x, w_dt, R: int, N: int):
     """The input-dependent projections ahead of the scan, as the TensorRT Mamba tensor-parallel
     builder (_add_mamba_tp_layer) lays them out: the conv activation u (window = the state's K-1

@@ -62,6 +62,10 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_decode.restype = ctypes.c_int
     lib.mamba_mixer_decode_replay.argtypes = [P] * 13 + [i32, i32, i32, i32, i32, i32, i32, i32, P]
     lib.mamba_mixer_decode_replay.restype = ctypes.c_int
+    lib.mamba_mixer_decode_replay_dual.argtypes = [P] * 15 + [i32] * 8 + [P]
+    lib.mamba_mixer_decode_replay_dual.restype = ctypes.c_int
+    lib.mamba_mixer_replay_checkpoint_lo.argtypes = [P] * 4 + [i32] * 4 + [P]
+    lib.mamba_mixer_replay_checkpoint_lo.restype = ctypes.c_int
     lib.mamba_mixer_decode_replay_multi.argtypes = [P] * 13 + [i32] * 9 + [P]
     lib.mamba_mixer_decode_replay_multi.restype = ctypes.c_int
     lib.mamba_mixer_prefill_backward.argtypes = [P] * 27 + [i32, i64, i32, i32, i32, i32, P, sz, P, P, i32]
@@ -471,6 +475,63 @@ def decode_replay(x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv
         W, int(k), 1 if commit else 0, _stream(stream))
     if rc != MM_OK:
         raise MambaMixError(rc, "mamba_mixer_decode_replay")
+    return y
+
+
+def replay_checkpoint_lo(conv_state, ssm_state, conv_lo=None, ssm_lo=None, stream=None):
+    """The bf16 copy of a replay checkpoint for ``decode_replay_dual``: returns (conv_lo [Bs, d, 4],
+    ssm_lo [Bs, d, N]) as bfloat16 (conv entry 3 zero)."""
+    import torch
+
+    Bs, d, N = ssm_state.shape
+    _check(conv_state, (Bs, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (Bs, d, N), torch.float32, "ssm_state")
+    if conv_lo is None:
+        conv_lo = torch.empty((Bs, d, 4), dtype=torch.bfloat16, device=ssm_state.device)
+    if ssm_lo is None:
+        ssm_lo = torch.empty((Bs, d, N), dtype=torch.bfloat16, device=ssm_state.device)
+    _check(conv_lo, (Bs, d, 4), torch.bfloat16, "conv_lo")
+    _check(ssm_lo, (Bs, d, N), torch.bfloat16, "ssm_lo")
+    rc = load().mamba_mixer_replay_checkpoint_lo(_ptr(conv_state), _ptr(ssm_state), _ptr(conv_lo), _ptr(ssm_lo),
+                                                 Bs, d, N, CONV_K, _stream(stream))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_replay_checkpoint_lo")
+    return conv_lo, ssm_lo
+
+
+def decode_replay_dual(x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state,
+                       conv_lo, ssm_lo, k: int, commit: bool = False, y=None, stream=None):
+    """Step k of a replay window with the dual-precision checkpoint (see
+    ``mamba_mixer_decode_replay_dual``): steps that do not commit read only the bf16 copy
+    (conv_lo [Bs, d, 4], ssm_lo [Bs, d, N]); a committing step reads the fp32 checkpoint and
+    rewrites both.  bf16 io.  Returns y [Bs, d]."""
+    import torch
+
+    W, Bs, d = x_ring.shape
+    N = B_ring.shape[2]
+    io = x_ring.dtype
+    _check(x_ring, (W, Bs, d), io, "x_ring")
+    _check(dt_ring, (W, Bs, d), io, "dt_ring")
+    _check(B_ring, (W, Bs, N), io, "B_ring")
+    _check(z, (Bs, d), io, "z")
+    _check(C, (Bs, N), io, "C")
+    _check(A_log, (d, N), torch.float32, "A_log")
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (conv_b, "conv_b")):
+        _check(t, (d,), torch.float32, n)
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(conv_state, (Bs, d, CONV_K - 1), torch.float32, "conv_state")
+    _check(ssm_state, (Bs, d, N), torch.float32, "ssm_state")
+    _check(conv_lo, (Bs, d, 4), torch.bfloat16, "conv_lo")
+    _check(ssm_lo, (Bs, d, N), torch.bfloat16, "ssm_lo")
+    if y is None:
+        y = torch.empty((Bs, d), dtype=io, device=x_ring.device)
+    _check(y, (Bs, d), io, "y")
+    rc = load().mamba_mixer_decode_replay_dual(
+        _ptr(x_ring), _ptr(dt_ring), _ptr(B_ring), _ptr(z), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias),
+        _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(ssm_state), _ptr(conv_lo), _ptr(ssm_lo), _ptr(y),
+        Bs, d, N, CONV_K, _io_code(x_ring), W, int(k), 1 if commit else 0, _stream(stream))
+    if rc != MM_OK:
+        raise MambaMixError(rc, "mamba_mixer_decode_replay_dual")
     return y
 
 

@@ -120,7 +120,8 @@ int make_plan(Plan& p, int64_t S, int64_t T, int d, int N, int64_t chunk_len, in
   p.engine = engine;
   if (engine == MM_ENGINE_ROW) p.nmax = kRow;  // one state entry per lane of a 16-lane row
   if (chunk_len > 0) {
-    p.Lc = chunk_len;
+    // a chunk longer than the stream is the same as one of T + 1 tokens (whole sequences)
+    p.Lc = std::min<int64_t>(chunk_len, T + 1);
   } else if (engine == MM_ENGINE_ROW) {
     // chunks shorter than ~256 tokens are not worth their carries
     const int64_t pmax = avg / 256 < 16 ? avg / 256 : 16;
@@ -357,6 +358,8 @@ int launch_decode(const void* x, const void* z, const void* dt, const void* B, c
 
 int check_common(int64_t rows, int32_t d, int32_t N, int32_t K, int32_t io) {
   if (rows < 0 || d < 0 || N < 0 || K < 0) return MM_ERR_DIM;
+  // keeps every byte extent (rows x d x 16 x 4 at most) far inside 64 bits
+  if (d > 0 && static_cast<uint64_t>(rows) > MM_MAX_ROWS_X_D / static_cast<uint64_t>(d)) return MM_ERR_DIM;
   if (K != kK || N < 1 || N > MM_MAX_N) return MM_ERR_UNSUPPORTED;
   if (io != MM_IO_F32 && io != MM_IO_BF16) return MM_ERR_UNSUPPORTED;
   return MM_OK;
@@ -368,18 +371,28 @@ int check_prefill_sizes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, i
   if (rc != MM_OK) return rc;
   if (S < 0 || T > INT32_MAX) return MM_ERR_DIM;
   if (S == 0 && T > 0) return MM_ERR_DIM;
+  if (d > 0 && static_cast<uint64_t>(S) > MM_MAX_ROWS_X_D / static_cast<uint64_t>(d)) return MM_ERR_DIM;
   return MM_OK;
 }
 
-// Validation and launch shared by the two replay entry points.  multi: z, C and y are
-// rings [W][Bs][...] indexed by window step; otherwise they are this step's [Bs][...].
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// Validation and launch shared by the replay entry points.  multi: z, C and y are rings
+// [W][Bs][...] indexed by window step; otherwise they are this step's [Bs][...].  dual: the
+// checkpoint's bf16 copy (conv_lo [Bs][d][4], ssm_lo [Bs][d][16]) is read by a call that
+// commits nothing and rewritten by one that commits (bf16 io only).
 int replay_launch(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z, const void* C,
                   const float* A_log, const float* D, const float* dt_bias, const float* conv_w, const float* conv_b,
                   float* conv_state, float* ssm_state, void* y, int32_t Bs, int32_t d, int32_t N, int32_t K,
-                  int32_t io_dtype, int32_t W, int32_t k0, int32_t k1, int32_t cstep, bool multi, void* stream) {
+                  int32_t io_dtype, int32_t W, int32_t k0, int32_t k1, int32_t cstep, bool multi, void* stream,
+                  bool dual = false, void* conv_lo = nullptr, void* ssm_lo = nullptr) {
   int rc = check_common(Bs, d, N, K, io_dtype);
   if (rc != MM_OK) return rc;
   if (N != kReplayN) return MM_ERR_UNSUPPORTED;
+  if (dual && io_dtype != MM_IO_BF16) return MM_ERR_UNSUPPORTED;
   if (W < 1 || W > kReplayMaxW || k0 < 0 || k0 > k1 || k1 >= W || cstep < -1 || cstep > k1) return MM_ERR_DIM;
   if (Bs == 0 || d == 0) return MM_OK;
   const void* req[] = {x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y};
@@ -406,26 +419,45 @@ int replay_launch(const void* x_ring, const void* dt_ring, const void* B_ring, c
     return MM_ERR_ALIAS;
   if (overlap(conv_state, static_cast<size_t>(Bs) * d * kKS * 4, ssm_state, static_cast<size_t>(Bs) * d * N * 4))
     return MM_ERR_ALIAS;
+  if (dual) {
+    if (conv_lo == nullptr || ssm_lo == nullptr) return MM_ERR_NULL;
+    if (!aligned(ssm_lo, 16) || !aligned(conv_lo, 8)) return MM_ERR_ALIGN;
+    const size_t nsl = static_cast<size_t>(Bs) * d * N * 2, ncl = static_cast<size_t>(Bs) * d * 4 * 2;
+    const Span other[] = {{x_ring, nring}, {dt_ring, nring}, {B_ring, nbr}, {z, nz}, {C, nc}, {y, ny},
+                          {conv_state, static_cast<size_t>(Bs) * d * kKS * 4},
+                          {ssm_state, static_cast<size_t>(Bs) * d * N * 4}, {conv_lo, ncl}};
+    for (const Span& v : other)
+      if (overlap(ssm_lo, nsl, v.p, v.n) || (v.p != conv_lo && overlap(conv_lo, ncl, v.p, v.n))) return MM_ERR_ALIAS;
+  }
   // z/C/y of step t sit at slot t - k0 of the pointers passed to the kernel
   const int64_t zs = multi ? static_cast<int64_t>(Bs) * d : 0, cs = multi ? static_cast<int64_t>(Bs) * N : 0;
   const int64_t off_d = multi ? static_cast<int64_t>(k0) * Bs * d : 0;
   const int64_t off_n = multi ? static_cast<int64_t>(k0) * Bs * N : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(cdiv(d, kBlock) * Bs));
+  uint16_t* slo = static_cast<uint16_t*>(ssm_lo);
+  uint16_t* clo = static_cast<uint16_t*>(conv_lo);
   if (io_dtype == MM_IO_BF16) {
     using T = uint16_t;
-    hipLaunchKernelGGL((k_decode_replay<T>), grid, dim3(kBlock), 0, st, static_cast<const T*>(x_ring),
-                       static_cast<const T*>(dt_ring), static_cast<const T*>(B_ring),
-                       static_cast<const T*>(z) + off_d, static_cast<const T*>(C) + off_n, A_log, D, dt_bias,
-                       conv_w, conv_b, conv_state, ssm_state, static_cast<T*>(y) + off_d, Bs, d, k0, k1, cstep, zs,
-                       cs, zs);
+    if (dual && cstep < 0)  // outputs from the bf16 copy, nothing committed
+      hipLaunchKernelGGL((k_decode_replay<T, true>), grid, dim3(kBlock), 0, st, static_cast<const T*>(x_ring),
+                         static_cast<const T*>(dt_ring), static_cast<const T*>(B_ring),
+                         static_cast<const T*>(z) + off_d, static_cast<const T*>(C) + off_n, A_log, D, dt_bias,
+                         conv_w, conv_b, conv_state, ssm_state, static_cast<T*>(y) + off_d, Bs, d, k0, k1, cstep,
+                         zs, cs, zs, slo, clo, nullptr, nullptr);
+    else  // from the fp32 checkpoint; a dual commit also rewrites the bf16 copy
+      hipLaunchKernelGGL((k_decode_replay<T, false>), grid, dim3(kBlock), 0, st, static_cast<const T*>(x_ring),
+                         static_cast<const T*>(dt_ring), static_cast<const T*>(B_ring),
+                         static_cast<const T*>(z) + off_d, static_cast<const T*>(C) + off_n, A_log, D, dt_bias,
+                         conv_w, conv_b, conv_state, ssm_state, static_cast<T*>(y) + off_d, Bs, d, k0, k1, cstep,
+                         zs, cs, zs, nullptr, nullptr, dual ? slo : nullptr, dual ? clo : nullptr);
   } else {
     using T = float;
-    hipLaunchKernelGGL((k_decode_replay<T>), grid, dim3(kBlock), 0, st, static_cast<const T*>(x_ring),
+    hipLaunchKernelGGL((k_decode_replay<T, false>), grid, dim3(kBlock), 0, st, static_cast<const T*>(x_ring),
                        static_cast<const T*>(dt_ring), static_cast<const T*>(B_ring),
                        static_cast<const T*>(z) + off_d, static_cast<const T*>(C) + off_n, A_log, D, dt_bias,
                        conv_w, conv_b, conv_state, ssm_state, static_cast<T*>(y) + off_d, Bs, d, k0, k1, cstep, zs,
-                       cs, zs);
+                       cs, zs, nullptr, nullptr, nullptr, nullptr);
   }
   return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }
@@ -517,11 +549,6 @@ int launch_backward(const BwdPlan& p, const BwdArgs& a, char* ws, hipStream_t st
   evs.mark(st);
   return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }
-
-struct Span {
-  const void* p;
-  size_t n;
-};
 
 // ---------------------------------------------------------------- projections
 
@@ -725,8 +752,10 @@ int mamba_mixer_prefill_ex(const void* x, const void* z, const void* dt, const v
 }
 
 size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d) {
-  if (S < 0 || T < 0 || d < 0) return 0;
-  return static_cast<size_t>(cdiv(T, kRow) + S) * d * kRow * sizeof(float);
+  if (S < 0 || T < 0 || d < 0 || T > INT32_MAX) return 0;
+  const uint64_t rows = static_cast<uint64_t>(cdiv(T, kRow) + S);
+  if (d > 0 && rows > MM_MAX_ROWS_X_D / static_cast<uint64_t>(d)) return 0;
+  return static_cast<size_t>(rows) * d * kRow * sizeof(float);
 }
 
 int mamba_mixer_prefill_train(const void* x, const void* z, const void* dt, const void* B, const void* C,
@@ -821,6 +850,36 @@ int mamba_mixer_decode_replay(const void* x_ring, const void* dt_ring, const voi
                        Bs, d, N, K, io_dtype, W, k, k, cstep, false, stream);
 }
 
+int mamba_mixer_decode_replay_dual(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z,
+                                   const void* C, const float* A_log, const float* D, const float* dt_bias,
+                                   const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
+                                   void* conv_lo, void* ssm_lo, void* y, int32_t Bs, int32_t d, int32_t N, int32_t K,
+                                   int32_t io_dtype, int32_t W, int32_t k, int32_t commit, void* stream) {
+  const int cstep = (commit != 0 || k == W - 1) ? k : -1;
+  return replay_launch(x_ring, dt_ring, B_ring, z, C, A_log, D, dt_bias, conv_w, conv_b, conv_state, ssm_state, y,
+                       Bs, d, N, K, io_dtype, W, k, k, cstep, false, stream, true, conv_lo, ssm_lo);
+}
+
+int mamba_mixer_replay_checkpoint_lo(const float* conv_state, const float* ssm_state, void* conv_lo, void* ssm_lo,
+                                     int32_t Bs, int32_t d, int32_t N, int32_t K, void* stream) {
+  int rc = check_common(Bs, d, N, K, MM_IO_BF16);
+  if (rc != MM_OK) return rc;
+  if (N != kReplayN) return MM_ERR_UNSUPPORTED;
+  if (Bs == 0 || d == 0) return MM_OK;
+  if (conv_state == nullptr || ssm_state == nullptr || conv_lo == nullptr || ssm_lo == nullptr) return MM_ERR_NULL;
+  if (!aligned(conv_state, 4) || !aligned(ssm_state, 16) || !aligned(ssm_lo, 16) || !aligned(conv_lo, 8))
+    return MM_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(Bs) * d;
+  const Span all[] = {{conv_state, n * kKS * 4}, {ssm_state, n * N * 4}, {conv_lo, n * 4 * 2}, {ssm_lo, n * N * 2}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(all[i].p, all[i].n, all[j].p, all[j].n)) return MM_ERR_ALIAS;
+  hipLaunchKernelGGL(k_checkpoint_lo, dim3(static_cast<unsigned>(cdiv(static_cast<int64_t>(n), kBlock))), dim3(kBlock),
+                     0, static_cast<hipStream_t>(stream), conv_state, ssm_state, static_cast<uint16_t*>(conv_lo),
+                     static_cast<uint16_t*>(ssm_lo), static_cast<int64_t>(n));
+  return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
+}
+
 int mamba_mixer_decode_replay_multi(const void* x_ring, const void* dt_ring, const void* B_ring, const void* z_ring,
                                     const void* C_ring, const float* A_log, const float* D, const float* dt_bias,
                                     const float* conv_w, const float* conv_b, float* conv_state, float* ssm_state,
@@ -872,7 +931,7 @@ int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, c
   const size_t nck = ckpt != nullptr ? mamba_mixer_checkpoint_bytes(S, T, d) : 0;
   const Span in[] = {{x, ntd}, {z, ntd}, {dt, ntd}, {B, ntn}, {C, ntn}, {dy, ntd},
                      {A_log, nd * N}, {D, nd}, {dt_bias, nd}, {conv_w, nd * K}, {conv_b, nd},
-                     {cu_seqlens, static_cast<size_t>(S + 1) * 4}, {conv_state, nsk},
+                     {cu_seqlens, (static_cast<size_t>(S) + 1) * 4}, {conv_state, nsk},
                      {ssm_state, ckpt != nullptr ? 0 : nsn}, {ckpt, nck}};
   const Span out[] = {{dx, ntd}, {dz, ntd}, {ddt, ntd}, {dB, ntn}, {dC, ntn},
                       {dA_log, nd * N}, {dD, nd}, {ddt_bias, nd}, {dconv_w, nd * K}, {dconv_b, nd},
@@ -929,7 +988,7 @@ int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b,
   const size_t P = static_cast<size_t>(R) + 2 * N;
   const size_t ntd = static_cast<size_t>(T) * d * 2, ntn = static_cast<size_t>(T) * N * 2;
   const Span in[] = {{x, ntd}, {conv_w, static_cast<size_t>(d) * kK * 4}, {conv_b, static_cast<size_t>(d) * 4},
-                     {cu_seqlens, static_cast<size_t>(S + 1) * 4}, {conv_state, static_cast<size_t>(S) * d * kKS * 4},
+                     {cu_seqlens, (static_cast<size_t>(S) + 1) * 4}, {conv_state, static_cast<size_t>(S) * d * kKS * 4},
                      {w_x, static_cast<size_t>(d) * P * 2}, {w_dt, static_cast<size_t>(R) * d * 2}};
   const Span out[] = {{dt, ntd}, {B, ntn}, {C, ntn}};
   for (const Span& v : in)

@@ -5,6 +5,11 @@
 
 namespace mm {
 
+typedef float f32x2_lo __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_lo __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_lo __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_lo __attribute__((ext_vector_type(2)));
+
 // Decode: one token per row; lane = channel, block = 256 channels of one row.
 template <typename IO, int NMAX>
 __global__ void __launch_bounds__(kBlock) k_decode(
@@ -181,13 +186,22 @@ __global__ void __launch_bounds__(kBlock) k_decode_vec(
 // Window steps 0..k1 are taken from the checkpoint; steps k0..k1 write their output
 // (z, C and y of step t at slot t - k0 of the z/C/y arrays, slot strides zs, cs_, ys);
 // if 0 <= cstep <= k1 the state after step cstep becomes the checkpoint.
-template <typename IO>
+//
+// Dual-precision checkpoint (the same page: a low-precision checkpoint serves the outputs of
+// most steps, a higher-precision one the recurrent updates): with LO, the checkpoint is read
+// from its bf16 copy (ssm_lo [Bs][d][16], conv_lo [Bs][d][4], entry 3 unused), 40 bytes per
+// (row, channel) instead of 76; such a call commits nothing.  A committing call reads the
+// fp32 checkpoint and, when ssm_lo_out is given, also writes the new checkpoint's bf16 copy
+// (rounded to nearest even).
+template <typename IO, bool LO>
 __global__ void __launch_bounds__(kBlock) k_decode_replay(
     const IO* __restrict__ x_ring, const IO* __restrict__ dt_ring, const IO* __restrict__ B_ring,
     const IO* __restrict__ z, const IO* __restrict__ C, const float* __restrict__ A_log,
     const float* __restrict__ D, const float* __restrict__ dt_bias, const float* __restrict__ conv_w,
     const float* __restrict__ conv_b, float* __restrict__ conv_state, float* __restrict__ ssm_state,
-    IO* __restrict__ y, int Bs, int d, int k0, int k1, int cstep, int64_t zs, int64_t cst, int64_t ys) {
+    IO* __restrict__ y, int Bs, int d, int k0, int k1, int cstep, int64_t zs, int64_t cst, int64_t ys,
+    const uint16_t* __restrict__ ssm_lo, const uint16_t* __restrict__ conv_lo, uint16_t* __restrict__ ssm_lo_out,
+    uint16_t* __restrict__ conv_lo_out) {
   constexpr int NMAX = 16;
   constexpr int W = 4;  // ring slots read at most
   const int nb = (d + kBlock - 1) / kBlock;
@@ -219,14 +233,32 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
   const int64_t slot = static_cast<int64_t>(Bs) * d;  // ring slot stride of x and dt
   const int64_t rc = static_cast<int64_t>(r) * d + c;
   float h[NMAX], cs[kKS], xs[W], ds[W], zv[W];
-  const float4* srow = reinterpret_cast<const float4*>(ssm_state + rc * NMAX);
+  if (LO) {  // the bf16 copy: two 16-byte loads of the state, one 8-byte load of the conv entries
+    const uint4* lrow = reinterpret_cast<const uint4*>(ssm_lo + rc * NMAX);
 #pragma unroll
-  for (int v = 0; v < NMAX / 4; ++v) {
-    const float4 t = srow[v];
-    h[4 * v] = t.x; h[4 * v + 1] = t.y; h[4 * v + 2] = t.z; h[4 * v + 3] = t.w;
+    for (int v = 0; v < NMAX / 8; ++v) {
+      const uint4 t = lrow[v];
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[8 * v + 2 * e] = __uint_as_float(w[e] << 16);
+        h[8 * v + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
+    const uint2 c2 = reinterpret_cast<const uint2*>(conv_lo)[rc];
+    cs[0] = __uint_as_float(c2.x << 16);
+    cs[1] = __uint_as_float(c2.x & 0xFFFF0000u);
+    cs[2] = __uint_as_float(c2.y << 16);
+  } else {
+    const float4* srow = reinterpret_cast<const float4*>(ssm_state + rc * NMAX);
+#pragma unroll
+    for (int v = 0; v < NMAX / 4; ++v) {
+      const float4 t = srow[v];
+      h[4 * v] = t.x; h[4 * v + 1] = t.y; h[4 * v + 2] = t.z; h[4 * v + 3] = t.w;
+    }
+#pragma unroll
+    for (int m = 0; m < kKS; ++m) cs[m] = conv_state[rc * kKS + m];
   }
-#pragma unroll
-  for (int m = 0; m < kKS; ++m) cs[m] = conv_state[rc * kKS + m];
 #pragma unroll
   for (int t = 0; t < W; ++t) {  // slots past k1 are not read
     xs[t] = (t <= k1) ? ld_io(x_ring, t * slot + rc) : 0.0f;
@@ -275,14 +307,55 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
       const float yp = (g[0] + g[1]) + (g[2] + g[3]);
       st_io(y, (t - k0) * ys + rc, __builtin_fmaf(Dc, u, yp) * silu(zv[t]));
     }
-    if (t == cstep) {  // the state after step t becomes the checkpoint
+    if (!LO && t == cstep) {  // the state after step t becomes the checkpoint
       float* so = ssm_state + rc * NMAX;
 #pragma unroll
       for (int n = 0; n < NMAX; ++n) nt_store(h[n], so + n);
 #pragma unroll
       for (int m = 0; m < kKS; ++m) conv_state[rc * kKS + m] = X(t - 2 + m);  // [X(t-2), X(t-1), X(t)]
+      if (ssm_lo_out != nullptr) {  // and its bf16 copy (uniform branch)
+        u32x4_lo* lo = reinterpret_cast<u32x4_lo*>(ssm_lo_out + rc * NMAX);
+#pragma unroll
+        for (int v = 0; v < NMAX / 8; ++v) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x2_lo pr = {h[8 * v + 2 * e], h[8 * v + 2 * e + 1]};
+            w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_lo));
+          }
+          nt_store(u32x4_lo{w[0], w[1], w[2], w[3]}, lo + v);
+        }
+        const f32x2_lo c01 = {X(t - 2), X(t - 1)}, c2z = {X(t), 0.0f};
+        nt_store(u32x2_lo{__builtin_bit_cast(uint32_t, __builtin_convertvector(c01, bf16x2_lo)),
+                          __builtin_bit_cast(uint32_t, __builtin_convertvector(c2z, bf16x2_lo))},
+                 reinterpret_cast<u32x2_lo*>(conv_lo_out) + rc);
+      }
     }
   }
+}
+
+// The bf16 copy of a replay checkpoint (rounded to nearest even): one thread per (row,
+// channel) converts its 16 state entries and 3 conv entries (entry 3 of conv_lo is zero).
+__global__ void __launch_bounds__(kBlock) k_checkpoint_lo(const float* __restrict__ conv_state,
+                                                         const float* __restrict__ ssm_state,
+                                                         uint16_t* __restrict__ conv_lo, uint16_t* __restrict__ ssm_lo,
+                                                         int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const float4* s4 = reinterpret_cast<const float4*>(ssm_state + i * 16);
+  uint4* o4 = reinterpret_cast<uint4*>(ssm_lo + i * 16);
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const float4 a = s4[2 * v], b = s4[2 * v + 1];
+    const f32x2_lo p0 = {a.x, a.y}, p1 = {a.z, a.w}, p2 = {b.x, b.y}, p3 = {b.z, b.w};
+    o4[v] = make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2_lo)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2_lo)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2_lo)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(p3, bf16x2_lo)));
+  }
+  const f32x2_lo c01 = {conv_state[i * kKS], conv_state[i * kKS + 1]}, c2z = {conv_state[i * kKS + 2], 0.0f};
+  reinterpret_cast<uint2*>(conv_lo)[i] = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(c01, bf16x2_lo)),
+                                                    __builtin_bit_cast(uint32_t, __builtin_convertvector(c2z, bf16x2_lo)));
 }
 
 }  // namespace mm

@@ -172,3 +172,106 @@ def test_speculative_accept_prefix_and_continue():
     R2 = _rings(toks[4:6] + toks[4:6], W, "bf16")  # slots 0, 1 hold the new tokens
     y2 = mm.decode_replay_multi(R2["x"], R2["dt"], R2["B"], R2["z"], R2["C"], *prm, csd, ssd, 0, 1, -1)
     assert np.array_equal(host(y2[0]), ye2[2]) and np.array_equal(host(y2[1]), ye2[3])
+
+
+# ---------------------------------------------------------------- dual-precision checkpoint
+
+
+def _run_dual(toks, p, cs, ss, W):
+    """Feed the steps through the dual-precision replay; returns per-step y, the fp32 and bf16
+    checkpoints after every committing step, and the checkpoint each window started from."""
+    Bs, d = toks[0]["x"].shape
+    N = toks[0]["B"].shape[1]
+    prm = [dev(p[k]) for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    csd, ssd = dev(cs), dev(ss)
+    clo, slo = mm.replay_checkpoint_lo(csd, ssd)
+    xr = torch.zeros((W, Bs, d), dtype=torch.bfloat16, device="cuda")
+    dr = torch.zeros_like(xr)
+    br = torch.zeros((W, Bs, N), dtype=torch.bfloat16, device="cuda")
+    ys, ckpts, starts = [], {}, {0: (cs, ss)}
+    k = 0
+    for s, t in enumerate(toks):
+        xr[k].copy_(dev(t["x"]))
+        dr[k].copy_(dev(t["dt"]))
+        br[k].copy_(dev(t["B"]))
+        y = mm.decode_replay_dual(xr, dr, br, dev(t["z"]), dev(t["C"]), *prm, csd, ssd, clo, slo, k)
+        ys.append(host(y))
+        if k == W - 1:
+            ckpts[s] = (host(csd), host(ssd), host(clo), host(slo))
+            starts[s + 1] = (host(csd), host(ssd))
+            k = 0
+        else:
+            k += 1
+    return ys, ckpts, starts
+
+
+@pytest.mark.parametrize("W", [2, 4])
+def test_replay_dual_precision(W):
+    """Steps that do not commit give the oracle's outputs from the bf16-rounded checkpoint (within
+    the bf16 tolerance); committing steps equal the eager decode bit for bit, output and state;
+    the bf16 copy written at a commit is the fp32 checkpoint rounded to nearest even (bit for
+    bit), with conv entry 3 zero."""
+    Bs, d, N = 6, 200, 16
+    steps = 2 * W + 1
+    toks, p, cs, ss = _stream(80 + W, steps, Bs, d, N, "bf16")
+    log(f"[replay-dual] W={W} Bs={Bs} d={d} steps={steps}")
+    yd, ck, starts = _run_dual(toks, p, cs, ss, W)
+    ye, st = _run_eager(toks, p, cs, ss, set(ck))
+    prm = [p[k] for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    for s in range(steps):
+        w0 = (s // W) * W
+        k = s - w0
+        if k == W - 1:
+            assert np.array_equal(yd[s], ye[s]), f"committing step {s}: y differs from the eager decode"
+            continue
+        cs0, ss0 = starts[w0]
+        ring = {q: np.stack([toks[w0 + i][q] for i in range(W) if w0 + i < steps]) for q in ("x", "dt", "B")}
+        yo, _, _ = oracle.decode_replay_lo(ring["x"], ring["dt"], ring["B"], k, toks[s]["z"], toks[s]["C"], *prm,
+                                           cs0, ss0)
+        assert_within(yd[s], yo, "bf16", f"dual step {s} (window step {k}) vs oracle from the rounded checkpoint")
+    for s, (c32, s32, clo, slo) in ck.items():
+        assert np.array_equal(c32, st[s][0]) and np.array_equal(s32, st[s][1]), f"checkpoint after step {s}"
+        want_s = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(s32.astype(np.float32))).reshape(s32.shape)
+        want_c = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(c32.astype(np.float32))).reshape(c32.shape)
+        assert np.array_equal(slo, want_s), "bf16 copy of the SSM state is not the rounded fp32 state"
+        assert np.array_equal(clo[..., :3], want_c) and np.all(clo[..., 3] == 0), "bf16 copy of the conv state"
+
+
+def test_replay_checkpoint_lo_rounds_to_nearest_even():
+    Bs, d, N = 5, 136, 16
+    rng = np.random.default_rng(3)
+    cs = rng.standard_normal((Bs, d, 3)).astype(np.float32)
+    ss = (rng.standard_normal((Bs, d, N)) * np.exp2(rng.integers(-10, 10, (Bs, d, N)))).astype(np.float32)
+    clo, slo = mm.replay_checkpoint_lo(dev(cs), dev(ss))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(slo), oracle.bf16_round(ss))
+    assert np.array_equal(host(clo)[..., :3], oracle.bf16_round(cs)) and np.all(host(clo)[..., 3] == 0)
+
+
+def test_replay_dual_7b_shape():
+    """Batch 256, d_inner 8192, one window of 4 and a step of the next: the committing step and its
+    state equal the eager decode; the other steps give the oracle's outputs from the bf16-rounded
+    checkpoint on sampled rows (within the bf16 tolerance), and stay within a normwise 1e-2 of the
+    exact replay on every row (the effect of rounding the state to 8 significant bits)."""
+    W, Bs, d, N = 4, 256, 8192, 16
+    steps = W + 1
+    toks, p, cs, ss = _stream(6, steps, Bs, d, N, "bf16")
+    log(f"[replay-dual] W={W} Bs={Bs} d={d} steps={steps}")
+    yd, ck, starts = _run_dual(toks, p, cs, ss, W)
+    ye, st = _run_eager(toks, p, cs, ss, {W - 1})
+    prm = [p[k] for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    rows = np.array([0, 1, 77, 128, 200, 255])
+    for s in range(steps):
+        if s == W - 1:
+            assert np.array_equal(yd[s], ye[s])
+            continue
+        w0 = (s // W) * W
+        k = s - w0
+        cs0, ss0 = starts[w0]
+        ring = {q: np.stack([toks[w0 + i][q][rows] for i in range(k + 1)]) for q in ("x", "dt", "B")}
+        yo, _, _ = oracle.decode_replay_lo(ring["x"], ring["dt"], ring["B"], k, toks[s]["z"][rows],
+                                           toks[s]["C"][rows], *prm, cs0[rows], ss0[rows])
+        assert_within(yd[s][rows], yo, "bf16", f"dual step {s} vs oracle from the rounded checkpoint")
+        norm = np.linalg.norm(yd[s].astype(np.float64) - ye[s]) / np.linalg.norm(ye[s].astype(np.float64))
+        assert norm < 1e-2, f"dual step {s}: normwise {norm:.3g} from the exact replay"
+    assert np.array_equal(ck[W - 1][1], st[W - 1][1]) and np.array_equal(ck[W - 1][0], st[W - 1][0])

@@ -367,3 +367,27 @@ def test_noalloc_prefill_rejects_plans_beyond_its_scratch(lib):
     assert lib.mamba_mixer_prefill_noalloc(*ptrs, S, T, d, 17, 4, 1, None) == MM_ERR_UNSUPPORTED
     # nothing to do: success without touching a device
     assert lib.mamba_mixer_prefill_noalloc(*ptrs, S, 0, d, N, 4, 1, None) == 0
+
+
+def test_replay_dual_host_checks(lib):
+    """The dual-precision replay and its copy helper reject bad arguments on the host."""
+    big = 0x100000000
+    p = [ctypes.c_void_p(0x1000000000 + i * big) for i in range(15)]
+    call = lambda ptrs, io=1, N=16, W=4, k=0: lib.mamba_mixer_decode_replay_dual(*ptrs, 2, 64, N, 4, io, W, k, 0, None)
+    assert call(p, io=0) == MM_ERR_UNSUPPORTED  # bf16 io only
+    assert call(p, N=8) == MM_ERR_UNSUPPORTED
+    assert call(p, k=4) == MM_ERR_DIM
+    q = list(p)
+    q[13] = None  # ssm_lo
+    assert call(q) == MM_ERR_NULL
+    q = list(p)
+    q[13] = ctypes.c_void_p(0x1000000000 + 13 * big + 8)  # ssm_lo not 16-byte aligned
+    assert call(q) == MM_ERR_ALIGN
+    q = list(p)
+    q[13] = q[11]  # ssm_lo on top of ssm_state
+    assert call(q) == MM_ERR_ALIAS
+    c = [ctypes.c_void_p(0x1000000000 + i * big) for i in range(4)]
+    assert lib.mamba_mixer_replay_checkpoint_lo(*c, 2, 64, 8, 4, None) == MM_ERR_UNSUPPORTED
+    assert lib.mamba_mixer_replay_checkpoint_lo(c[0], c[1], c[0], c[3], 2, 64, 16, 4, None) == MM_ERR_ALIAS
+    assert lib.mamba_mixer_replay_checkpoint_lo(c[0], c[1], c[2], None, 2, 64, 16, 4, None) == MM_ERR_NULL
+    assert lib.mamba_mixer_replay_checkpoint_lo(*c, 0, 64, 16, 4, None) == 0

@@ -506,3 +506,76 @@ def test_oracle_project_isolates_sequences():
     for k in ("u", "dt", "B", "C"):
         assert np.array_equal(o1[k][:6], o2[k][:6]) and np.array_equal(o1[k][11:], o2[k][11:]), k
         assert not np.array_equal(o1[k][6:11], o2[k][6:11]), k
+
+
+# --- dual-precision replay: the bf16 rounding of the checkpoint --------------------------------
+
+def _bf16_nearest_brute(f32):
+    """For float32 values, the nearest bfloat16 by enumeration of the two bracketing bf16
+    patterns (the float32 pattern with its low 16 bits cleared, and the next one), ties to the
+    candidate whose last kept bit is 0."""
+    bits = np.asarray(f32, dtype=np.float32).view(np.uint32)
+    lo = bits & np.uint32(0xFFFF0000)
+    hi = lo + np.uint32(0x10000)
+    out = np.empty(bits.shape, dtype=np.float64)
+    for i, (b, l, h) in enumerate(zip(bits.ravel(), lo.ravel(), hi.ravel())):
+        v = float(np.uint32(b).view(np.float32))
+        cands = [np.uint32(l), np.uint32(h)]
+        dist = [abs(float(c.view(np.float32)) - v) for c in cands]
+        if dist[0] < dist[1] or (dist[0] == dist[1] and (int(l) >> 16) % 2 == 0):
+            out.ravel()[i] = float(cands[0].view(np.float32))
+        else:
+            out.ravel()[i] = float(cands[1].view(np.float32))
+    return out
+
+
+def test_oracle_bf16_round_matches_enumeration():
+    """bf16_round against enumeration of the bracketing bf16 values: random values of both signs
+    over many binades, exact ties (low 16 bits 0x8000, rounding to the even neighbour either way)
+    and values that carry into the next power of two.  A truncation, ties away from zero or a
+    wrong significand width fails it."""
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal(4000) * np.exp2(rng.integers(-20, 20, 4000))).astype(np.float32)
+    ties = (rng.integers(0x3F800000, 0x40800000, 500, dtype=np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    carry = np.array([0x3FFF8000, 0x3FFFC000, 0x407FFFFF, 0xBF7FFFFF, 0x3F808000, 0x3F818000], dtype=np.uint32)
+    allv = np.concatenate([v, ties.view(np.float32), -ties.view(np.float32), carry.view(np.float32)])
+    got = oracle_bf16_round(allv)
+    want = _bf16_nearest_brute(allv)
+    assert np.array_equal(got, want)
+    # both tie directions occur
+    t = ties.view(np.float32).astype(np.float64)
+    r = oracle_bf16_round(t)
+    assert np.any(r > t) and np.any(r < t)
+
+
+def oracle_bf16_round(a):
+    import oracle
+
+    return oracle.bf16_round(a)
+
+
+def test_oracle_decode_replay_lo(oracle_lib):
+    """decode_replay_lo is decode_replay from the rounded checkpoint: identical outputs when the
+    checkpoint is already bf16-representable, and outputs that differ (by a small amount, at the
+    rounding's scale) when it is not."""
+    W, Bs, d, N = 4, 3, 24, 16
+    rng = np.random.default_rng(8)
+    p = inputs.params_per_channel(8, d, N, 4)
+    toks = [inputs.decode_inputs(8, s, Bs, d, N, "bf16") for s in range(W)]
+    ring = {k: np.stack([t[k] for t in toks]) for k in ("x", "dt", "B")}
+    cs = rng.standard_normal((Bs, d, 3))
+    ss = 0.5 * rng.standard_normal((Bs, d, N))
+    prm = [p[k] for k in ("A_log", "D", "dt_bias", "conv_w", "conv_b")]
+    csr, ssr = oracle_lib.bf16_round(cs), oracle_lib.bf16_round(ss)
+    for k in range(W):
+        ye, _, _ = oracle_lib.decode_replay(ring["x"], ring["dt"], ring["B"], k, toks[k]["z"], toks[k]["C"], *prm, cs, ss)
+        yl, _, _ = oracle_lib.decode_replay_lo(ring["x"], ring["dt"], ring["B"], k, toks[k]["z"], toks[k]["C"], *prm,
+                                               cs, ss)
+        yr, _, _ = oracle_lib.decode_replay(ring["x"], ring["dt"], ring["B"], k, toks[k]["z"], toks[k]["C"], *prm,
+                                            csr, ssr)
+        assert np.array_equal(yl, yr)
+        diff = np.max(np.abs(yl - ye)) / np.max(np.abs(ye))
+        assert 0 < diff < 2e-2, diff
+    yb, _, _ = oracle_lib.decode_replay_lo(ring["x"], ring["dt"], ring["B"], 2, toks[2]["z"], toks[2]["C"], *prm, csr, ssr)
+    yc, _, _ = oracle_lib.decode_replay(ring["x"], ring["dt"], ring["B"], 2, toks[2]["z"], toks[2]["C"], *prm, csr, ssr)
+    assert np.array_equal(yb, yc)
