@@ -121,7 +121,8 @@ PROFILE_DECODE = os.path.join(ROOT, "profiles", "k_decode_vec__m7b_decode_b256_d
 PROFILE_REPLAY = os.path.join(ROOT, "profiles", "k_decode_replay__m7b_decode_b256_d8192_N16_W4_bf16.txt")
 PROFILE_DUAL = os.path.join(ROOT, "profiles", "k_decode_replay_dual__m7b_decode_b256_d8192_N16_W4_bf16.txt")
 PROFILE_BACKWARD = os.path.join(ROOT, "profiles", "k_row_bwd__m130_backward_8x2048_d1536_N16_bf16.txt")
-PROFILE_PROJECT = os.path.join(ROOT, "profiles", "k_project__m130_project_8x2048_d1536_R48_N16_bf16.txt")
+PROFILE_PROJECT = {(k, sh): os.path.join(ROOT, "profiles", f"{k}__{sh}_project_8x2048_d{d}_R{r}_N16_bf16.txt")
+                   for k in ("k_proj_in", "k_proj_dt") for sh, d, r in (("m130", 1536, 48), ("m1p4b", 4096, 128))}
 
 
 def counted_traffic(profile_path):
@@ -574,13 +575,21 @@ def bench_backward(args):
 
 
 def project_alg_bytes(T, S, d, N, R):
-    """HBM bytes one k_project launch must move: x in, dt, B, C out (bf16), the re-laid weights,
-    the conv parameters, the initial conv state and cu_seqlens."""
+    """HBM bytes of the two projection kernels, each counted as its own launch.
+
+    k_proj_in: x in (bf16), B and C out, dt_in out as bf16 high and low parts [T][Rp], the re-laid
+    w_x, the conv parameters, the initial conv state and cu_seqlens.  k_proj_dt: dt out (bf16),
+    dt_in in, the re-laid w_dt.  "call" is the projection as one operation: x in, dt, B, C out,
+    the weights and conv parameters (dt_in stays between the kernels)."""
     P = R + 2 * N
     Pp = -(-P // 16) * 16
     dk = -(-d // 32) * 32
     Rp = -(-R // 32) * 32
-    return T * d * 2 * 2 + 2 * T * N * 2 + (Pp * dk + d * Rp) * 2 + d * 5 * 4 + S * d * 3 * 4 + (S + 1) * 4
+    params = d * 5 * 4 + S * d * 3 * 4 + (S + 1) * 4
+    dtin = 2 * T * Rp * 2
+    return dict(k_proj_in=T * d * 2 + 2 * T * N * 2 + dtin + Pp * dk * 2 + params,
+                k_proj_dt=T * d * 2 + dtin + d * Rp * 2,
+                call=2 * T * d * 2 + 2 * T * N * 2 + (d * P + R * d) * 2 + params)
 
 
 def bench_project(args, only_m130=False):
@@ -592,6 +601,7 @@ def bench_project(args, only_m130=False):
     from selective_state_space_causal_amd import inputs
 
     out = {}
+    names = ["k_proj_pack", "k_proj_in", "k_proj_dt"]
     shapes = (("m130", 8, 2048, 1536, 48), ("m1p4b", 8, 2048, 4096, 128))
     for name, S, L, d, R in shapes[:1] if only_m130 else shapes:
         N = 16
@@ -607,25 +617,33 @@ def bench_project(args, only_m130=False):
         dt = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
         Bo = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
         Co = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(max(int(mm.load().mamba_mixer_project_workspace_bytes(d, N, R)), 1), dtype=torch.uint8,
+        ws = torch.empty(max(int(mm.load().mamba_mixer_project_workspace_bytes(T, d, N, R)), 1), dtype=torch.uint8,
                          device="cuda")
         ms, kern = _time_calls(lambda ev: mm.project(x, cw, cb, cu, cs, w_x, w_dt, dt=dt, B=Bo, C=Co, workspace=ws,
-                                                     events=ev), 2, ["k_proj_pack", "k_project"], reps=20)
-        kp = kern["k_project"]
+                                                     events=ev), len(names), names, reps=20)
         alg = project_alg_bytes(T, S, d, N, R)
-        gbs = alg / (kp * 1e-3) / 1e9
+        roofs = {}
+        for k in ("k_proj_in", "k_proj_dt"):
+            gbs = alg[k] / (kern[k] * 1e-3) / 1e9
+            prof = PROFILE_PROJECT.get((k, name))
+            roofs[k] = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                            frac=round(gbs / HBM_PEAK_GBS, 4),
+                            traffic=counted_traffic(prof) if prof else None,
+                            kernel=k, kernel_ms=round(kern[k], 4), alg_bytes_per_launch=alg[k])
+        dom = max(("k_proj_in", "k_proj_dt"), key=lambda k: kern[k])
         flops = 2.0 * T * d * (R + 2 * N) + 2.0 * T * R * d
+        kms = kern["k_proj_in"] + kern["k_proj_dt"]
         out[name] = dict(
             workload=f"dt/B/C projections: {S} x {L} tokens, d_inner {d}, dt_rank {R}, d_state {N}, bf16",
             ms=round(ms, 4), kernels_ms={k: round(v, 4) for k, v in kern.items()},
             tokens_per_s=round(T / (ms * 1e-3), 1),
-            roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                          frac=round(gbs / HBM_PEAK_GBS, 4),
-                          traffic=counted_traffic(PROFILE_PROJECT) if name == "m130" else None,
-                          kernel="k_project", kernel_ms=round(kp, 4), alg_bytes_per_launch=alg,
-                          mfma_view=dict(achieved_TFLOPs=round(flops / (kp * 1e-3) / 1e12, 2), peak_TFLOPs=2500.0,
-                                         note="algorithmic bf16 FLOP (2 T d (R+2N) + 2 T R d); the kernel issues "
-                                              "twice that (high and low operand parts)")))
+            roofline=roofs[dom], kernel_rooflines=roofs,
+            call_hbm_view=dict(alg_bytes=alg["call"], achieved_GBs=round(alg["call"] / (kms * 1e-3) / 1e9, 1),
+                               note="the projection as one operation over the two projection kernels' time "
+                                    "(the weight re-layout excluded: it depends on the weights only)"),
+            mfma_view=dict(achieved_TFLOPs=round(flops / (kms * 1e-3) / 1e12, 2), peak_TFLOPs=2500.0,
+                           note="algorithmic bf16 FLOP (2 T d (R+2N) + 2 T R d) over both kernels' time; the "
+                                "kernels issue twice that (high and low operand parts)"))
         del x, dt, Bo, Co, ws, w_x, w_dt
     torch.cuda.empty_cache()
     return out
@@ -985,7 +1003,7 @@ def main():
         print(json.dumps(dict(diag, prefill={args.only_prefill: prefill_line(pf)})), flush=True)
         return
     if args.only_project:
-        print(json.dumps(dict(diag, project=bench_project(args, only_m130=True))), flush=True)
+        print(json.dumps(dict(diag, project=bench_project(args))), flush=True)
         return
     if args.only_backward:
         print(json.dumps(dict(diag, backward=bench_backward(args))), flush=True)

@@ -392,24 +392,25 @@ size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d);
  *   w_dt         [R, d]      bf16   w_dt_out
  *   dt           [T, d]      bf16   out, 16-byte aligned
  *   B, C         [T, N]      bf16   out
- *   workspace    mamba_mixer_project_workspace_bytes(d, N, R) bytes, 256-byte aligned (the
- *                weights re-laid for the matrix cores; contents on entry do not matter)
+ *   workspace    mamba_mixer_project_workspace_bytes(T, d, N, R) bytes, 256-byte aligned (the
+ *                weights re-laid for the matrix cores, and dt_in between the two products;
+ *                contents on entry do not matter)
  * Both products run on the matrix cores (bf16 MFMA, fp32 accumulation); the computed operands
  * u and dt_in enter as bf16 high + low parts, so the products have fp32-quality operands and
  * the outputs are rounded once, to bf16 (nearest even).
  * Limits: io MM_IO_BF16 only, d a multiple of 16, 1 <= R <= 256 (else MM_ERR_UNSUPPORTED).
  * T == 0 or d == 0 is a successful no-op.  Outputs overlapping an input or one another are
- * MM_ERR_ALIAS.  Two kernels are enqueued (weight re-layout, projection); events, n_events are
- * optional as in mamba_mixer_prefill_ex (n = 2: events[0] before the first kernel, events[1]
- * between them, events[2] after the second).
+ * MM_ERR_ALIAS.  Three kernels are enqueued (weight re-layout; u x w_x, which writes B, C and
+ * dt_in; dt_in x w_dt, which writes dt); events, n_events are optional as in
+ * mamba_mixer_prefill_ex (n = 3: events[i] before kernel i, events[3] after the last).
  */
 int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
                         const float* conv_state, const void* w_x, const void* w_dt, void* dt, void* B, void* C,
                         int32_t S, int64_t T, int32_t d, int32_t N, int32_t R, int32_t K, int32_t io_dtype,
                         void* workspace, size_t workspace_bytes, void* stream, void* const* events,
                         int32_t n_events);
-/* Workspace bytes of mamba_mixer_project (0 for invalid sizes).  Host only. */
-size_t mamba_mixer_project_workspace_bytes(int32_t d, int32_t N, int32_t R);
+/* Workspace bytes of mamba_mixer_project for T tokens (0 for invalid sizes).  Host only. */
+size_t mamba_mixer_project_workspace_bytes(int64_t T, int32_t d, int32_t N, int32_t R);
 /* Static text for a status code (never NULL).  Host only. */
 const char* mamba_mixer_status_string(int status);
 

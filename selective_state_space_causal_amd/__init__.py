@@ -81,7 +81,7 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_checkpoint_bytes.restype = sz
     lib.mamba_mixer_project.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, P, sz, P, P, i32]
     lib.mamba_mixer_project.restype = ctypes.c_int
-    lib.mamba_mixer_project_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.mamba_mixer_project_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.mamba_mixer_project_workspace_bytes.restype = sz
     lib.mamba_mixer_status_string.argtypes = [ctypes.c_int]
     lib.mamba_mixer_status_string.restype = ctypes.c_char_p
@@ -399,7 +399,7 @@ def project(x, conv_w, conv_b, cu_seqlens, conv_state, w_x, w_dt, dt=None, B=Non
     _check(B, (T, N), torch.bfloat16, "B")
     _check(C, (T, N), torch.bfloat16, "C")
     if workspace is None:  # (a caller-provided workspace is size-checked by the library)
-        need = int(load().mamba_mixer_project_workspace_bytes(d, N, R))
+        need = int(load().mamba_mixer_project_workspace_bytes(T, d, N, R))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     rc = load().mamba_mixer_project(
         _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(cu_seqlens), _ptr(conv_state), _ptr(w_x), _ptr(w_dt), _ptr(dt),

@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <initializer_list>
 #include <mutex>
+#include <utility>
 
 #include <stdint.h>
 #include <string.h>
@@ -552,12 +553,36 @@ int launch_backward(const BwdPlan& p, const BwdArgs& a, char* ws, hipStream_t st
 
 // ---------------------------------------------------------------- projections
 
+// the projection kernels for NT output column tiles (1 .. 18) and KR K steps of dt_in (1 .. 8)
+using KernIn = void (*)(const uint16_t*, const float*, const float*, const int32_t*, const float*, const uint16_t*,
+                        uint16_t*, uint16_t*, uint16_t*, uint16_t*, int, int64_t, int, int, int, int, int);
+using KernDt = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, int, int);
+template <int... I>
+KernIn proj_in_table(int nt, std::integer_sequence<int, I...>) {
+  static const KernIn t[] = {k_proj_in<I + 1>...};
+  return t[nt - 1];
+}
+template <int... I>
+KernDt proj_dt_table(int kr, std::integer_sequence<int, I...>) {
+  static const KernDt t[] = {k_proj_dt<I + 1>...};
+  return t[kr - 1];
+}
+KernIn proj_in_kernel(int nt) { return proj_in_table(nt, std::make_integer_sequence<int, kProjMaxP / 16>{}); }
+template <int... I>
+size_t proj_in_lds_table(int nt, std::integer_sequence<int, I...>) {
+  static const size_t t[] = {pin_lds_bytes_t<I + 1>()...};
+  return t[nt - 1];
+}
+size_t proj_in_lds(int nt) { return proj_in_lds_table(nt, std::make_integer_sequence<int, kProjMaxP / 16>{}); }
+KernDt proj_dt_kernel(int kr) { return proj_dt_table(kr, std::make_integer_sequence<int, kProjMaxR / kProjK>{}); }
+
 struct ProjPlan {
   int P, Pp, dk, Rp;
-  size_t off_wx, off_wdt, total;
+  size_t off_wx, off_wdt, off_dth, off_dtl, total;
 };
 
-void make_proj_plan(ProjPlan& p, int d, int N, int R) {
+// workspace: the re-laid w_x and w_dt, then dt_in's bf16 high and low parts [T][Rp]
+void make_proj_plan(ProjPlan& p, int64_t T, int d, int N, int R) {
   p.P = R + 2 * N;
   p.Pp = static_cast<int>(cdiv(p.P, 16) * 16);
   p.dk = static_cast<int>(cdiv(d, kProjK) * kProjK);
@@ -565,6 +590,8 @@ void make_proj_plan(ProjPlan& p, int d, int N, int R) {
   size_t off = 0;
   p.off_wx = off; off += align256(static_cast<size_t>(p.Pp) * p.dk * 2);
   p.off_wdt = off; off += align256(static_cast<size_t>(d) * p.Rp * 2);
+  p.off_dth = off; off += align256(static_cast<size_t>(T) * p.Rp * 2);
+  p.off_dtl = off; off += align256(static_cast<size_t>(T) * p.Rp * 2);
   p.total = off;
 }
 
@@ -625,7 +652,7 @@ const char* mamba_mixer_status_string(int status) {
   }
 }
 
-const char* mamba_mixer_version(void) { return "libmambamix 0.3 gfx950"; }
+const char* mamba_mixer_version(void) { return "libmambamix 0.4 gfx950"; }
 
 int mamba_mixer_prefill_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len,
                              int32_t engine, int64_t* chunk_len_out, int32_t* engine_out, size_t* workspace_out,
@@ -970,10 +997,11 @@ int mamba_mixer_prefill_backward(const void* x, const void* z, const void* dt, c
   return launch_backward<float>(p, a, ws, st, evs);
 }
 
-size_t mamba_mixer_project_workspace_bytes(int32_t d, int32_t N, int32_t R) {
-  if (d < 0 || N < 1 || N > MM_MAX_N || R < 1 || R > kProjMaxR) return 0;
+size_t mamba_mixer_project_workspace_bytes(int64_t T, int32_t d, int32_t N, int32_t R) {
+  if (T < 0 || T > INT32_MAX || d < 0 || N < 1 || N > MM_MAX_N || R < 1 || R > kProjMaxR) return 0;
+  if (d > 0 && static_cast<uint64_t>(T) > MM_MAX_ROWS_X_D / static_cast<uint64_t>(d)) return 0;
   ProjPlan p{};
-  make_proj_plan(p, d, N, R);
+  make_proj_plan(p, T, d, N, R);
   return p.total;
 }
 
@@ -1008,39 +1036,50 @@ int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b,
       if (overlap(out[i].p, out[i].n, out[k].p, out[k].n)) return MM_ERR_ALIAS;
   }
   ProjPlan p{};
-  make_proj_plan(p, d, N, R);
+  make_proj_plan(p, T, d, N, R);
   if (workspace == nullptr || workspace_bytes < p.total) return MM_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MM_ERR_ALIGN;
-  if (cdiv(T, kProjTokens) > INT32_MAX) return MM_ERR_DIM;
-  if (events != nullptr && n_events < 3) return MM_ERR_DIM;
+  const int ncb = static_cast<int>(cdiv(d, kPdtCh));
+  if (cdiv(T, kPinTok) > INT32_MAX) return MM_ERR_DIM;
+  if (events != nullptr && n_events < 4) return MM_ERR_DIM;
   StageEvents evs{events, n_events, 0};
   char* ws = static_cast<char*>(workspace);
-  uint16_t* wxT = reinterpret_cast<uint16_t*>(ws + p.off_wx);
-  uint16_t* wdtT = reinterpret_cast<uint16_t*>(ws + p.off_wdt);
+  uint16_t* wxP = reinterpret_cast<uint16_t*>(ws + p.off_wx);
+  uint16_t* wdtP = reinterpret_cast<uint16_t*>(ws + p.off_wdt);
+  uint16_t* dth = reinterpret_cast<uint16_t*>(ws + p.off_dth);
+  uint16_t* dtl = reinterpret_cast<uint16_t*>(ws + p.off_dtl);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t npack = static_cast<int64_t>(p.Pp) * p.dk + static_cast<int64_t>(d) * p.Rp;
+  const int64_t npack = static_cast<int64_t>(p.dk / 8) * p.Pp + static_cast<int64_t>(p.Rp / 8) * d;
   evs.mark(st);
   hipLaunchKernelGGL(k_proj_pack, dim3(static_cast<unsigned>(cdiv(npack, kBlock))), dim3(kBlock), 0, st,
-                     static_cast<const uint16_t*>(w_x), static_cast<const uint16_t*>(w_dt), wxT, wdtT, d,
+                     static_cast<const uint16_t*>(w_x), static_cast<const uint16_t*>(w_dt), wxP, wdtP, d,
                      static_cast<int>(P), p.Pp, p.dk, R, p.Rp);
-  const size_t lds = proj_lds_bytes(p.Pp, p.Rp);
   const int nt = p.Pp / 16;
   const int nkr = p.Rp / kProjK;
-  using KernP = void (*)(const uint16_t*, const float*, const float*, const int32_t*, const float*, const uint16_t*,
-                         const uint16_t*, uint16_t*, uint16_t*, uint16_t*, int, int64_t, int, int, int, int, int, int);
-  static const KernP table[3][3] = {{k_project<6, 2>, k_project<6, 4>, k_project<6, 8>},
-                                    {k_project<12, 2>, k_project<12, 4>, k_project<12, 8>},
-                                    {k_project<18, 2>, k_project<18, 4>, k_project<18, 8>}};
-  const KernP kern = table[nt <= 6 ? 0 : (nt <= 12 ? 1 : 2)][nkr <= 2 ? 0 : (nkr <= 4 ? 1 : 2)];
+  const KernIn kin = proj_in_kernel(nt);
+  const size_t lds = proj_in_lds(nt);
   if (lds > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kin), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds)) != hipSuccess)
     return MM_ERR_HIP;
   evs.mark(st);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(cdiv(T, kProjTokens))), dim3(kProjThreads), lds, st,
-                     static_cast<const uint16_t*>(x), conv_w, conv_b, cu_seqlens, conv_state, wxT, wdtT,
-                     static_cast<uint16_t*>(dt), static_cast<uint16_t*>(B), static_cast<uint16_t*>(C), S, T, d, N, R,
-                     p.dk, p.Rp, nt);
+  hipLaunchKernelGGL(kin, dim3(static_cast<unsigned>(cdiv(T, kPinTok))), dim3(kPinThreads), lds, st,
+                     static_cast<const uint16_t*>(x), conv_w, conv_b, cu_seqlens, conv_state, wxP, dth, dtl,
+                     static_cast<uint16_t*>(B), static_cast<uint16_t*>(C), S, T, d, N, R, p.Rp, p.dk / kProjK);
+  // dt: about kPdtWGs workgroups, each a 128-channel block and a run of 16-token tiles
+  const int64_t ntt = cdiv(T, 16);
+  const int64_t G = std::max<int64_t>(1, std::min<int64_t>(cdiv(kPdtWGs, ncb), cdiv(ntt, kPdtWaves)));
+  const int64_t per = cdiv(cdiv(ntt, G), kPdtWaves) * kPdtWaves;
+  const int64_t groups = cdiv(ntt, per);
+  const KernDt kdt = proj_dt_kernel(nkr);
+  const size_t ldt = pdt_lds_bytes(nkr);
+  if (ldt > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kdt), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(ldt)) != hipSuccess)
+    return MM_ERR_HIP;
+  evs.mark(st);
+  hipLaunchKernelGGL(kdt, dim3(static_cast<unsigned>(groups * ncb)), dim3(kPdtThreads), ldt, st, dth, dtl, wdtP,
+                     static_cast<uint16_t*>(dt), T, d, ncb, static_cast<int>(per));
   evs.mark(st);
   return hipGetLastError() == hipSuccess ? MM_OK : MM_ERR_HIP;
 }

@@ -15,25 +15,23 @@
 // column l % 16 of B, each with the 8 consecutive K indices 8 (l / 16) .. 8 (l / 16) + 7; the
 // result leaves rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16 in lane l.
 //
-// Memory access: the vector L1 looks up one cache line per 16-lane quarter of a wave and line,
-// so operand loads in the MFMA layout (16 lanes = 16 rows of a row-major matrix) cost 16
-// lookups per quarter.  Hence:
-//  * k_proj_pack re-lays the weights once per call in the operands' own order, w_x as
-//    [K step][K group][column][8] and w_dt as [K step][K group][channel][8], zero-padded to
-//    Pp = P rounded up to 16 columns, dk = d rounded up to 32, Rp = R rounded up to 32: a
-//    quarter wave then reads 256 contiguous bytes;
-//  * x and the conv parameters are read with row-contiguous loads into a per-wave LDS tile and
-//    taken from there in the operand layout.
-// k_project: a workgroup of 8 waves takes 32 tokens (two 16-token row tiles):
-//  1. wave w takes row tile w % 2 and the K quarter w / 2 of d: per K step of 32 channels it
-//     stages the x rows t-3 .. t of its 16 tokens and the 32 channels' conv parameters, each
-//     lane computes u for its token and 8 channels (rows before a sequence from the initial
-//     conv state), and the wave issues the MFMAs of all output columns.  Splitting K four ways
-//     gives four waves per SIMD at the 130m shape (a wave per 16 tokens alone would give one);
-//  2. the quarters' accumulators are summed through LDS in quarter order (deterministic); B and
-//     C leave from the sums, dt_in goes to LDS as bf16 high and low parts;
-//  3. the eight waves split dt's 16-channel tiles: A = dt_in from LDS (both row tiles), B =
-//     the re-laid w_dt.
+// The two products have opposite memory profiles, so each has a kernel of its own:
+//  * k_proj_in reads x (T d bf16, the layer's large input) and writes only R + 2N values per
+//    token: a read-streaming kernel.  A workgroup of four waves takes 16 tokens; wave w takes
+//    the K quarter w of d.  Per staging step a wave loads 128 channels of the 19 x rows its
+//    16 tokens need (t-3 .. t) with row-contiguous 16-byte loads, one step ahead of their use,
+//    into its own LDS tile; each lane then computes u for its token and 8 channels per MFMA K
+//    step and issues the MFMAs of all output columns.  The quarters' sums are added in
+//    quarter order through LDS (deterministic).  B and C go to their outputs, dt_in to the
+//    workspace as bf16 high and low parts [T][Rp] (zero past R).
+//  * k_proj_dt writes dt (T d bf16) from dt_in (T Rp, small): a write-streaming kernel with
+//    one workgroup per 64 tokens x 128 channels, far more workgroups than token tiles.  A wave
+//    takes 16 tokens x 128 channels (8 column tiles); its output tile goes through LDS so
+//    that it leaves as 16-byte row pieces.
+//  * k_proj_pack re-lays the weights once per call in the operands' own order (a quarter wave
+//    then reads 256 contiguous bytes): w_x as [K step][K group][column][8], w_dt as
+//    [K step][K group][channel][8], zero-padded to Pp = R + 2N rounded up to 16 columns,
+//    dk = d rounded up to 32 and Rp = R rounded up to 32.
 #pragma once
 
 #include <type_traits>
@@ -44,68 +42,76 @@ namespace mm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kProjTokens = 32;  // tokens per workgroup
-constexpr int kProjMaxP = 288;   // R + 2N, rounded up to 16
+constexpr int kProjMaxP = 288;  // R + 2N, rounded up to 16
 constexpr int kProjMaxR = 256;
-constexpr int kProjK = 32;       // K per MFMA
-constexpr int kProjWaves = 8;
-constexpr int kProjThreads = kProjWaves * kWave;
-constexpr int kProjRowTiles = kProjTokens / 16;          // 16-token row tiles per workgroup
-constexpr int kProjKSplit = kProjWaves / kProjRowTiles;  // K quarters
-constexpr int kProjXRows = 16 + kKS;                     // staged x rows per wave: t-3 .. t+15
-constexpr int kProjXStride = kProjK + 8;                 // bf16 per staged row (padded)
+constexpr int kProjK = 32;      // K per MFMA
+
+// k_proj_in
+constexpr int kPinRT = 4;                      // 16-token row tiles per workgroup
+constexpr int kPinTok = 16 * kPinRT;           // tokens per workgroup
+constexpr int kPinHalves = 2;                  // K halves
+constexpr int kPinWaves = kPinRT * kPinHalves;
+constexpr int kPinThreads = kPinWaves * kWave;
+constexpr int kPinXRows = kPinTok + kKS;       // staged x rows: t-3 .. t+63
+
+// Stage geometry of k_proj_in for NT output column tiles.  A stage holds KC channels (64, so that
+// every x row piece is a whole 128-byte line; 32 for the widest outputs, whose w_x operands
+// would not fit twice in LDS otherwise) for each K half: x [kPinXRows][KC + 8] bf16, the conv
+// weights [KC] float4 and biases [KC] float of those channels, then the KC / 32 MFMA K steps'
+// w_x operands [K step][4 K groups][Pp][8] bf16.
+template <int NT>
+struct PinGeo {
+  static constexpr int Pp = NT * 16;
+  static constexpr int KC = NT <= 12 ? 64 : 32;
+  static constexpr int SUB = KC / kProjK;                  // MFMA K steps per stage
+  static constexpr int XSTRIDE = KC + 8;                   // bf16 per staged x row
+  static constexpr int XP = kPinXRows * KC / 8;            // 16-byte pieces per half: x,
+  static constexpr int CWP = KC;                           // conv weights,
+  static constexpr int CBP = KC / 4;                       // biases,
+  static constexpr int WP = SUB * 4 * Pp;                  // w_x operands
+  static constexpr int HP = XP + CWP + CBP + WP;
+  static constexpr int CWOFF = kPinXRows * XSTRIDE * 2;    // byte offsets within a half
+  static constexpr int CBOFF = CWOFF + KC * 16;
+  static constexpr int WOFF = CBOFF + KC * 4;
+  static constexpr int HB = WOFF + WP * 16;                // bytes per half
+  static constexpr int L = (kPinHalves * HP + kPinThreads - 1) / kPinThreads;  // loads per thread and stage
+  static constexpr int D = NT <= 6 ? 4 : 1;                // stages in flight (1 or 4)
+};
+template <int NT>
+inline size_t pin_lds_bytes_t() {  // two stage buffers (+ a dummy slot); the halves' sums reuse them
+  const size_t stage = static_cast<size_t>(2) * kPinHalves * PinGeo<NT>::HB + 16;
+  const size_t red = static_cast<size_t>(kPinRT) * NT * kWave * 16;
+  return stage > red ? stage : red;
+}
+
+// k_proj_dt
+constexpr int kPdtWaves = 4;
+constexpr int kPdtThreads = kPdtWaves * kWave;
+constexpr int kPdtCh = 128;                // channels per workgroup (8 column tiles)
+constexpr int kPdtTiles = kPdtCh / 16;
+constexpr int kPdtOStride = kPdtCh + 8;    // bf16 per row of a wave's output tile (272 bytes)
+constexpr int kPdtWGs = 768;               // about three workgroups per CU
+inline size_t pdt_lds_bytes(int KR) {      // the block's w_dt operands, then per wave an output tile
+  return static_cast<size_t>(KR) * 4 * kPdtCh * 16 + static_cast<size_t>(kPdtWaves) * 16 * kPdtOStride * 2;
+}
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) {
   const __bf16 b = static_cast<__bf16>(v);
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// wxP[ks][g][j][e] = w_x[32 ks + 8 g + e][j] (zero past P and past d);
-// wdtP[kk][g][c][e] = w_dt[32 kk + 8 g + e][c] (zero past R)
-__global__ void __launch_bounds__(kBlock) k_proj_pack(const uint16_t* __restrict__ w_x,
-                                                      const uint16_t* __restrict__ w_dt, uint16_t* __restrict__ wxP,
-                                                      uint16_t* __restrict__ wdtP, int d, int P, int Pp, int dk, int R,
-                                                      int Rp) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  const int64_t nx = static_cast<int64_t>(Pp) * dk;
-  if (i < nx) {
-    const int e = static_cast<int>(i & 7);
-    const int64_t q = i >> 3;  // (ks * 4 + g) * Pp + j
-    const int j = static_cast<int>(q % Pp);
-    const int k = static_cast<int>(q / Pp) * 8 + e;
-    wxP[i] = (j < P && k < d) ? w_x[static_cast<int64_t>(k) * P + j] : static_cast<uint16_t>(0);
-    return;
-  }
-  const int64_t i2 = i - nx;
-  if (i2 >= static_cast<int64_t>(d) * Rp) return;
-  const int e = static_cast<int>(i2 & 7);
-  const int64_t q = i2 >> 3;  // (kk * 4 + g) * d + c
-  const int c = static_cast<int>(q % d);
-  const int r = static_cast<int>(q / d) * 8 + e;
-  wdtP[i2] = r < R ? w_dt[static_cast<int64_t>(r) * d + c] : static_cast<uint16_t>(0);
+// every lane of a 16-lane row reads lane I of the row (DPP row_newbcast:I); float in, float out
+template <int I>
+__device__ __forceinline__ float pj_bcast(float v) {
+  return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + I, 0xF, 0xF, true);
 }
-
-// LDS (dynamic, sized per call): a first region that holds, in turn, per wave two staging
-// buffers (double-buffered across K steps), each the x rows [kProjXRows][kProjXStride] bf16 and
-// conv parameters [40] float4 (32 channels' weights, then 8 x 4 biases); the K quarters' partial
-// accumulators [row tile][quarter 1..3][Pp / 16][64 lanes] floatx4; and per wave the dt output
-// tile.  After it, dt_in's high and low bf16 parts [kProjTokens][Rp + 8] (rows padded to keep
-// the 16-byte reads aligned).
-constexpr int kProjOStride = 32 + 8;  // bf16 per row of a wave's dt output tile [32 tokens][32 channels]
-constexpr size_t kProjStageBytes = kProjXRows * kProjXStride * 2 + 40 * 16;  // one staging buffer
-constexpr size_t kProjWaveBytes = (2 * kProjStageBytes > kProjTokens * kProjOStride * 2)
-                                      ? 2 * kProjStageBytes
-                                      : kProjTokens * kProjOStride * 2;
-__host__ __device__ inline size_t proj_red_bytes(int Pp) {
-  return static_cast<size_t>(kProjRowTiles) * (kProjKSplit - 1) * (Pp / 16) * kWave * 16;
-}
-__host__ __device__ inline size_t proj_region_bytes(int Pp) {
-  const size_t a = kProjWaves * kProjWaveBytes, b = proj_red_bytes(Pp);
-  return a > b ? a : b;
-}
-inline size_t proj_lds_bytes(int Pp, int Rp) {
-  return proj_region_bytes(Pp) + static_cast<size_t>(2) * kProjTokens * (Rp + 8) * 2;
+// lane j of a row reads lane j - K (row_shr:K) or j + K (row_shl:K, CTRL 0x100); lanes with no
+// such lane in the row get 0
+template <int CTRL>
+__device__ __forceinline__ uint32_t pj_shift(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
 }
 
 // split v into bf16 parts with hi + lo = v to about 2^-16 relative
@@ -114,276 +120,385 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
   lo = static_cast<__bf16>(v - static_cast<float>(hi));
 }
 
-// NT = Pp / 16 output column tiles of the first product, at most MAXNT (6, 12 or 18: the
-// accumulators of MAXNT tiles stay in registers); Rp / 32 K steps of the second, at most MAXKR
-// (2, 4 or 8: the w_dt operands of a tile pair stay in registers)
-template <int MAXNT, int MAXKR>
-__global__ void __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(MAXNT <= 6 ? 4 : (MAXNT <= 12 ? 3 : 2)))) k_project(
+// One thread per 8-element output piece:
+//   wxP[q][j][e] = w_x[8 q + e][j]   (q < dk / 8, j < Pp; zero past P and past d)
+//   wdtP[q][c][e] = w_dt[8 q + e][c] (q < Rp / 8, c < d;  zero past R)
+// Consecutive threads take consecutive j (or c): their reads of one row are contiguous and
+// their 16-byte writes follow one another.
+__global__ void __launch_bounds__(kBlock) k_proj_pack(const uint16_t* __restrict__ w_x,
+                                                      const uint16_t* __restrict__ w_dt, uint16_t* __restrict__ wxP,
+                                                      uint16_t* __restrict__ wdtP, int d, int P, int Pp, int dk, int R,
+                                                      int Rp) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t nx = static_cast<int64_t>(dk / 8) * Pp;
+  uint16_t v[8];
+  if (i < nx) {
+    const int q = static_cast<int>(i / Pp), j = static_cast<int>(i % Pp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 8 * q + e;
+      v[e] = (j < P && k < d) ? w_x[static_cast<int64_t>(k) * P + j] : static_cast<uint16_t>(0);
+    }
+    *reinterpret_cast<uint4*>(wxP + i * 8) = *reinterpret_cast<const uint4*>(v);
+    return;
+  }
+  const int64_t i2 = i - nx;
+  if (i2 >= static_cast<int64_t>(Rp / 8) * d) return;
+  const int q = static_cast<int>(i2 / d), c = static_cast<int>(i2 % d);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 8 * q + e;
+    v[e] = r < R ? w_dt[static_cast<int64_t>(r) * d + c] : static_cast<uint16_t>(0);
+  }
+  *reinterpret_cast<uint4*>(wdtP + i2 * 8) = *reinterpret_cast<const uint4*>(v);
+}
+
+// [dt_in | B | C] = u x w_x for 64 tokens per workgroup, NT = Pp / 16 output column tiles (a
+// template argument: the MFMAs run without guards); nks = dk / 32 MFMA K steps, grouped in
+// stages of G::SUB.  Wave w takes row tile w % 4 and K half w / 4 (the first half of the
+// stages, then the rest).  Stage g holds, for each half, everything its g-th stage needs (see
+// PinGeo); the four waves of a half share its w_x operands.  The 512 threads load stage g + D
+// into registers while stage g runs; those are the only global loads of the loop (bar the
+// conv state of a sequence's first tokens), so waiting for stage g, which was issued first,
+// never waits for a later one.  Two LDS stage buffers and one barrier per stage.  LDS
+// (dynamic): the stage buffers; after the K loop, the second half's accumulators
+// [row tile][NT][64 lanes] floatx4.
+template <int NT>
+__global__ void __launch_bounds__(kPinThreads) k_proj_in(
     const uint16_t* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     const int32_t* __restrict__ cu, const float* __restrict__ conv_state, const uint16_t* __restrict__ wxP,
-    const uint16_t* __restrict__ wdtP, uint16_t* __restrict__ dt, uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    int S, int64_t T, int d, int N, int R, int dk, int Rp, int NT) {
-  constexpr int kMaxNT = MAXNT;
+    uint16_t* __restrict__ dth, uint16_t* __restrict__ dtl, uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    int S, int64_t T, int d, int N, int R, int Rp, int nks) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int Pp = NT * 16;
-  const int dstride = Rp + 8;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);  // wave-uniform
-  auto xt = [&](int b) {  // staged x rows of buffer b, [kProjXRows][kProjXStride]
-    return reinterpret_cast<uint16_t*>(smem + w * kProjWaveBytes + b * kProjStageBytes);
-  };
-  auto cpar = [&](int b) {  // conv parameters of buffer b, [40]
-    return reinterpret_cast<float4*>(smem + w * kProjWaveBytes + b * kProjStageBytes + kProjXRows * kProjXStride * 2);
-  };
-  floatx4_t* red = reinterpret_cast<floatx4_t*>(smem);  // over the staging buffers, after the K loops
-  uint16_t* dh = reinterpret_cast<uint16_t*>(smem + proj_region_bytes(Pp));
-  uint16_t* dl = dh + static_cast<size_t>(kProjTokens) * dstride;
-  const int mt = w % kProjRowTiles;  // row tile
-  const int kq = w / kProjRowTiles;  // K quarter
-  const int row = lane & 15;  // token row within the tile (A operand), column within a tile (B operand)
+  using G = PinGeo<NT>;
+  constexpr int Pp = G::Pp, HB = G::HB, HP = G::HP, L = G::L, D = G::D, SUB = G::SUB, KC = G::KC;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const int rt = w % kPinRT, h = w / kPinRT;
+  const int row = lane & 15;  // token row of the tile (A operand) / column within a tile (B operand)
   const int kg = lane >> 4;   // 8-wide K group
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kProjTokens;
-  const int64_t tw = t0 + mt * 16;  // the wave's first token
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPinTok;
   const int64_t d64 = d;
+  const int nstg = (nks + SUB - 1) / SUB;
+  const int len0 = nstg / 2;
+  const int nst = nstg - len0;  // loop stages (the second half's; the first has len0 <= nst)
+  const int sbeg = h == 0 ? 0 : len0, slen = h == 0 ? len0 : nst;
 
-  // this lane's token and its sequence
-  int64_t t = tw + row;
-  if (t >= T) t = T - 1;  // rows past T compute on a valid token and store nothing
+  // this lane's token and its sequence (rows past T compute on a valid token and store nothing)
+  int64_t t = t0 + rt * 16 + row;
+  if (t >= T) t = T - 1;
   const int s = seq_of(cu, S, t);
   const int64_t back = t - cu[s];  // tokens of the sequence before t
   const float* cs = conv_state + static_cast<int64_t>(s) * d64 * kKS;
 
-  floatx4_t acc[kMaxNT];
+  // The staging pieces of thread i are q = i + 512 k (k < L): half q / HP, and within it piece
+  // p = q % HP: the x pieces (staged row p / (KC/8) = token t0 - 3 + p / (KC/8) clamped into
+  // 0 .. T-1, channels 8 (p % (KC/8)) .. of the stage), KC conv weight rows (float4), KC / 4
+  // pieces of four biases, and the stage's w_x operand pieces (contiguous).  Channels past d
+  // read clamped, valid addresses (their u is forced to 0); pieces past both halves load a
+  // valid address and go to a dummy slot.
+  const unsigned char* pbase[L];
+  int pstep[L], pch[L], pmax[L], pdst[L];
+  unsigned char kinds = 0;   // bit k: a channel-clamped piece (x or conv), else a w_x piece
+  unsigned char halves = 0;  // bit k: a piece of the second half
 #pragma unroll
-  for (int j = 0; j < kMaxNT; ++j) acc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < L; ++k) {
+    const int q = tid + kPinThreads * k;
+    const bool real = q < kPinHalves * HP;
+    const int hh = real ? q / HP : 0;
+    const int p = real ? q % HP : G::XP + G::CWP + G::CBP;  // a w_x piece
+    const int kb = (hh == 0 ? 0 : len0) * KC;  // the half's first channel
+    halves |= hh << k;
+    pdst[k] = hh * HB;
+    if (p < G::XP) {
+      int64_t tok = t0 - kKS + p / (KC / 8);
+      tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
+      pbase[k] = reinterpret_cast<const unsigned char*>(x + tok * d64);
+      pch[k] = kb + 8 * (p % (KC / 8));  // first channel of the piece in the half's first stage
+      pmax[k] = d - 8;
+      pstep[k] = 2;                       // bytes per channel
+      pdst[k] += (p / (KC / 8)) * G::XSTRIDE * 2 + (p % (KC / 8)) * 16;
+      kinds |= 1 << k;
+    } else if (p < G::XP + G::CWP) {
+      pbase[k] = reinterpret_cast<const unsigned char*>(conv_w);
+      pch[k] = kb + (p - G::XP);
+      pmax[k] = d - 1;
+      pstep[k] = 16;
+      pdst[k] += G::CWOFF + (p - G::XP) * 16;
+      kinds |= 1 << k;
+    } else if (p < G::XP + G::CWP + G::CBP) {
+      pbase[k] = reinterpret_cast<const unsigned char*>(conv_b);
+      pch[k] = kb + 4 * (p - G::XP - G::CWP);
+      pmax[k] = d - 4;
+      pstep[k] = 4;
+      pdst[k] += G::CBOFF + (p - G::XP - G::CWP) * 16;
+      kinds |= 1 << k;
+    } else {  // w_x: a stage's operands are SUB * 4 Pp contiguous pieces
+      const int pw = p - G::XP - G::CWP - G::CBP;
+      pbase[k] = reinterpret_cast<const unsigned char*>(wxP);
+      pch[k] = kb / kProjK * 4 * Pp + pw;  // piece index in the half's first stage
+      pmax[k] = nks * 4 * Pp - 1;          // the last operand piece
+      pstep[k] = 16;
+      pdst[k] += G::WOFF + pw * 16;
+    }
+    if (!real) pdst[k] = -1;  // staged nowhere
+  }
+  // stage g of a half of len stages (clamped to its last stage)
+  auto rel_stage = [&](int g, int len) { return len > 0 ? (g < len ? g : len - 1) : 0; };
+  auto load_stage = [&](int g, u32x4_t (&pf)[L]) {
+    const int r0 = rel_stage(g, len0), r1 = rel_stage(g, nst);
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+      const int rel = (halves >> k) & 1 ? r1 : r0;
+      const int adv = (kinds >> k) & 1 ? rel * KC : rel * SUB * 4 * Pp;  // channels, or operand pieces
+      const int o = pch[k] + adv;
+      pf[k] = *reinterpret_cast<const u32x4_t*>(pbase[k] + static_cast<int64_t>(o <= pmax[k] ? o : pmax[k]) * pstep[k]);
+    }
+  };
+  // (pieces past both halves go to a 16-byte slot after the two stage buffers: no branch, so the
+  // compiler's count of outstanding loads stays exact)
+  unsigned char* dummy = smem + 2 * kPinHalves * HB;
+  auto write_stage = [&](unsigned char* buf, const u32x4_t (&pf)[L]) {
+#pragma unroll
+    for (int k = 0; k < L; ++k) *reinterpret_cast<u32x4_t*>(pdst[k] >= 0 ? buf + pdst[k] : dummy) = pf[k];
+  };
 
-  // this lane's staging loads: 16 bytes (part lane % 4) of staged row lane / 4, and of row
-  // 16 + lane / 4 for lanes < 12; the conv parameters for lanes < 40
-  const int q4 = lane & 3;
-  auto xsrc = [&](int rr) {  // staged row rr holds token tw - 3 + rr (clamped into 0 .. T-1)
-    int64_t tok = tw - kKS + rr;
-    tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
-    return x + tok * d64 + q4 * 8;
-  };
-  const uint16_t* xa = xsrc(lane >> 2);
-  const uint16_t* xb = xsrc(16 + ((lane >> 2) < kKS ? (lane >> 2) : 0));
+  floatx4_t acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nks = dk / kProjK;
-  const int ks0 = kq * nks / kProjKSplit, ks1 = (kq + 1) * nks / kProjKSplit;
-  // A wave holding one of a sequence's first three tokens takes the loop that reads the conv
-  // state; every other wave runs the loop without that branch.
-  // the staging loads of K step ks: x rows and conv parameters (channels past d read valid
-  // ones; their u is 0), issued one step ahead of their use
-  uint4 pva, pvb;  // prefetched staging data
-  float4 pvp;
-  auto step_load = [&](int ks) {
-    const int c0 = ks * kProjK;
-    const int cx = c0 + q4 * 8 < d ? c0 : d - 8 - q4 * 8;
-    pva = *reinterpret_cast<const uint4*>(xa + cx);
-    pvb = *reinterpret_cast<const uint4*>(xb + cx);
-    const int pc = lane < kProjK ? c0 + lane : c0 + (lane - kProjK) * 4;  // weight channel, or first bias
-    const float* psrc = lane < kProjK ? conv_w + static_cast<int64_t>(pc < d ? pc : d - 1) * kK
-                                      : conv_b + (pc < d ? pc : d - 4);
-    pvp = *reinterpret_cast<const float4*>(psrc);
-  };
-  auto stage_write = [&](int b) {
-    *reinterpret_cast<uint4*>(xt(b) + (lane >> 2) * kProjXStride + q4 * 8) = pva;
-    if (lane < 4 * kKS) *reinterpret_cast<uint4*>(xt(b) + (16 + (lane >> 2)) * kProjXStride + q4 * 8) = pvb;
-    if (lane < 40) cpar(b)[lane] = pvp;
-  };
-  // Per K step: the staging buffer of step ks was written at the end of the previous step (its
-  // global loads issued a step before that), so neither the loads nor the LDS round trip stall
-  // the step's arithmetic.
-  auto kloop = [&](auto state) {
+  // MFMA K step ks, the sub-th of the stage in buf (this wave's half)
+  auto kstep = [&](const unsigned char* buf, int ks, int sub, auto state) {
     constexpr bool STATE = decltype(state)::value;
-    step_load(ks0 < ks1 ? ks0 : 0);
-    stage_write(0);
-    step_load(ks0 + 1 < ks1 ? ks0 + 1 : ks0);
-    for (int ks = ks0; ks < ks1; ++ks) {
-      const int c0 = ks * kProjK;
-      const int b = (ks - ks0) & 1;
-      // this step's w_x operands, used after the u arithmetic
-      uint4 wb[kMaxNT];
-      const uint16_t* wk = wxP + (static_cast<int64_t>(ks * 4 + kg) * Pp + row) * 8;
+    const unsigned char* hb = buf + h * HB;
+    const int c = ks * kProjK + kg * 8;
+    const bool live = c < d;
+    // x of tokens t-3 .. t: four row reads (the LDS has room to spare; the VALU has none)
+    const int xo = sub * kProjK * 2 + kg * 16;
+    float xr[4][8];
 #pragma unroll
-      for (int j = 0; j < kMaxNT; ++j)
-        if (j < NT) wb[j] = *reinterpret_cast<const uint4*>(wk + j * 16 * 8);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging writes before its reads
-      const int c = c0 + kg * 8;
-      const bool live = c < d;
-      float xr[4][8];
+    for (int r = 0; r < 4; ++r) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(hb + (rt * 16 + row + r) * G::XSTRIDE * 2 + xo);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xt(b) + (row + r) * kProjXStride + kg * 8);
-        const uint32_t pv[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 4; ++e) {
+        xr[r][2 * e] = __uint_as_float(v[e] << 16);
+        xr[r][2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+      }
+    }
+    if (STATE && back < kKS && live) {  // rows before the sequence: its initial conv state
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xr[r][2 * e] = __uint_as_float(pv[e] << 16);
-          xr[r][2 * e + 1] = __uint_as_float(pv[e] & 0xFFFF0000u);
+      for (int r = 0; r < kKS; ++r) {
+        if (back - (kKS - r) < 0) {
+          const int64_t col = back + r;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xr[r][e] = cs[static_cast<int64_t>(c + e) * kKS + col];
         }
       }
-      if (STATE && back < kKS && live) {  // older rows from the initial conv state, or 0 before it
+    }
+    // the conv parameters of the lane's 8 channels (the 16 lanes of a K group read the same ones)
+    const float4* cwp = reinterpret_cast<const float4*>(hb + G::CWOFF) + sub * kProjK + kg * 8;
+    const float4* cbp = reinterpret_cast<const float4*>(hb + G::CBOFF + (sub * kProjK + kg * 8) * 4);
+    const float4 b0 = cbp[0], b1 = cbp[1];
+    const float bias[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    bf16x8_t ua, ul;  // u's high and low parts
+    auto conv_e = [&](auto ec) {
+      constexpr int e = decltype(ec)::value;
+      const float4 wv = cwp[e];
+      float xc = bias[e];
+      xc = __builtin_fmaf(wv.x, xr[0][e], xc);
+      xc = __builtin_fmaf(wv.y, xr[1][e], xc);
+      xc = __builtin_fmaf(wv.z, xr[2][e], xc);
+      xc = __builtin_fmaf(wv.w, xr[3][e], xc);
+      const float uv = silu(xc);  // computed for every lane (no branch), then zeroed past d
+      __bf16 hi, lo;
+      split_bf16(live ? uv : 0.0f, hi, lo);
+      ua[e] = hi;
+      ul[e] = lo;
+    };
+    conv_e(std::integral_constant<int, 0>{});
+    conv_e(std::integral_constant<int, 1>{});
+    conv_e(std::integral_constant<int, 2>{});
+    conv_e(std::integral_constant<int, 3>{});
+    conv_e(std::integral_constant<int, 4>{});
+    conv_e(std::integral_constant<int, 5>{});
+    conv_e(std::integral_constant<int, 6>{});
+    conv_e(std::integral_constant<int, 7>{});
+    const u32x4_t* wo = reinterpret_cast<const u32x4_t*>(hb + G::WOFF) + (sub * 4 + kg) * Pp + row;
+    u32x4_t wb[NT];
 #pragma unroll
-        for (int r = 0; r < kKS; ++r) {
-          const int64_t col = back - (3 - r) + kKS;
-          if (back - (3 - r) < 0) {
+    for (int j = 0; j < NT; ++j) wb[j] = wo[j * 16];
+    // the high parts over all column tiles, then the low parts: consecutive MFMAs are independent
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xr[r][e] = col >= 0 ? cs[static_cast<int64_t>(c + e) * kKS + col] : 0.0f;
-          }
+    for (int j = 0; j < NT; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
+  };
+
+  // A wave holding one of a sequence's first three tokens takes the loop that reads the conv state.
+  // The D register sets are written out one after another (not a loop the compiler may roll
+  // back up: rotating registers that still wait for loads would wait for them at once).
+  auto kloop = [&](auto state) {
+    u32x4_t pf[D][L];
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_stage(u, pf[u]);
+    // (stages past the last one repeat it without computing: the loads, writes and barriers stay
+    // unconditional and in a fixed order)
+    auto stage = [&](int g0, auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const int g = g0 + u;
+      unsigned char* buf = smem + (g & 1) * (kPinHalves * HB);
+      write_stage(buf, pf[u]);  // waits for stage g's loads only (the earliest outstanding)
+      load_stage(g + D, pf[u]);  // near the end a harmless repeat (clamped)
+      __syncthreads();  // stage g visible; every wave done with stage g - 1 (the other buffer)
+      if (g < slen) {
+#pragma unroll
+        for (int sub = 0; sub < SUB; ++sub) {
+          const int ks = (sbeg + g) * SUB + sub;
+          if (ks < nks) kstep(buf, ks, sub, state);
         }
       }
-      const float4 b0 = cpar(b)[kProjK + kg * 2], b1 = cpar(b)[kProjK + kg * 2 + 1];
-      const float bias[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      bf16x8_t ua, ul;  // u's high and low parts
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float4 wv = cpar(b)[kg * 8 + e];
-        float xc = bias[e];
-        xc = __builtin_fmaf(wv.x, xr[0][e], xc);
-        xc = __builtin_fmaf(wv.y, xr[1][e], xc);
-        xc = __builtin_fmaf(wv.z, xr[2][e], xc);
-        xc = __builtin_fmaf(wv.w, xr[3][e], xc);
-        __bf16 hi, lo;
-        split_bf16(live ? silu(xc) : 0.0f, hi, lo);
-        ua[e] = hi;
-        ul[e] = lo;
+    };
+    for (int g0 = 0; g0 < nst; g0 += D) {
+      stage(g0, std::integral_constant<int, 0>{});
+      if constexpr (D > 1) stage(g0, std::integral_constant<int, 1>{});
+      if constexpr (D > 2) {
+        stage(g0, std::integral_constant<int, 2>{});
+        stage(g0, std::integral_constant<int, 3>{});
       }
-      // the high parts over all column tiles, then the low parts: consecutive MFMAs are independent
-#pragma unroll
-      for (int j = 0; j < kMaxNT; ++j)
-        if (j < NT) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < kMaxNT; ++j)
-        if (j < NT) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
-      if (ks + 1 < ks1) stage_write(b ^ 1);  // step ks + 1; that buffer was last read in step ks - 1
-      step_load(ks + 2 < ks1 ? ks + 2 : ks);  // near the end a harmless repeat
     }
   };
   if (__any(back < kKS)) kloop(std::true_type{});
   else kloop(std::false_type{});
 
-  // sum the K quarters in order: quarters 1..3 leave their accumulators in LDS, quarter 0 adds
-  // them (fully unrolled loops with guards: a loop the compiler cannot unroll would index acc at
-  // run time and move it to scratch memory)
-  auto red_at = [&](int q, int j) {
-    return red + ((static_cast<size_t>(mt) * (kProjKSplit - 1) + (q - 1)) * NT + j) * kWave + lane;
-  };
-  __syncthreads();  // every wave's K loop done: the staging buffers become the partial sums
-  if (kq > 0) {
+  // the halves' sums: the second half leaves its accumulators in LDS, the first adds them in
+  // (first + second) and writes the outputs
+  floatx4_t* red = reinterpret_cast<floatx4_t*>(smem);
+  __syncthreads();  // every wave's K loop done: the stage buffers become the partial sums
+  if (h == 1) {
 #pragma unroll
-    for (int j = 0; j < kMaxNT; ++j)
-      if (j < NT) *red_at(kq, j) = acc[j];
+    for (int j = 0; j < NT; ++j) red[(static_cast<size_t>(rt) * NT + j) * kWave + lane] = acc[j];
   }
   __syncthreads();
-  const int P = R + 2 * N;
-  if (kq == 0) {
+  if (h == 0) {
+    const int P = R + 2 * N;
 #pragma unroll
-    for (int j = 0; j < kMaxNT; ++j) {
-      if (j < NT) {
+    for (int j = 0; j < NT; ++j) {
+      const floatx4_t v = acc[j] + red[(static_cast<size_t>(rt) * NT + j) * kWave + lane];
+      const int col = j * 16 + row;
+      // v[i]: token t0 + 16 rt + 4 kg + i, output column col
 #pragma unroll
-        for (int q = 1; q < kProjKSplit; ++q) acc[j] += *red_at(q, j);
-        const int col = j * 16 + row;
-        // B, C out; dt_in to LDS.  acc[j][i]: token 16 mt + 4 kg + i, output column 16 j + row
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tl = mt * 16 + kg * 4 + i;
-          const int64_t tg = t0 + tl;
-          const float v = acc[j][i];
-          if (col < R) {
-            __bf16 hi, lo;
-            split_bf16(v, hi, lo);
-            dh[tl * dstride + col] = __builtin_bit_cast(uint16_t, hi);
-            dl[tl * dstride + col] = __builtin_bit_cast(uint16_t, lo);
-          } else if (col < P && tg < T) {
-            if (col < R + N) B[tg * N + (col - R)] = bf16_bits(v);
-            else C[tg * N + (col - R - N)] = bf16_bits(v);
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int64_t tg = t0 + rt * 16 + kg * 4 + i;
+        if (tg >= T) continue;
+        if (col < R) {
+          __bf16 hi, lo;
+          split_bf16(v[i], hi, lo);
+          dth[tg * Rp + col] = __builtin_bit_cast(uint16_t, hi);
+          dtl[tg * Rp + col] = __builtin_bit_cast(uint16_t, lo);
+        } else if (col < R + N) {
+          B[tg * N + (col - R)] = bf16_bits(v[i]);
+        } else if (col < P) {
+          C[tg * N + (col - R - N)] = bf16_bits(v[i]);
         }
       }
     }
   }
-  for (int i = threadIdx.x; i < kProjTokens * (Rp - R); i += kProjThreads) {  // zero K padding of dt_in
-    const int tl = i / (Rp - R), r = R + i % (Rp - R);
-    dh[tl * dstride + r] = 0;
-    dl[tl * dstride + r] = 0;
+  // dt_in's K padding (columns R .. Rp-1) is zero
+  for (int i = tid; i < kPinTok * (Rp - R); i += kPinThreads) {
+    const int64_t tg = t0 + i / (Rp - R);
+    const int col = R + i % (Rp - R);
+    if (tg < T) {
+      dth[tg * Rp + col] = 0;
+      dtl[tg * Rp + col] = 0;
+    }
   }
-  __syncthreads();
+}
 
-  // dt = dt_in x w_dt: wave w takes a contiguous run of 16-channel tiles, two at a time; the
-  // 32 tokens x 32 channels of a tile pair go through the wave's LDS area so that they leave as
-  // 16-byte row pieces (a quarter wave writes four 64-byte row segments)
-  constexpr int kMaxKR = MAXKR;
-  const int nkr = Rp / kProjK;
-  const int ntiles = d / 16;
-  const int per_wave = (ntiles + kProjWaves - 1) / kProjWaves;
-  const int nt_lo = w * per_wave;
-  const int nt_hi = nt_lo + per_wave < ntiles ? nt_lo + per_wave : ntiles;
-  uint16_t* ot = reinterpret_cast<uint16_t*>(smem + w * kProjWaveBytes);  // [kProjTokens][kProjOStride]
-  // the w_dt operands of a tile pair (a lone last tile is taken twice and stored once), loaded a
-  // pair ahead of their use
-  bf16x8_t wv[2][kMaxKR];
-  auto wdt_load = [&](int nt) {
+// dt = dt_in x w_dt.  Workgroup (cb, g) of ncb x G (g fastest) takes channels 128 cb .. 128 cb + 127
+// and the 16-token tiles g * per .. (g + 1) * per - 1; wave w takes every fourth of them.  The block's
+// w_dt operands (KR = Rp / 32 K steps, a template argument) are staged in LDS once, zero past
+// d; per token tile a wave loads dt_in's high and low parts (prefetched one tile ahead: they
+// are the only global loads of the loop), runs 8 x KR x 2 MFMAs and writes the 16 x 128 tile
+// through its LDS tile as 16-byte row pieces.
+template <int KR>
+__global__ void __launch_bounds__(kPdtThreads) k_proj_dt(const uint16_t* __restrict__ dth,
+                                                         const uint16_t* __restrict__ dtl,
+                                                         const uint16_t* __restrict__ wdtP, uint16_t* __restrict__ dt,
+                                                         int64_t T, int d, int ncb, int per) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int Rp = KR * kProjK;
+  u32x4_t* wl = reinterpret_cast<u32x4_t*>(smem);  // [KR * 4][kPdtCh] pieces of 8 bf16
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  uint16_t* o = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(KR) * 4 * kPdtCh * 16) + w * 16 * kPdtOStride;
+  const int row = lane & 15, kg = lane >> 4;
+  // workgroups that run at the same time take different token ranges (they would otherwise all
+  // read the same dt_in rows at once)
+  const int64_t ngr = gridDim.x / ncb;
+  const int cb = static_cast<int>(blockIdx.x / ngr);
+  const int64_t g = blockIdx.x % ngr;
+  const int c0 = cb * kPdtCh;
+  const int64_t d64 = d;
+  // the block's operands: piece (q, c) = wdtP[q][c0 + c][0..7] for q < KR * 4 (zero past d)
+  for (int i = threadIdx.x; i < KR * 4 * kPdtCh; i += kPdtThreads) {
+    const int q = i / kPdtCh, c = i % kPdtCh;
+    wl[i] = c0 + c < d ? *reinterpret_cast<const u32x4_t*>(wdtP + (static_cast<int64_t>(q) * d + c0 + c) * 8)
+                       : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  const int64_t ntt = (T + 15) / 16;  // token tiles
+  const int64_t tt0 = g * per;
+  const int64_t tt1 = tt0 + per < ntt ? tt0 + per : ntt;
+  auto load_a = [&](int64_t tt, u32x4_t (&a)[2 * KR]) {
+    int64_t tk = tt * 16 + row;
+    if (tk >= T) tk = T - 1;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ntile = nt + h < nt_hi ? nt + h : nt;
-      const int64_t base = static_cast<int64_t>(ntile * 16 + row) * 8;
-#pragma unroll
-      for (int kk = 0; kk < kMaxKR; ++kk)
-        if (kk < nkr)
-          wv[h][kk] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(wdtP + static_cast<int64_t>(kk * 4 + kg) * d * 8 + base));
+    for (int kk = 0; kk < KR; ++kk) {
+      a[kk] = *reinterpret_cast<const u32x4_t*>(dth + tk * Rp + kk * kProjK + kg * 8);
+      a[KR + kk] = *reinterpret_cast<const u32x4_t*>(dtl + tk * Rp + kk * kProjK + kg * 8);
     }
   };
-  if (nt_lo < nt_hi) wdt_load(nt_lo);
-  for (int nt = nt_lo; nt < nt_hi; nt += 2) {
-    bf16x8_t wc[2][kMaxKR];
+  u32x4_t acur[2 * KR], anxt[2 * KR];
+  int64_t tt = tt0 + w;
+  load_a(tt < tt1 ? tt : tt0, acur);
+  for (; tt < tt1; tt += kPdtWaves) {
+    load_a(tt + kPdtWaves < tt1 ? tt + kPdtWaves : tt, anxt);  // past the last tile a harmless repeat
+    floatx4_t acc[kPdtTiles];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < kPdtTiles; ++j) acc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < kMaxKR; ++kk) wc[h][kk] = wv[h][kk];
-    wdt_load(nt + 2 < nt_hi ? nt + 2 : nt);  // on the last pair a harmless repeat
-    // four independent accumulations (two tiles x two row tiles), interleaved
-    floatx4_t a[2][kProjRowTiles];
+    for (int kk = 0; kk < KR; ++kk) {
+      u32x4_t wv[kPdtTiles];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int j = 0; j < kPdtTiles; ++j) wv[j] = wl[(kk * 4 + kg) * kPdtCh + j * 16 + row];
+      const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, acur[kk]), al = __builtin_bit_cast(bf16x8_t, acur[KR + kk]);
 #pragma unroll
-      for (int m = 0; m < kProjRowTiles; ++m) a[h][m] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < kPdtTiles; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, __builtin_bit_cast(bf16x8_t, wv[j]), acc[j], 0, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < kMaxKR; ++kk) {
-      if (kk < nkr) {
-        bf16x8_t ah[kProjRowTiles], al[kProjRowTiles];
+      for (int j = 0; j < kPdtTiles; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, __builtin_bit_cast(bf16x8_t, wv[j]), acc[j], 0, 0, 0);
+    }
+    // acc[j][i]: token 16 tt + 4 kg + i, channel c0 + 16 j + row -> the wave's LDS tile, then out
+    // as 16-byte row pieces (a store instruction writes four 256-byte row segments)
 #pragma unroll
-        for (int m = 0; m < kProjRowTiles; ++m) {
-          const size_t o = static_cast<size_t>(m * 16 + row) * dstride + kk * kProjK + kg * 8;
-          ah[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dh + o));
-          al[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dl + o));
-        }
+    for (int j = 0; j < kPdtTiles; ++j)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+      for (int i = 0; i < 4; ++i) o[(kg * 4 + i) * kPdtOStride + j * 16 + row] = bf16_bits(acc[j][i]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's tile written before it reads it
 #pragma unroll
-          for (int m = 0; m < kProjRowTiles; ++m) a[h][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], wc[h][kk], a[h][m], 0, 0, 0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int m = 0; m < kProjRowTiles; ++m) a[h][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], wc[h][kk], a[h][m], 0, 0, 0);
-      }
+    for (int k = 0; k < 16 * kPdtCh / 8 / kWave; ++k) {
+      const int i = lane + kWave * k;
+      const int r = i / (kPdtCh / 8), part = i % (kPdtCh / 8);
+      const int64_t tg = tt * 16 + r;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + r * kPdtOStride + part * 8);
+      if (tg < T && c0 + part * 8 < d) *reinterpret_cast<u32x4_t*>(dt + tg * d64 + c0 + part * 8) = v;
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int m = 0; m < kProjRowTiles; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ot[(m * 16 + kg * 4 + i) * kProjOStride + h * 16 + row] = bf16_bits(a[h][m][i]);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile written before this wave reads it
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tl = half * 16 + (lane >> 2), part = lane & 3;
-      const int64_t tg = t0 + tl;
-      const int ch = nt * 16 + part * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(ot + tl * kProjOStride + part * 8);
-      if (tg < T && ch < nt_hi * 16) *reinterpret_cast<uint4*>(dt + tg * d64 + ch) = v;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile read before the next pair overwrites it
+    for (int k = 0; k < 2 * KR; ++k) acur[k] = anxt[k];
   }
 }
 

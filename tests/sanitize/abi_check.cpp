@@ -108,7 +108,8 @@ static void sweep_plans() {
         }
   for (int32_t d : I32)
     for (int32_t N : NS)
-      for (int32_t R : {-1, 0, 1, 64, 256, 257, INT32_MAX}) (void)mamba_mixer_project_workspace_bytes(d, N, R);
+      for (int32_t R : {-1, 0, 1, 64, 256, 257, INT32_MAX})
+        for (int64_t T : I64) (void)mamba_mixer_project_workspace_bytes(T, d, N, R);
   for (int code : {INT_MIN, -8, -7, -1, 0, 1, INT_MAX}) EXPECT(mamba_mixer_status_string(code) != nullptr, "status");
   EXPECT(mamba_mixer_version() != nullptr && std::strlen(mamba_mixer_version()) > 0, "version");
   std::printf("plan queries: %ld calls\n", calls);

@@ -311,8 +311,10 @@ def test_prefill_train_validation(lib):
 def test_project_validation(lib):
     # x, conv_w, conv_b, cu, conv_state, w_x, w_dt, dt, B, C
     p = _ptrs(10)
-    need = lib.mamba_mixer_project_workspace_bytes(64, 16, 4)
-    assert need >= (48 * 64 + 64 * 32) * 2  # w_x^T padded to 48 x 64, w_dt^T 64 x 32, bf16
+    need = lib.mamba_mixer_project_workspace_bytes(100, 64, 16, 4)
+    # w_x re-laid, padded to 48 x 64, w_dt to 32 x 64, and dt_in's high and low parts [100][32], bf16
+    assert need == 48 * 64 * 2 + 32 * 64 * 2 + 2 * ((100 * 32 * 2 + 255) // 256 * 256)
+    assert lib.mamba_mixer_project_workspace_bytes(-1, 64, 16, 4) == 0
     ws = ctypes.c_void_p(0x7F000000)
 
     def call(q, S=2, T=100, d=64, N=16, R=4, K=4, io=1, wsb=need, w=ws):
