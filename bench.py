@@ -40,9 +40,11 @@ if ROOT not in sys.path:
 
 METRIC = "prefill tokens/s + decode steps/s (B=256); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-# FP32 vector peak (AMD's published figure): 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 2.4 GHz x 64 FMA
-# lanes per clock x 2 FLOP; reaching it takes packed fp32 (two fp32 operations per lane and
-# instruction), which this build does not generate.  The rooflines count algorithmic FLOP against it.
+# FP32 vector peak (AMD's published figure): 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 2.4 GHz x 32 fp32
+# FMA per clock x 2 FLOP.  A SIMD retires one wave64 instruction per 4 clocks (16 lanes per clock);
+# the factor 2 on top is packed fp32 (two fp32 operations per lane and instruction), which this build
+# does not generate, so its own ceiling is half the peak.  The rooflines count algorithmic FLOP
+# against the published peak.
 ALU_PEAK_TFLOPS = 157.3
 
 
@@ -917,6 +919,41 @@ def copy_calibration():
                           launches=3)), flush=True)
 
 
+def hbm_probe():
+    """Plain streams of known size on this GPU with torch's own kernels: write-only (fill) and
+    read+write (copy), each timed alone with events after a 1 GiB read that leaves the Infinity
+    Cache holding clean lines of another buffer.  Context for the HBM rooflines: what a simple
+    stream reaches here against the 8 TB/s peak."""
+    import torch
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    res = []
+    for mib in (64, 256, 1024):
+        n = (mib << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        ops = (("write", n * 4, lambda: a.fill_(2.0)), ("copy", n * 8, lambda: b.copy_(a)))
+        for name, nbytes, fn in ops:
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(10):
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = float(np.median(ts))
+            res.append(dict(op=name, MiB=mib, bytes=nbytes, us=round(ms * 1e3, 2),
+                            GBs=round(nbytes / (ms * 1e-3) / 1e9, 1)))
+            log(f"[hbm-probe] {name:5s} {mib:5d} MiB  {ms * 1e3:9.2f} us  {res[-1]['GBs']:8.1f} GB/s")
+        del a, b
+    print(json.dumps(dict(hbm_probe=res, peak_GBs=HBM_PEAK_GBS,
+                          note="median of 10 launches, each after a 1 GiB read")), flush=True)
+
+
 def _short_kernel_name(name):
     return name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
 
@@ -972,6 +1009,8 @@ def main():
     ap.add_argument("--source-sha", action="store_true", help="print the HIP source hash and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy three times (to scale HBM byte counters)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="time plain write and copy streams of 64 MiB to 1 GiB and exit")
     args = ap.parse_args()
     global SETTLE_MS
     SETTLE_MS = args.settle_ms
@@ -988,6 +1027,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.hbm_probe:
+        hbm_probe()
         return
 
     import torch
