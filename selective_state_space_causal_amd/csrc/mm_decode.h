@@ -232,49 +232,88 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
   if (c >= d) return;
   const int64_t slot = static_cast<int64_t>(Bs) * d;  // ring slot stride of x and dt
   const int64_t rc = static_cast<int64_t>(r) * d + c;
-  float h[NMAX], cs[kKS], xs[W], ds[W], zv[W];
-  if (LO) {  // the bf16 copy: two 16-byte loads of the state, one 8-byte load of the conv entries
+  // the checkpoint as loaded: 16 fp32 state entries and 3 conv entries, or with LO their bf16
+  // copy, two 16-byte loads of the state (in the first 8 words) and one 8-byte load of the conv
+  // entries (in cw[0], cw[1])
+  uint32_t hw[NMAX], cw[kKS];
+  if (LO) {
     const uint4* lrow = reinterpret_cast<const uint4*>(ssm_lo + rc * NMAX);
 #pragma unroll
     for (int v = 0; v < NMAX / 8; ++v) {
       const uint4 t = lrow[v];
-      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[8 * v + 2 * e] = __uint_as_float(w[e] << 16);
-        h[8 * v + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      }
+      hw[4 * v] = t.x; hw[4 * v + 1] = t.y; hw[4 * v + 2] = t.z; hw[4 * v + 3] = t.w;
     }
+#pragma unroll
+    for (int i = NMAX / 2; i < NMAX; ++i) hw[i] = 0u;
     const uint2 c2 = reinterpret_cast<const uint2*>(conv_lo)[rc];
-    cs[0] = __uint_as_float(c2.x << 16);
-    cs[1] = __uint_as_float(c2.x & 0xFFFF0000u);
-    cs[2] = __uint_as_float(c2.y << 16);
+    cw[0] = c2.x; cw[1] = c2.y; cw[2] = 0u;
   } else {
     const float4* srow = reinterpret_cast<const float4*>(ssm_state + rc * NMAX);
 #pragma unroll
     for (int v = 0; v < NMAX / 4; ++v) {
       const float4 t = srow[v];
-      h[4 * v] = t.x; h[4 * v + 1] = t.y; h[4 * v + 2] = t.z; h[4 * v + 3] = t.w;
+      hw[4 * v] = __float_as_uint(t.x); hw[4 * v + 1] = __float_as_uint(t.y);
+      hw[4 * v + 2] = __float_as_uint(t.z); hw[4 * v + 3] = __float_as_uint(t.w);
     }
 #pragma unroll
-    for (int m = 0; m < kKS; ++m) cs[m] = conv_state[rc * kKS + m];
+    for (int m = 0; m < kKS; ++m) cw[m] = __float_as_uint(conv_state[rc * kKS + m]);
   }
+  uint32_t xr[W], dr[W], zr[W];  // raw io words
+  // Every slot index is clamped into the call's range instead of skipping loads: the loads are
+  // then unconditional and all in flight together (a load under a branch is waited for before
+  // the next one issues).  Values of steps past k1 and z of steps before k0 are never used.
 #pragma unroll
-  for (int t = 0; t < W; ++t) {  // slots past k1 are not read
-    xs[t] = (t <= k1) ? ld_io(x_ring, t * slot + rc) : 0.0f;
-    ds[t] = (t <= k1) ? ld_io(dt_ring, t * slot + rc) : 0.0f;
-    zv[t] = (t >= k0 && t <= k1) ? ld_io(z, (t - k0) * zs + rc) : 0.0f;
+  for (int t = 0; t < W; ++t) {
+    const int tx = t <= k1 ? t : k1;
+    const int tz = (t >= k0 ? (t <= k1 ? t : k1) : k0) - k0;
+    xr[t] = ld_io_raw(x_ring, tx * slot + rc);
+    dr[t] = ld_io_raw(dt_ring, tx * slot + rc);
+    zr[t] = ld_io_raw(z, tz * zs + rc);
   }
   const float4 w = reinterpret_cast<const float4*>(conv_w)[c];
   const float cb = conv_b[c], dtb = dt_bias[c], Dc = D[c];
+  float4 al[NMAX / 4];
+#pragma unroll
+  for (int v = 0; v < NMAX / 4; ++v) al[v] = reinterpret_cast<const float4*>(A_log + static_cast<int64_t>(c) * NMAX)[v];
+  // Every value loaded above is consumed here at once (an empty asm), so all the loads are in
+  // flight together and the lane waits once: otherwise the compiler sinks the ring loads into
+  // the steps that use them, behind the first step's waits (more round trips to memory).
+  asm volatile("" ::"v"(hw[0]), "v"(hw[1]), "v"(hw[2]), "v"(hw[3]), "v"(hw[4]), "v"(hw[5]), "v"(hw[6]), "v"(hw[7]),
+               "v"(hw[8]), "v"(hw[9]), "v"(hw[10]), "v"(hw[11]), "v"(hw[12]), "v"(hw[13]), "v"(hw[14]), "v"(hw[15]),
+               "v"(cw[0]), "v"(cw[1]), "v"(cw[2]), "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(dr[0]),
+               "v"(dr[1]), "v"(dr[2]), "v"(dr[3]), "v"(zr[0]), "v"(zr[1]), "v"(zr[2]), "v"(zr[3]));
+  asm volatile("" ::"v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(cb), "v"(dtb), "v"(Dc), "v"(al[0].x), "v"(al[0].y),
+               "v"(al[0].z), "v"(al[0].w), "v"(al[1].x), "v"(al[1].y), "v"(al[1].z), "v"(al[1].w), "v"(al[2].x),
+               "v"(al[2].y), "v"(al[2].z), "v"(al[2].w), "v"(al[3].x), "v"(al[3].y), "v"(al[3].z), "v"(al[3].w));
+  float h[NMAX], cs[kKS], xs[W], ds[W], zv[W];
+#pragma unroll
+  for (int t = 0; t < W; ++t) {
+    xs[t] = io_value<IO>(xr[t]);
+    ds[t] = io_value<IO>(dr[t]);
+    zv[t] = io_value<IO>(zr[t]);
+  }
+  if (LO) {  // bf16 -> fp32: the value in the upper half of the word
+#pragma unroll
+    for (int i = 0; i < NMAX / 2; ++i) {
+      h[2 * i] = __uint_as_float(hw[i] << 16);
+      h[2 * i + 1] = __uint_as_float(hw[i] & 0xFFFF0000u);
+    }
+    cs[0] = __uint_as_float(cw[0] << 16);
+    cs[1] = __uint_as_float(cw[0] & 0xFFFF0000u);
+    cs[2] = __uint_as_float(cw[1] << 16);
+  } else {
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) h[n] = __uint_as_float(hw[n]);
+#pragma unroll
+    for (int m = 0; m < kKS; ++m) cs[m] = __uint_as_float(cw[m]);
+  }
   float A2[NMAX];
 #pragma unroll
   for (int v = 0; v < NMAX / 4; ++v) {
-    const float4 al = reinterpret_cast<const float4*>(A_log + static_cast<int64_t>(c) * NMAX)[v];
-    A2[4 * v] = -exp2_hw(al.x * kLog2e) * kLog2e;
-    A2[4 * v + 1] = -exp2_hw(al.y * kLog2e) * kLog2e;
-    A2[4 * v + 2] = -exp2_hw(al.z * kLog2e) * kLog2e;
-    A2[4 * v + 3] = -exp2_hw(al.w * kLog2e) * kLog2e;
+    A2[4 * v] = -exp2_hw(al[v].x * kLog2e) * kLog2e;
+    A2[4 * v + 1] = -exp2_hw(al[v].y * kLog2e) * kLog2e;
+    A2[4 * v + 2] = -exp2_hw(al[v].z * kLog2e) * kLog2e;
+    A2[4 * v + 3] = -exp2_hw(al[v].w * kLog2e) * kLog2e;
   }
   // X(m) = x of window step m (m >= 0) or checkpoint conv entry 3+m (m < 0)
   auto X = [&](int m) -> float { return m >= 0 ? xs[m] : cs[kKS + m]; };

@@ -4,6 +4,8 @@
 // (_add_mamba_tp_layer), and the sequential token loop built on it.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,6 +24,13 @@ constexpr float kLn2 = 0.69314718055994531f;
 __device__ __forceinline__ float ld_io(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld_io(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+// the same in two halves: the raw word as loaded, then its value
+__device__ __forceinline__ uint32_t ld_io_raw(const float* p, int64_t i) { return __float_as_uint(p[i]); }
+__device__ __forceinline__ uint32_t ld_io_raw(const uint16_t* p, int64_t i) { return p[i]; }
+template <typename IO>
+__device__ __forceinline__ float io_value(uint32_t raw) {
+  return std::is_same<IO, float>::value ? __uint_as_float(raw) : __uint_as_float(raw << 16);
 }
 __device__ __forceinline__ void st_io(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st_io(uint16_t* p, int64_t i, float v) {
