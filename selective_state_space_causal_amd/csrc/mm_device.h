@@ -81,15 +81,17 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 // x * sigmoid(x)
 __device__ __forceinline__ float silu(float x) { return x * rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
-// softplus(v) = log(1 + e^v).  For e = e^v < 1/64 the rounding of 1 + e would cost
-// up to ~4e-6 relative, so the Taylor series e - e^2/2 + e^3/3 - e^4/4 (error < e^5/5)
-// is used there.  softplus(v) > v everywhere, and past v = 20 it exceeds v by less
-// than 2.1e-9: the result is the larger of v and the value at min(v, 20).
+// softplus(v) = log(1 + e^v) = log(u) + log(1 + (1 + e - u) / u) with u = 1 + e rounded to
+// float.  u - 1 is exact, and so is the rounding error d = e - (u - 1); log(u) + d differs
+// from log(1 + e) by about d * e, under 2^-24 of the result, where log(u) alone would lose
+// up to 2^-24 / log(1 + e) relative for small e.  The hardware log2 keeps ~1e-7 relative
+// accuracy for u just above 1.  softplus(v) > v everywhere, and past v = 20 it exceeds v by
+// less than 2.1e-9: the result is the larger of v and the value at min(v, 20).
 __device__ __forceinline__ float softplus(float v) {
   const float e = exp2_hw(fminf(v, 20.0f) * kLog2e);
-  const float series = e * __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, -0.25f, 1.0f / 3.0f), -0.5f), 1.0f);
-  const float viaLog = log2_hw(1.0f + e) * kLn2;
-  return fmaxf(v, (e < 0.015625f) ? series : viaLog);
+  const float u = 1.0f + e;
+  const float d = e - (u - 1.0f);
+  return fmaxf(v, __builtin_fmaf(log2_hw(u), kLn2, d));
 }
 
 // largest s in [0, S-1] with cu[s] <= g (the sequence that holds token g; empty

@@ -756,21 +756,24 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
     const uint64_t mlo = lo >= 4 ? ~0ull : (1ull << (16 * lo)) - 1ull;
     return mhi & ~mlo & ych_lanes;
   };
-  // y of the slot at sl, read from LDS (vector staging: wave 1, four channels per lane)
-  // and then stored to the rows of the lane mask m
+  // per-lane LDS offsets within a slot, held opaque so that each block's address is one add
+  // of the slot's (scalar) offset rather than a rebuilt index expression
+  uint32_t lx = static_cast<uint32_t>(offsetof(RowSlot, x) + (j * kTS + ch) * 4);   // x[j][ch]
+  uint32_t lyw = static_cast<uint32_t>(offsetof(RowSlot, y) + (j * kTS + ch) * 4);  // y[j][ch]
+  uint32_t lyr = VEC ? vy : static_cast<uint32_t>(offsetof(RowSlot, y)) + so.tc;    // y read for the store
+  asm volatile("" : "+v"(lx), "+v"(lyw), "+v"(lyr));
+  // y of the slot at sl, read from LDS (vector staging: four channels per lane) and then
+  // stored to the rows of the lane mask m.  With vector staging only wave 1 stores, but every
+  // wave reads (the same valid tile addresses): a read on one wave alone would leave the other
+  // waves a value to set on every block, which costs more issue slots than the read.
   auto read_y = [&](uint32_t sl) -> f32x4_t {
-    const char* yb = reinterpret_cast<const char*>(&L.slot[0]) + sl;
-    f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+    const char* yb = reinterpret_cast<const char*>(&L.slot[0]) + (sl + lyr);
     if (VEC) {
-      if (wv == kKindDt) {
-        const float2* q = reinterpret_cast<const float2*>(yb + vy);
-        const float2 a = q[0], b = q[1];
-        v = f32x4_t{a.x, a.y, b.x, b.y};
-      }
-    } else {
-      v.x = *reinterpret_cast<const float*>(yb + offsetof(RowSlot, y) + so.tc);
+      const float2* q = reinterpret_cast<const float2*>(yb);
+      const float2 a = q[0], b = q[1];
+      return f32x4_t{a.x, a.y, b.x, b.y};
     }
-    return v;
+    return f32x4_t{*reinterpret_cast<const float*>(yb), 0.0f, 0.0f, 0.0f};
   };
   auto write_y = [&](const f32x4_t& v, uint64_t m) {
     if (VEC) {
@@ -828,10 +831,11 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       }
       // block ib+1's conv window (inputs of tokens t-3 .. t: rows j .. j+3), dt and z
       // (past the last block these are stale values, computed on and not used)
-      const float* xr = &Sn.x[j][ch];
+      const float* xr = reinterpret_cast<const float*>(reinterpret_cast<const char*>(&L.slot[0]) + (s1 + lx));
       const float x3 = xr[0], x2 = xr[kTS], x1 = xr[2 * kTS], xv = xr[3 * kTS];
-      const float dtv = Sn.dt[j][ch];
-      const float zv = FINAL ? Sn.z[j][ch] : 0.0f;
+      // dt[j][ch] and z[j][ch] at fixed distances from x[j][ch]
+      const float dtv = xr[(offsetof(RowSlot, dt) - offsetof(RowSlot, x)) / 4];
+      const float zv = FINAL ? xr[(offsetof(RowSlot, z) - offsetof(RowSlot, x)) / 4] : 0.0f;
       // all of the block's LDS reads are in flight before the arithmetic starts
       __builtin_amdgcn_sched_barrier(0);
       const Tok tn = token_work(x3, x2, x1, xv, dtv, zv, ib + 1 == nb - 1 ? mlast : ~0ull);
@@ -839,7 +843,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row(
       row_steps<FINAL>(std::make_integer_sequence<int, kRow>{}, tk.delta, tk.du, A2, Bq, Cq, h, p);
       if (FINAL) {
         const float s = row_transpose_sum(p, j);
-        slot_at(L, s0).y[j][ch] = __builtin_fmaf(Dc, tk.u, s) * tk.zs;
+        *reinterpret_cast<float*>(reinterpret_cast<char*>(&L.slot[0]) + (s0 + lyw)) = __builtin_fmaf(Dc, tk.u, s) * tk.zs;
       }
       tk = tn;
     }
