@@ -38,6 +38,9 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    # torch first: the library then binds to the HIP runtime torch has loaded, the one that owns
+    # the streams and device memory it is handed (loaded first, it would bring in a second one)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
