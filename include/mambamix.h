@@ -398,12 +398,14 @@ size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d);
  * Both products run on the matrix cores (bf16 MFMA, fp32 accumulation); the computed operands
  * u and dt_in enter as bf16 high + low parts, so the products have fp32-quality operands and
  * the outputs are rounded once, to bf16 (nearest even).
- * Limits: io MM_IO_BF16 only, d a multiple of 16, 1 <= R <= 256 (else MM_ERR_UNSUPPORTED).
+ * Limits: io MM_IO_BF16 only, d a multiple of 16 and at most MM_PROJECT_MAX_D, 1 <= R <= 256
+ * (else MM_ERR_UNSUPPORTED).
  * T == 0 or d == 0 is a successful no-op.  Outputs overlapping an input or one another are
  * MM_ERR_ALIAS.  Three kernels are enqueued (weight re-layout; u x w_x, which writes B, C and
  * dt_in; dt_in x w_dt, which writes dt); events, n_events are optional as in
  * mamba_mixer_prefill_ex (n = 3: events[i] before kernel i, events[3] after the last).
  */
+#define MM_PROJECT_MAX_D (1 << 22) /* channels of mamba_mixer_project (its per-row offsets are 32-bit) */
 int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b, const int32_t* cu_seqlens,
                         const float* conv_state, const void* w_x, const void* w_dt, void* dt, void* B, void* C,
                         int32_t S, int64_t T, int32_t d, int32_t N, int32_t R, int32_t K, int32_t io_dtype,

@@ -599,7 +599,7 @@ int check_proj_sizes(int32_t S, int64_t T, int32_t d, int32_t N, int32_t R, int3
   const int rc = check_prefill_sizes(S, T, d, N, K, io);
   if (rc != MM_OK) return rc;
   if (R < 0) return MM_ERR_DIM;
-  if (io != MM_IO_BF16 || R < 1 || R > kProjMaxR || d % 16 != 0) return MM_ERR_UNSUPPORTED;
+  if (io != MM_IO_BF16 || R < 1 || R > kProjMaxR || d % 16 != 0 || d > MM_PROJECT_MAX_D) return MM_ERR_UNSUPPORTED;
   return MM_OK;
 }
 

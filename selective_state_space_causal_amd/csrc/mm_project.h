@@ -17,13 +17,14 @@
 //
 // The two products have opposite memory profiles, so each has a kernel of its own:
 //  * k_proj_in reads x (T d bf16, the layer's large input) and writes only R + 2N values per
-//    token: a read-streaming kernel.  A workgroup of four waves takes 16 tokens; wave w takes
-//    the K quarter w of d.  Per staging step a wave loads 128 channels of the 19 x rows its
-//    16 tokens need (t-3 .. t) with row-contiguous 16-byte loads, one step ahead of their use,
-//    into its own LDS tile; each lane then computes u for its token and 8 channels per MFMA K
-//    step and issues the MFMAs of all output columns.  The quarters' sums are added in
-//    quarter order through LDS (deterministic).  B and C go to their outputs, dt_in to the
-//    workspace as bf16 high and low parts [T][Rp] (zero past R).
+//    token: a read-streaming kernel.  A workgroup of eight waves takes 64 tokens: four 16-token
+//    row tiles times two halves of the K range.  Per K stage the workgroup's threads load the x
+//    rows its tokens need (t-3 .. t) with row-contiguous 16-byte loads, the stage's conv
+//    parameters and its w_x operands, several stages ahead of their use, into a double-buffered
+//    LDS area; each lane then computes u for its token and 8 channels per MFMA K step and issues
+//    the MFMAs of all output columns.  The halves' sums are added in a fixed order through LDS
+//    (deterministic).  B and C go to their outputs, dt_in to the workspace as bf16 high and low
+//    parts [T][Rp] (zero past R).
 //  * k_proj_dt writes dt (T d bf16) from dt_in (T Rp, small): a write-streaming kernel with
 //    one workgroup per 64 tokens x 128 channels, far more workgroups than token tiles.  A wave
 //    takes 16 tokens x 128 channels (8 column tiles); its output tile goes through LDS so
@@ -76,7 +77,7 @@ struct PinGeo {
   static constexpr int CBOFF = CWOFF + KC * 16;
   static constexpr int WOFF = CBOFF + KC * 4;
   static constexpr int HB = WOFF + WP * 16;                // bytes per half
-  static constexpr int L = (kPinHalves * HP + kPinThreads - 1) / kPinThreads;  // loads per thread and stage
+  static constexpr int L = (HP + kPinThreads / kPinHalves - 1) / (kPinThreads / kPinHalves);  // loads per thread and stage
   static constexpr int D = NT <= 6 ? 4 : 1;                // stages in flight (1 or 4)
 };
 template <int NT>
@@ -192,68 +193,68 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
   const int64_t back = t - cu[s];  // tokens of the sequence before t
   const float* cs = conv_state + static_cast<int64_t>(s) * d64 * kKS;
 
-  // The staging pieces of thread i are q = i + 512 k (k < L): half q / HP, and within it piece
-  // p = q % HP: the x pieces (staged row p / (KC/8) = token t0 - 3 + p / (KC/8) clamped into
-  // 0 .. T-1, channels 8 (p % (KC/8)) .. of the stage), KC conv weight rows (float4), KC / 4
-  // pieces of four biases, and the stage's w_x operand pieces (contiguous).  Channels past d
-  // read clamped, valid addresses (their u is forced to 0); pieces past both halves load a
-  // valid address and go to a dummy slot.
+  // Waves 0-3 stage the first half's pieces and waves 4-7 the second's, so that a thread's stage
+  // index is wave-uniform.  The pieces of thread i of a half are p = i + 256 k (k < L): the x
+  // pieces (staged row p / (KC/8) = token t0 - 3 + p / (KC/8) clamped into 0 .. T-1, channels
+  // 8 (p % (KC/8)) .. of the stage), KC conv weight rows (float4), KC / 4 pieces of four biases,
+  // and the stage's w_x operand pieces (contiguous).  Each piece keeps a 64-bit base, the byte
+  // offset of its half's first stage, the bytes it advances per stage and the largest offset it
+  // may read: channels past d read clamped, valid addresses (their u is forced to 0); slots past
+  // the half's pieces load a valid address and go to a dummy slot.  (Offsets fit 32 bits for
+  // d <= 2^22, which the host checks.)
+  const int hs = w / kPinRT;                       // the half this wave stages (wave-uniform)
+  const int ht = tid - hs * (kPinThreads / kPinHalves);
   const unsigned char* pbase[L];
-  int pstep[L], pch[L], pmax[L], pdst[L];
-  unsigned char kinds = 0;   // bit k: a channel-clamped piece (x or conv), else a w_x piece
-  unsigned char halves = 0;  // bit k: a piece of the second half
+  uint32_t poff[L], pinc[L], plim[L];
+  int pdst[L];
+  {
+    const int kb = (hs == 0 ? 0 : len0) * KC;  // the half's first channel
 #pragma unroll
-  for (int k = 0; k < L; ++k) {
-    const int q = tid + kPinThreads * k;
-    const bool real = q < kPinHalves * HP;
-    const int hh = real ? q / HP : 0;
-    const int p = real ? q % HP : G::XP + G::CWP + G::CBP;  // a w_x piece
-    const int kb = (hh == 0 ? 0 : len0) * KC;  // the half's first channel
-    halves |= hh << k;
-    pdst[k] = hh * HB;
-    if (p < G::XP) {
-      int64_t tok = t0 - kKS + p / (KC / 8);
-      tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
-      pbase[k] = reinterpret_cast<const unsigned char*>(x + tok * d64);
-      pch[k] = kb + 8 * (p % (KC / 8));  // first channel of the piece in the half's first stage
-      pmax[k] = d - 8;
-      pstep[k] = 2;                       // bytes per channel
-      pdst[k] += (p / (KC / 8)) * G::XSTRIDE * 2 + (p % (KC / 8)) * 16;
-      kinds |= 1 << k;
-    } else if (p < G::XP + G::CWP) {
-      pbase[k] = reinterpret_cast<const unsigned char*>(conv_w);
-      pch[k] = kb + (p - G::XP);
-      pmax[k] = d - 1;
-      pstep[k] = 16;
-      pdst[k] += G::CWOFF + (p - G::XP) * 16;
-      kinds |= 1 << k;
-    } else if (p < G::XP + G::CWP + G::CBP) {
-      pbase[k] = reinterpret_cast<const unsigned char*>(conv_b);
-      pch[k] = kb + 4 * (p - G::XP - G::CWP);
-      pmax[k] = d - 4;
-      pstep[k] = 4;
-      pdst[k] += G::CBOFF + (p - G::XP - G::CWP) * 16;
-      kinds |= 1 << k;
-    } else {  // w_x: a stage's operands are SUB * 4 Pp contiguous pieces
-      const int pw = p - G::XP - G::CWP - G::CBP;
-      pbase[k] = reinterpret_cast<const unsigned char*>(wxP);
-      pch[k] = kb / kProjK * 4 * Pp + pw;  // piece index in the half's first stage
-      pmax[k] = nks * 4 * Pp - 1;          // the last operand piece
-      pstep[k] = 16;
-      pdst[k] += G::WOFF + pw * 16;
+    for (int k = 0; k < L; ++k) {
+      const int q = ht + (kPinThreads / kPinHalves) * k;
+      const bool real = q < HP;
+      const int p = real ? q : G::XP + G::CWP + G::CBP;  // a w_x piece
+      pdst[k] = hs * HB;
+      if (p < G::XP) {
+        int64_t tok = t0 - kKS + p / (KC / 8);
+        tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
+        pbase[k] = reinterpret_cast<const unsigned char*>(x + tok * d64);
+        poff[k] = static_cast<uint32_t>(kb + 8 * (p % (KC / 8))) * 2u;
+        pinc[k] = KC * 2;
+        plim[k] = static_cast<uint32_t>(d - 8) * 2u;
+        pdst[k] += (p / (KC / 8)) * G::XSTRIDE * 2 + (p % (KC / 8)) * 16;
+      } else if (p < G::XP + G::CWP) {
+        pbase[k] = reinterpret_cast<const unsigned char*>(conv_w);
+        poff[k] = static_cast<uint32_t>(kb + (p - G::XP)) * 16u;
+        pinc[k] = KC * 16;
+        plim[k] = static_cast<uint32_t>(d - 1) * 16u;
+        pdst[k] += G::CWOFF + (p - G::XP) * 16;
+      } else if (p < G::XP + G::CWP + G::CBP) {
+        pbase[k] = reinterpret_cast<const unsigned char*>(conv_b);
+        poff[k] = static_cast<uint32_t>(kb + 4 * (p - G::XP - G::CWP)) * 4u;
+        pinc[k] = KC * 4;
+        plim[k] = static_cast<uint32_t>(d - 4) * 4u;
+        pdst[k] += G::CBOFF + (p - G::XP - G::CWP) * 16;
+      } else {  // w_x: a stage's operands are SUB * 4 Pp contiguous pieces
+        const int pw = p - G::XP - G::CWP - G::CBP;
+        pbase[k] = reinterpret_cast<const unsigned char*>(wxP);
+        poff[k] = static_cast<uint32_t>(kb / kProjK * 4 * Pp + pw) * 16u;
+        pinc[k] = SUB * 4 * Pp * 16;
+        plim[k] = static_cast<uint32_t>(nks * 4 * Pp - 1) * 16u;  // the last operand piece
+        pdst[k] += G::WOFF + pw * 16;
+      }
+      if (!real) pdst[k] = -1;  // staged nowhere
     }
-    if (!real) pdst[k] = -1;  // staged nowhere
   }
   // stage g of a half of len stages (clamped to its last stage)
   auto rel_stage = [&](int g, int len) { return len > 0 ? (g < len ? g : len - 1) : 0; };
+  const int hlen = hs == 0 ? len0 : nst;
   auto load_stage = [&](int g, u32x4_t (&pf)[L]) {
-    const int r0 = rel_stage(g, len0), r1 = rel_stage(g, nst);
+    const uint32_t rel = static_cast<uint32_t>(rel_stage(g, hlen));  // wave-uniform
 #pragma unroll
     for (int k = 0; k < L; ++k) {
-      const int rel = (halves >> k) & 1 ? r1 : r0;
-      const int adv = (kinds >> k) & 1 ? rel * KC : rel * SUB * 4 * Pp;  // channels, or operand pieces
-      const int o = pch[k] + adv;
-      pf[k] = *reinterpret_cast<const u32x4_t*>(pbase[k] + static_cast<int64_t>(o <= pmax[k] ? o : pmax[k]) * pstep[k]);
+      const uint32_t o = __umul24(rel, pinc[k]) + poff[k];
+      pf[k] = *reinterpret_cast<const u32x4_t*>(pbase[k] + (o < plim[k] ? o : plim[k]));
     }
   };
   // (pieces past both halves go to a 16-byte slot after the two stage buffers: no branch, so the

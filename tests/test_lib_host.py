@@ -323,6 +323,7 @@ def test_project_validation(lib):
     assert call(p, d=40) == MM_ERR_UNSUPPORTED       # d not a multiple of 16
     assert call(p, R=0) == MM_ERR_UNSUPPORTED
     assert call(p, R=257) == MM_ERR_UNSUPPORTED
+    assert call(p, T=1, d=(1 << 22) + 16) == MM_ERR_UNSUPPORTED  # past the projection's channel limit
     assert call(p, S=0) == MM_ERR_DIM
     for i in range(10):
         q = list(p)
