@@ -92,3 +92,34 @@ def test_project_feeds_prefill():
                                  dev(f["w_x"]), dev(f["w_dt"]))
         torch.cuda.synchronize()
         assert torch.equal(dts, dt[a:b]) and torch.equal(Bs, B[a:b]) and torch.equal(Cs, C[a:b]), s
+
+
+def _sweep_shape(nt):
+    """N and R whose R + 2N needs exactly nt 16-column output tiles (one short of a full tile), so
+    that every kernel instance (1..18 column tiles; dt_rank in 1..8 K steps of 32) runs once."""
+    N = 4 if nt == 1 else (8 if nt == 2 else 16)
+    return N, 16 * nt - 2 * N - 3
+
+
+@pytest.mark.parametrize("nt", range(1, 19))
+def test_project_every_instance(nt):
+    N, R = _sweep_shape(nt)
+    d = (48, 80, 144)[nt % 3]
+    lens = [1, 2, 0, 57, 3, 40 + nt]
+    f = _case(200 + nt, lens, d, N, R)
+    log(f"[proj] instance nt={nt}: lens={lens} d={d} N={N} R={R} (K steps of dt_rank {(R + 31) // 32})")
+    dt, B, C = _run(f)
+    o = oracle.project(f["x"], f["conv_w"], f["conv_b"], f["cu"], f["cs"], f["w_x"], f["w_dt"], R, N)
+    w = [_close(dt, o["dt"], "dt"), _close(B, o["B"], "B"), _close(C, o["C"], "C")]
+    log(f"[proj] instance nt={nt}: worst err/bound dt {w[0]:.3g} B {w[1]:.3g} C {w[2]:.3g}")
+
+
+def test_project_m1p4b_width():
+    """The 1.4B layer's d_inner 4096 and dt_rank 128 (10 column tiles, 4 K steps of dt_rank) on
+    ragged sequences: every output against the oracle."""
+    lens, d, N, R = [5, 130, 2, 200], 4096, 16, 128
+    f = _case(14, lens, d, N, R)
+    dt, B, C = _run(f)
+    o = oracle.project(f["x"], f["conv_w"], f["conv_b"], f["cu"], f["cs"], f["w_x"], f["w_dt"], R, N)
+    w = [_close(dt, o["dt"], "dt"), _close(B, o["B"], "B"), _close(C, o["C"], "C")]
+    log(f"[proj] 1.4B width: worst err/bound dt {w[0]:.3g} B {w[1]:.3g} C {w[2]:.3g}")
