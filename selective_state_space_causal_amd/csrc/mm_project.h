@@ -478,17 +478,26 @@ __global__ void __launch_bounds__(kPdtThreads) k_proj_dt(const uint16_t* __restr
       const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, acur[kk]), al = __builtin_bit_cast(bf16x8_t, acur[KR + kk]);
 #pragma unroll
       for (int j = 0; j < kPdtTiles; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, __builtin_bit_cast(bf16x8_t, wv[j]), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[j]), ah, acc[j], 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < kPdtTiles; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, __builtin_bit_cast(bf16x8_t, wv[j]), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[j]), al, acc[j], 0, 0, 0);
     }
-    // acc[j][i]: token 16 tt + 4 kg + i, channel c0 + 16 j + row -> the wave's LDS tile, then out
-    // as 16-byte row pieces (a store instruction writes four 256-byte row segments)
+    // The MFMAs form the transposed tile (w_dt^T x dt_in^T): acc[j][i] is channel c0 + 16 j +
+    // 4 kg + i of token 16 tt + row, so each lane writes four consecutive channels of one token
+    // to the wave's LDS tile as 8 bytes; the tile then leaves as 16-byte row pieces.
+    {
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int j = 0; j < kPdtTiles; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[(kg * 4 + i) * kPdtOStride + j * 16 + row] = bf16_bits(acc[j][i]);
+      for (int j = 0; j < kPdtTiles; ++j) {
+        const f32x2_t lo2 = {acc[j][0], acc[j][1]}, hi2 = {acc[j][2], acc[j][3]};
+        *reinterpret_cast<u32x2_t*>(o + row * kPdtOStride + j * 16 + 4 * kg) =
+            u32x2_t{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo2, bf16x2_t)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2_t))};
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's tile written before it reads it
 #pragma unroll
     for (int k = 0; k < 16 * kPdtCh / 8 / kWave; ++k) {
