@@ -1057,7 +1057,7 @@ int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b,
   const int nt = p.Pp / 16;
   const int nkr = p.Rp / kProjK;
   const KernIn kin = proj_in_kernel(nt);
-  const size_t lds = proj_in_lds(nt);
+  const size_t lds = std::max(proj_in_lds(nt), pin_out_bytes(p.Pp, p.Rp));
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(kin), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds)) != hipSuccess)

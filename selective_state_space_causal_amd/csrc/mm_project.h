@@ -86,6 +86,10 @@ inline size_t pin_lds_bytes_t() {  // two stage buffers (+ a dummy slot); the ha
   const size_t red = static_cast<size_t>(kPinRT) * NT * kWave * 16;
   return stage > red ? stage : red;
 }
+// row stride (floats) of k_proj_in's output tile: room for the Pp output columns and for the Rp
+// columns that dt_in's pieces read, plus 4 (rows start 4 banks apart)
+__host__ __device__ inline int pin_out_stride(int Pp, int Rp) { return (Pp > Rp ? Pp : Rp) + 4; }
+inline size_t pin_out_bytes(int Pp, int Rp) { return static_cast<size_t>(kPinTok) * pin_out_stride(Pp, Rp) * 4; }
 
 // k_proj_dt
 constexpr int kPdtWaves = 4;
@@ -374,8 +378,10 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
   if (__any(back < kKS)) kloop(std::true_type{});
   else kloop(std::false_type{});
 
-  // the halves' sums: the second half leaves its accumulators in LDS, the first adds them in
-  // (first + second) and writes the outputs
+  // The halves' sums: the second half leaves its accumulators in LDS and the first adds them to
+  // its own (first + second).  The sums then go through a float tile [64 tokens][OS] in LDS,
+  // so that every output leaves in contiguous runs: the workgroup's 64 rows of B, of C and of
+  // dt_in's two parts are each one contiguous block.
   floatx4_t* red = reinterpret_cast<floatx4_t*>(smem);
   __syncthreads();  // every wave's K loop done: the stage buffers become the partial sums
   if (h == 1) {
@@ -384,36 +390,54 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
   }
   __syncthreads();
   if (h == 0) {
-    const int P = R + 2 * N;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const floatx4_t v = acc[j] + red[(static_cast<size_t>(rt) * NT + j) * kWave + lane];
-      const int col = j * 16 + row;
-      // v[i]: token t0 + 16 rt + 4 kg + i, output column col
+    for (int j = 0; j < NT; ++j) acc[j] += red[(static_cast<size_t>(rt) * NT + j) * kWave + lane];
+  }
+  __syncthreads();  // the partial sums are read: the area becomes the output tile
+  const int OS = pin_out_stride(Pp, Rp);
+  float* ot = reinterpret_cast<float*>(smem);
+  if (h == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t tg = t0 + rt * 16 + kg * 4 + i;
-        if (tg >= T) continue;
-        if (col < R) {
-          __bf16 hi, lo;
-          split_bf16(v[i], hi, lo);
-          dth[tg * Rp + col] = __builtin_bit_cast(uint16_t, hi);
-          dtl[tg * Rp + col] = __builtin_bit_cast(uint16_t, lo);
-        } else if (col < R + N) {
-          B[tg * N + (col - R)] = bf16_bits(v[i]);
-        } else if (col < P) {
-          C[tg * N + (col - R - N)] = bf16_bits(v[i]);
-        }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ot[(rt * 16 + kg * 4 + i) * OS + j * 16 + row] = acc[j][i];  // token row, column
+  }
+  __syncthreads();
+  const int64_t nrows = T - t0 < kPinTok ? T - t0 : kPinTok;  // the workgroup's tokens
+  // dt_in: 8 columns per piece (Rp is a multiple of 32), high and low parts, zero past R
+  {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const int npc = Rp / 8;
+    uint16_t* hb = dth + t0 * Rp;
+    uint16_t* lb = dtl + t0 * Rp;
+    for (int e = tid; e < nrows * npc; e += kPinThreads) {
+      const int r = e / npc, c = (e % npc) * 8;
+      const float4 a = *reinterpret_cast<const float4*>(ot + r * OS + c);
+      const float4 b = *reinterpret_cast<const float4*>(ot + r * OS + c + 4);
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v0 = c + 2 * q < R ? v[2 * q] : 0.0f, v1 = c + 2 * q + 1 < R ? v[2 * q + 1] : 0.0f;
+        const f32x2_t f = {v0, v1};
+        const bf16x2_t hi = __builtin_convertvector(f, bf16x2_t);
+        const f32x2_t hf = __builtin_convertvector(hi, f32x2_t);
+        wh[q] = __builtin_bit_cast(uint32_t, hi);
+        wl[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f - hf, bf16x2_t));
       }
+      *reinterpret_cast<u32x4_t*>(hb + static_cast<int64_t>(e) * 8) = u32x4_t{wh[0], wh[1], wh[2], wh[3]};
+      *reinterpret_cast<u32x4_t*>(lb + static_cast<int64_t>(e) * 8) = u32x4_t{wl[0], wl[1], wl[2], wl[3]};
     }
   }
-  // dt_in's K padding (columns R .. Rp-1) is zero
-  for (int i = tid; i < kPinTok * (Rp - R); i += kPinThreads) {
-    const int64_t tg = t0 + i / (Rp - R);
-    const int col = R + i % (Rp - R);
-    if (tg < T) {
-      dth[tg * Rp + col] = 0;
-      dtl[tg * Rp + col] = 0;
+  // B and C: the workgroup's rows are N contiguous values each
+  {
+    uint16_t* bb = B + t0 * N;
+    uint16_t* cb_ = C + t0 * N;
+    for (int e = tid; e < nrows * N; e += kPinThreads) {
+      const int r = e / N, c = e % N;
+      bb[e] = bf16_bits(ot[r * OS + R + c]);
+      cb_[e] = bf16_bits(ot[r * OS + R + N + c]);
     }
   }
 }
