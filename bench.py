@@ -1159,7 +1159,14 @@ def decode_result(args):
                       kernel="k_decode_vec",
                       kernel_ms=round(dc["kern_ms"], 4), kernel_ms_min=round(dc["kern_ms_min"], 4),
                       alg_bytes_per_launch=db,
-                      note="kernel timed alone with HIP events, Infinity Cache flushed before each step"),
+                      note="kernel timed alone with HIP events, Infinity Cache flushed before each step",
+                      steady_state=dict(
+                          kernel_ms=round(dc["graph_ms"] / dc["steps"], 4),
+                          achieved_GBs=round(db / (dc["graph_ms"] / dc["steps"] * 1e-3) / 1e9, 1),
+                          frac=round(db / (dc["graph_ms"] / dc["steps"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          note="the graph's back-to-back steps (one kernel each, no gaps between them): here "
+                               "every step also writes back the previous step's state from the Infinity "
+                               "Cache, which after a read flush the timed kernel can leave dirty in the cache")),
         graph_replay_matches_flushed_run=dc["graph_matches_eager"],
         replay=replay_result(dc),
         replay_dual=dual_result(dc),
