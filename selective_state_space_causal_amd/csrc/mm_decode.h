@@ -9,6 +9,8 @@ typedef float f32x2_lo __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_lo __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_lo __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_lo __attribute__((ext_vector_type(2)));
+typedef float f32x4_lo __attribute__((ext_vector_type(4)));
+constexpr int kRpStride = 20;  // floats per channel row of the replay's LDS tile (16 + 4: rows 4 banks apart)
 
 // Decode: one token per row; lane = channel, block = 256 channels of one row.
 template <typename IO, int NMAX>
@@ -229,32 +231,35 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
       }
     }
   }
-  if (c >= d) return;
+  // Threads past d compute on channel d - 1 and store nothing (every thread takes the block's
+  // barriers).
+  const bool live = c < d;
+  const int cl = live ? c : d - 1;
   const int64_t slot = static_cast<int64_t>(Bs) * d;  // ring slot stride of x and dt
-  const int64_t rc = static_cast<int64_t>(r) * d + c;
-  // the checkpoint as loaded: 16 fp32 state entries and 3 conv entries, or with LO their bf16
-  // copy, two 16-byte loads of the state (in the first 8 words) and one 8-byte load of the conv
-  // entries (in cw[0], cw[1])
-  uint32_t hw[NMAX], cw[kKS];
+  const int64_t rc = static_cast<int64_t>(r) * d + cl;
+  // The block's checkpoint rows are one contiguous run of its channels' states: the threads load
+  // it together in 16-byte pieces (consecutive lanes, consecutive pieces) and pass it through an
+  // LDS tile [256 channels][kRpStride floats], from which each lane takes its own channel (a lane
+  // loading its own 64 bytes would make every load instruction touch 64 separate pieces).  The
+  // committing step returns the new state the same way.
+  __shared__ __align__(16) float tile[kBlock * kRpStride];
+  const int c0 = static_cast<int>(blockIdx.x % nb) * kBlock;
+  const int nvalid = d - c0 < kBlock ? d - c0 : kBlock;  // the block's channels
+  const int64_t rc0 = static_cast<int64_t>(r) * d + c0;
+  constexpr int kPieces = LO ? NMAX / 8 : NMAX / 4;  // 16-byte pieces per channel
+  u32x4_lo sp[kPieces];
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    int i = static_cast<int>(threadIdx.x) + kBlock * k;  // piece i: channel i / kPieces
+    if (i >= nvalid * kPieces) i = nvalid * kPieces - 1;  // (a valid piece, loaded again)
+    sp[k] = LO ? reinterpret_cast<const u32x4_lo*>(ssm_lo + rc0 * NMAX)[i]
+               : reinterpret_cast<const u32x4_lo*>(ssm_state + rc0 * NMAX)[i];
+  }
+  uint32_t cw[kKS];  // the conv entries: 3 fp32, or with LO their bf16 copy in cw[0], cw[1]
   if (LO) {
-    const uint4* lrow = reinterpret_cast<const uint4*>(ssm_lo + rc * NMAX);
-#pragma unroll
-    for (int v = 0; v < NMAX / 8; ++v) {
-      const uint4 t = lrow[v];
-      hw[4 * v] = t.x; hw[4 * v + 1] = t.y; hw[4 * v + 2] = t.z; hw[4 * v + 3] = t.w;
-    }
-#pragma unroll
-    for (int i = NMAX / 2; i < NMAX; ++i) hw[i] = 0u;
     const uint2 c2 = reinterpret_cast<const uint2*>(conv_lo)[rc];
     cw[0] = c2.x; cw[1] = c2.y; cw[2] = 0u;
   } else {
-    const float4* srow = reinterpret_cast<const float4*>(ssm_state + rc * NMAX);
-#pragma unroll
-    for (int v = 0; v < NMAX / 4; ++v) {
-      const float4 t = srow[v];
-      hw[4 * v] = __float_as_uint(t.x); hw[4 * v + 1] = __float_as_uint(t.y);
-      hw[4 * v + 2] = __float_as_uint(t.z); hw[4 * v + 3] = __float_as_uint(t.w);
-    }
 #pragma unroll
     for (int m = 0; m < kKS; ++m) cw[m] = __float_as_uint(conv_state[rc * kKS + m]);
   }
@@ -270,21 +275,34 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
     dr[t] = ld_io_raw(dt_ring, tx * slot + rc);
     zr[t] = ld_io_raw(z, tz * zs + rc);
   }
-  const float4 w = reinterpret_cast<const float4*>(conv_w)[c];
-  const float cb = conv_b[c], dtb = dt_bias[c], Dc = D[c];
+  const float4 w = reinterpret_cast<const float4*>(conv_w)[cl];
+  const float cb = conv_b[cl], dtb = dt_bias[cl], Dc = D[cl];
   float4 al[NMAX / 4];
 #pragma unroll
-  for (int v = 0; v < NMAX / 4; ++v) al[v] = reinterpret_cast<const float4*>(A_log + static_cast<int64_t>(c) * NMAX)[v];
+  for (int v = 0; v < NMAX / 4; ++v) al[v] = reinterpret_cast<const float4*>(A_log + static_cast<int64_t>(cl) * NMAX)[v];
   // Every value loaded above is consumed here at once (an empty asm), so all the loads are in
   // flight together and the lane waits once: otherwise the compiler sinks the ring loads into
   // the steps that use them, behind the first step's waits (more round trips to memory).
-  asm volatile("" ::"v"(hw[0]), "v"(hw[1]), "v"(hw[2]), "v"(hw[3]), "v"(hw[4]), "v"(hw[5]), "v"(hw[6]), "v"(hw[7]),
-               "v"(hw[8]), "v"(hw[9]), "v"(hw[10]), "v"(hw[11]), "v"(hw[12]), "v"(hw[13]), "v"(hw[14]), "v"(hw[15]),
-               "v"(cw[0]), "v"(cw[1]), "v"(cw[2]), "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(dr[0]),
-               "v"(dr[1]), "v"(dr[2]), "v"(dr[3]), "v"(zr[0]), "v"(zr[1]), "v"(zr[2]), "v"(zr[3]));
+  asm volatile("" ::"v"(sp[0]), "v"(sp[1]), "v"(sp[kPieces - 1]), "v"(cw[0]), "v"(cw[1]), "v"(cw[2]), "v"(xr[0]),
+               "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(dr[0]), "v"(dr[1]), "v"(dr[2]), "v"(dr[3]), "v"(zr[0]),
+               "v"(zr[1]), "v"(zr[2]), "v"(zr[3]));
   asm volatile("" ::"v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(cb), "v"(dtb), "v"(Dc), "v"(al[0].x), "v"(al[0].y),
                "v"(al[0].z), "v"(al[0].w), "v"(al[1].x), "v"(al[1].y), "v"(al[1].z), "v"(al[1].w), "v"(al[2].x),
                "v"(al[2].y), "v"(al[2].z), "v"(al[2].w), "v"(al[3].x), "v"(al[3].y), "v"(al[3].z), "v"(al[3].w));
+  // the checkpoint pieces into the tile, then this lane's channel out of it
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const int i = static_cast<int>(threadIdx.x) + kBlock * k;
+    if (i < nvalid * kPieces)
+      *reinterpret_cast<u32x4_lo*>(tile + (i / kPieces) * kRpStride + (i % kPieces) * 4) = sp[k];
+  }
+  __syncthreads();
+  uint32_t hw[NMAX];
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const u32x4_lo v = *reinterpret_cast<const u32x4_lo*>(tile + static_cast<int>(threadIdx.x) * kRpStride + 4 * k);
+    hw[4 * k] = v[0]; hw[4 * k + 1] = v[1]; hw[4 * k + 2] = v[2]; hw[4 * k + 3] = v[3];
+  }
   float h[NMAX], cs[kKS], xs[W], ds[W], zv[W];
 #pragma unroll
   for (int t = 0; t < W; ++t) {
@@ -292,7 +310,7 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
     ds[t] = io_value<IO>(dr[t]);
     zv[t] = io_value<IO>(zr[t]);
   }
-  if (LO) {  // bf16 -> fp32: the value in the upper half of the word
+  if (LO) {  // bf16 -> fp32: the value in the upper half of the word (words 0..7 hold the state)
 #pragma unroll
     for (int i = 0; i < NMAX / 2; ++i) {
       h[2 * i] = __uint_as_float(hw[i] << 16);
@@ -344,26 +362,35 @@ __global__ void __launch_bounds__(kBlock) k_decode_replay(
         for (int e = 0; e < 4; ++e) g[v] = __builtin_fmaf(h[4 * v + e], cvv[t][4 * v + e], g[v]);
       }
       const float yp = (g[0] + g[1]) + (g[2] + g[3]);
-      st_io(y, (t - k0) * ys + rc, __builtin_fmaf(Dc, u, yp) * silu(zv[t]));
+      if (live) st_io(y, (t - k0) * ys + rc, __builtin_fmaf(Dc, u, yp) * silu(zv[t]));
     }
-    if (!LO && t == cstep) {  // the state after step t becomes the checkpoint
-      float* so = ssm_state + rc * NMAX;
+    if (!LO && t == cstep) {  // the state after step t becomes the checkpoint (uniform branch)
+      // this lane's channel into its own tile row (the row it read the checkpoint from), then the
+      // block's rows out together in 16-byte pieces, with their bf16 copy when one is kept
 #pragma unroll
-      for (int n = 0; n < NMAX; ++n) nt_store(h[n], so + n);
+      for (int k = 0; k < NMAX / 4; ++k)
+        *reinterpret_cast<f32x4_lo*>(tile + static_cast<int>(threadIdx.x) * kRpStride + 4 * k) =
+            f32x4_lo{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+      if (live) {
 #pragma unroll
-      for (int m = 0; m < kKS; ++m) conv_state[rc * kKS + m] = X(t - 2 + m);  // [X(t-2), X(t-1), X(t)]
-      if (ssm_lo_out != nullptr) {  // and its bf16 copy (uniform branch)
-        u32x4_lo* lo = reinterpret_cast<u32x4_lo*>(ssm_lo_out + rc * NMAX);
+        for (int m = 0; m < kKS; ++m) conv_state[rc * kKS + m] = X(t - 2 + m);  // [X(t-2), X(t-1), X(t)]
+      }
+      __syncthreads();
 #pragma unroll
-        for (int v = 0; v < NMAX / 8; ++v) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f32x2_lo pr = {h[8 * v + 2 * e], h[8 * v + 2 * e + 1]};
-            w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_lo));
+      for (int k = 0; k < NMAX / 4; ++k) {
+        const int i = static_cast<int>(threadIdx.x) + kBlock * k;  // piece i: channel i / 4
+        if (i < nvalid * 4) {
+          const f32x4_lo v = *reinterpret_cast<const f32x4_lo*>(tile + (i / 4) * kRpStride + (i % 4) * 4);
+          nt_store(v, reinterpret_cast<f32x4_lo*>(ssm_state + rc0 * NMAX) + i);
+          if (ssm_lo_out != nullptr) {
+            const f32x2_lo p0 = {v[0], v[1]}, p1 = {v[2], v[3]};
+            nt_store(u32x2_lo{__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2_lo)),
+                              __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2_lo))},
+                     reinterpret_cast<u32x2_lo*>(ssm_lo_out + rc0 * NMAX) + i);
           }
-          nt_store(u32x4_lo{w[0], w[1], w[2], w[3]}, lo + v);
         }
+      }
+      if (ssm_lo_out != nullptr && live) {
         const f32x2_lo c01 = {X(t - 2), X(t - 1)}, c2z = {X(t), 0.0f};
         nt_store(u32x2_lo{__builtin_bit_cast(uint32_t, __builtin_convertvector(c01, bf16x2_lo)),
                           __builtin_bit_cast(uint32_t, __builtin_convertvector(c2z, bf16x2_lo))},
