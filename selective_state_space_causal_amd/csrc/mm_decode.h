@@ -52,8 +52,10 @@ __global__ void __launch_bounds__(kBlock) k_decode(
 // Decode, streaming layout: G = NMAX/4 lanes per channel, each lane owning four
 // consecutive state entries, so every state load/store instruction of a wave moves
 // one contiguous 1 KiB run.  The fp32 state is touched exactly once in each
-// direction; it is stored with nontemporal stores (it is not reused by this kernel)
-// and loaded with plain loads (measured faster here than nontemporal ones).  The readout is summed across
+// direction, with nontemporal loads and stores (it is not reused by this kernel).  In a
+// stream of back-to-back steps the nontemporal loads are the faster choice (measured at batch
+// 256, d_inner 8192: 61.8 against 67.7 us per step in a HIP graph), though a single step
+// after a cache flush is about 5% slower with them.  The readout is summed across
 // the G lanes of a channel with lane exchanges.  Requires N == NMAX, 16-byte aligned
 // ssm_state, A_log and conv_w, and B/C rows aligned for 4-element vector loads.
 
@@ -113,7 +115,7 @@ __global__ void __launch_bounds__(kBlock) k_decode_vec(
     const int r = (r0 + i < Bs) ? r0 + i : Bs - 1;  // rows past Bs load a valid row and store nothing
     const float* srow = ssm_state + (static_cast<int64_t>(r) * d + c) * NMAX + 4 * q;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[i][e] = srow[e];
+    for (int e = 0; e < 4; ++e) h[i][e] = nt_load(srow + e);
     ld4_io(B + static_cast<int64_t>(r) * NMAX + 4 * q, bq[i]);
     ld4_io(C + static_cast<int64_t>(r) * NMAX + 4 * q, cq[i]);
   }
