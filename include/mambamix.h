@@ -47,7 +47,8 @@
  *    then.  MM_ERR_HIP reports a failed kernel launch.
  *  - Preconditions NOT checked (checking would need a device sync):
  *    cu_seqlens[0] == 0, cu_seqlens non-decreasing, cu_seqlens[S] == T.
- *    Violating them is undefined behaviour.
+ *    Violating them is undefined behaviour (the kernels may read and write outside
+ *    the arrays).  mamba_mixer_check_cu_seqlens checks a host copy of the array.
  */
 #ifndef MAMBAMIX_H
 #define MAMBAMIX_H
@@ -418,6 +419,12 @@ const char* mamba_mixer_status_string(int status);
 
 /* Library version, e.g. "libmambamix 0.1 gfx950".  Host only. */
 const char* mamba_mixer_version(void);
+
+/* The cu_seqlens preconditions of every call that takes the array, checked on a HOST copy of
+ * it (cu_seqlens_host [S+1]): cu[0] == 0, cu non-decreasing, cu[S] == T.  MM_OK, or MM_ERR_DIM
+ * for a violation or negative S or T, MM_ERR_NULL for a NULL array.  For callers that want the
+ * check (the calls themselves never read the array on the host).  Host only. */
+int mamba_mixer_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t S, int64_t T);
 
 #ifdef __cplusplus
 }

@@ -90,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.mamba_mixer_status_string.restype = ctypes.c_char_p
     lib.mamba_mixer_version.argtypes = []
     lib.mamba_mixer_version.restype = ctypes.c_char_p
+    lib.mamba_mixer_check_cu_seqlens.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
+    lib.mamba_mixer_check_cu_seqlens.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -100,6 +102,25 @@ def status_string(code: int) -> str:
 
 def version() -> str:
     return load().mamba_mixer_version().decode()
+
+
+# MAMBAMIX_CHECK_CU=1 makes every call check its cu_seqlens first (a device-to-host copy and a
+# sync per call: for debugging).
+CHECK_CU = os.environ.get("MAMBAMIX_CHECK_CU", "") == "1"
+
+
+def check_cu_seqlens(cu_seqlens, T: int) -> None:
+    """Raise MambaMixError unless cu_seqlens [S+1] (device or host int32) starts at 0, never
+    decreases and ends at T: the precondition of every call that takes it."""
+    import numpy as np
+
+    cu = np.ascontiguousarray(cu_seqlens.detach().cpu().numpy() if hasattr(cu_seqlens, "detach") else cu_seqlens,
+                              dtype=np.int32)
+    if cu.ndim != 1 or cu.size < 1:
+        raise ValueError("cu_seqlens: expected a 1-D array of S+1 >= 1 entries")
+    rc = load().mamba_mixer_check_cu_seqlens(cu.ctypes.data_as(ctypes.c_void_p), cu.size - 1, int(T))
+    if rc != 0:
+        raise MambaMixError(rc, "mamba_mixer_check_cu_seqlens")
 
 
 def plan(S: int, T: int, d: int, N: int, K: int = CONV_K, chunk_len: int = 0, engine: int = ENGINE_AUTO) -> dict:
@@ -186,6 +207,8 @@ def prefill(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens, conv_
         _check(t, (d,), torch.float32, n)
     _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
     _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    if CHECK_CU:
+        check_cu_seqlens(cu_seqlens, T)
     _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
     _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
     if y is None:
@@ -235,6 +258,8 @@ def prefill_noalloc(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlen
         _check(t, (d,), torch.float32, n)
     _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
     _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    if CHECK_CU:
+        check_cu_seqlens(cu_seqlens, T)
     _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
     _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
     if y is None:
@@ -282,6 +307,13 @@ def prefill_train(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqlens,
         _check(t, (T, d), io, n)
     for t, n in ((B, "B"), (C, "C")):
         _check(t, (T, N), io, n)
+    _check(A_log, (d, N), torch.float32, "A_log")
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (conv_b, "conv_b")):
+        _check(t, (d,), torch.float32, n)
+    _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
+    _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    if CHECK_CU:
+        check_cu_seqlens(cu_seqlens, T)
     _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
     _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
     if y is None:
@@ -331,6 +363,8 @@ def prefill_backward(x, z, dt, B, C, A_log, D, dt_bias, conv_w, conv_b, cu_seqle
         _check(t, (d,), torch.float32, n)
     _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
     _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    if CHECK_CU:
+        check_cu_seqlens(cu_seqlens, T)
     _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
     if ssm_state is not None:
         _check(ssm_state, (S, d, N), torch.float32, "ssm_state")
@@ -389,6 +423,8 @@ def project(x, conv_w, conv_b, cu_seqlens, conv_state, w_x, w_dt, dt=None, B=Non
     _check(conv_w, (d, CONV_K), torch.float32, "conv_w")
     _check(conv_b, (d,), torch.float32, "conv_b")
     _check(cu_seqlens, (S + 1,), torch.int32, "cu_seqlens")
+    if CHECK_CU:
+        check_cu_seqlens(cu_seqlens, T)
     _check(conv_state, (S, d, CONV_K - 1), torch.float32, "conv_state")
     _check(w_x, (d, P), torch.bfloat16, "w_x")
     _check(w_dt, (R, d), torch.bfloat16, "w_dt")

@@ -654,6 +654,15 @@ const char* mamba_mixer_status_string(int status) {
 
 const char* mamba_mixer_version(void) { return "libmambamix 0.4 gfx950"; }
 
+int mamba_mixer_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t S, int64_t T) {
+  if (S < 0 || T < 0) return MM_ERR_DIM;
+  if (cu_seqlens_host == nullptr) return MM_ERR_NULL;
+  if (cu_seqlens_host[0] != 0 || cu_seqlens_host[S] != T) return MM_ERR_DIM;
+  for (int32_t s = 0; s < S; ++s)
+    if (cu_seqlens_host[s + 1] < cu_seqlens_host[s]) return MM_ERR_DIM;
+  return MM_OK;
+}
+
 int mamba_mixer_prefill_plan(int32_t S, int64_t T, int32_t d, int32_t N, int32_t K, int64_t chunk_len,
                              int32_t engine, int64_t* chunk_len_out, int32_t* engine_out, size_t* workspace_out,
                              int32_t* kernels_out) {

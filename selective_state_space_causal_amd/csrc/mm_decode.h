@@ -184,9 +184,11 @@ __global__ void __launch_bounds__(kBlock) k_decode_vec(
 // Layout: one lane per channel with its 16 state entries in registers, 256 channels
 // of one row per block.  x and dt of every window step are one coalesced load per
 // row; B and C of a row are the same for every lane, so they come through the
-// scalar unit; the state moves as four 16-byte loads per lane.  Few, wide vector
-// loads per (row, channel) keep this kernel on the HBM roofline where a
-// lanes-per-channel layout spent its time issuing small loads.  W <= 4, N = 16.
+// scalar unit; the block's checkpoint rows, one contiguous run, move between memory and
+// an LDS tile in coalesced 16-byte pieces, and each lane takes its channel's 16 entries
+// from the tile.  The per-step arithmetic stays in one lane, as in the eager step's
+// order (a layout of several lanes per channel spent its time on the exchanges).
+// W <= 4, N = 16.
 // Window steps 0..k1 are taken from the checkpoint; steps k0..k1 write their output
 // (z, C and y of step t at slot t - k0 of the z/C/y arrays, slot strides zs, cs_, ys);
 // if 0 <= cstep <= k1 the state after step cstep becomes the checkpoint.

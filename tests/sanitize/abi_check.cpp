@@ -112,6 +112,15 @@ static void sweep_plans() {
         for (int64_t T : I64) (void)mamba_mixer_project_workspace_bytes(T, d, N, R);
   for (int code : {INT_MIN, -8, -7, -1, 0, 1, INT_MAX}) EXPECT(mamba_mixer_status_string(code) != nullptr, "status");
   EXPECT(mamba_mixer_version() != nullptr && std::strlen(mamba_mixer_version()) > 0, "version");
+  {  // the host check of cu_seqlens reads exactly S + 1 entries (the vectors are sized to that)
+    const std::vector<int32_t> ok{0, 3, 3, 10}, bad{0, 5, 4, 10}, one{0};
+    EXPECT(mamba_mixer_check_cu_seqlens(ok.data(), 3, 10) == MM_OK, "cu ok");
+    EXPECT(mamba_mixer_check_cu_seqlens(bad.data(), 3, 10) == MM_ERR_DIM, "cu decreasing");
+    EXPECT(mamba_mixer_check_cu_seqlens(ok.data(), 3, 9) == MM_ERR_DIM, "cu end");
+    EXPECT(mamba_mixer_check_cu_seqlens(one.data(), 0, 0) == MM_OK, "cu empty");
+    EXPECT(mamba_mixer_check_cu_seqlens(one.data(), -1, 0) == MM_ERR_DIM, "cu S");
+    EXPECT(mamba_mixer_check_cu_seqlens(nullptr, 2, 10) == MM_ERR_NULL, "cu null");
+  }
   std::printf("plan queries: %ld calls\n", calls);
 }
 

@@ -359,3 +359,26 @@ def test_plain_c_prefill_entry_point(shape):
     assert_within(host(y), yr, "bf16", f"plain C {shape} y")
     assert_within(host(ss), ssr, "bf16", f"plain C {shape} ssm_state")
     assert np.array_equal(host(cs), csr)
+
+
+def test_check_cu_seqlens_before_calls():
+    """With the binding's cu_seqlens check on, a call whose cu_seqlens does not end at T raises
+    before anything is launched (the array used here stays inside the buffers, so the call would
+    be harmless even unchecked), and a valid one runs as usual."""
+    lens, d, N = [5, 7], 32, 16
+    T = sum(lens)
+    tok = inputs.prefill_inputs(4, T, d, N, "f32")
+    p = inputs.params_per_channel(4, d, N, 4)
+    cs, ss = inputs.zero_states(len(lens), d, N, 4)
+    args = [dev(tok[k]) for k in ("x", "z", "dt", "B", "C")] + [dev(p[k]) for k in PRM]
+    saved = mm.CHECK_CU
+    mm.CHECK_CU = True
+    try:
+        bad = dev(np.array([0, 5, T - 1], dtype=np.int32))
+        with pytest.raises(mm.MambaMixError):
+            mm.prefill(*args, bad, dev(cs), dev(ss))
+        y = mm.prefill(*args, dev(inputs.cu_from_lengths(lens)), dev(cs), dev(ss))
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(host(y)))
+    finally:
+        mm.CHECK_CU = saved

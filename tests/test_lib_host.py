@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import selective_state_space_causal_amd as mm
@@ -394,3 +395,24 @@ def test_replay_dual_host_checks(lib):
     assert lib.mamba_mixer_replay_checkpoint_lo(c[0], c[1], c[0], c[3], 2, 64, 16, 4, None) == MM_ERR_ALIAS
     assert lib.mamba_mixer_replay_checkpoint_lo(c[0], c[1], c[2], None, 2, 64, 16, 4, None) == MM_ERR_NULL
     assert lib.mamba_mixer_replay_checkpoint_lo(*c, 0, 64, 16, 4, None) == 0
+
+
+def test_check_cu_seqlens(lib):
+    """The host check of the cu_seqlens preconditions (the calls never read the array on the
+    host): starts at 0, never decreases, ends at T."""
+    def rc(cu, T, S=None):
+        a = np.ascontiguousarray(cu, dtype=np.int32)
+        return lib.mamba_mixer_check_cu_seqlens(a.ctypes.data_as(ctypes.c_void_p),
+                                                a.size - 1 if S is None else S, T)
+    assert rc([0, 3, 3, 10], 10) == 0
+    assert rc([0], 0) == 0                       # no sequences
+    assert rc([0, 0, 0], 0) == 0                 # empty sequences only
+    assert rc([1, 3, 10], 10) == MM_ERR_DIM      # does not start at 0
+    assert rc([0, 5, 4, 10], 10) == MM_ERR_DIM   # decreases
+    assert rc([0, 3, 9], 10) == MM_ERR_DIM       # does not end at T
+    assert rc([0, 3, 10], -1) == MM_ERR_DIM
+    assert rc([0, 3, 10], 10, S=-1) == MM_ERR_DIM
+    assert lib.mamba_mixer_check_cu_seqlens(None, 2, 10) == MM_ERR_NULL
+    mm.check_cu_seqlens(np.array([0, 4, 9], dtype=np.int32), 9)
+    with pytest.raises(mm.MambaMixError):
+        mm.check_cu_seqlens(np.array([0, 9, 4], dtype=np.int32), 4)
