@@ -574,6 +574,12 @@ size_t proj_in_lds_table(int nt, std::integer_sequence<int, I...>) {
   return t[nt - 1];
 }
 size_t proj_in_lds(int nt) { return proj_in_lds_table(nt, std::make_integer_sequence<int, kProjMaxP / 16>{}); }
+template <int... I>
+int proj_in_threads_table(int nt, std::integer_sequence<int, I...>) {
+  static const int t[] = {PinGeo<I + 1>::THREADS...};
+  return t[nt - 1];
+}
+int proj_in_threads(int nt) { return proj_in_threads_table(nt, std::make_integer_sequence<int, kProjMaxP / 16>{}); }
 KernDt proj_dt_kernel(int kr) { return proj_dt_table(kr, std::make_integer_sequence<int, kProjMaxR / kProjK>{}); }
 
 struct ProjPlan {
@@ -1072,7 +1078,7 @@ int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b,
                           static_cast<int>(lds)) != hipSuccess)
     return MM_ERR_HIP;
   evs.mark(st);
-  hipLaunchKernelGGL(kin, dim3(static_cast<unsigned>(cdiv(T, kPinTok))), dim3(kPinThreads), lds, st,
+  hipLaunchKernelGGL(kin, dim3(static_cast<unsigned>(cdiv(T, kPinTok))), dim3(proj_in_threads(nt)), lds, st,
                      static_cast<const uint16_t*>(x), conv_w, conv_b, cu_seqlens, conv_state, wxP, dth, dtl,
                      static_cast<uint16_t*>(B), static_cast<uint16_t*>(C), S, T, d, N, R, p.Rp, p.dk / kProjK);
   // dt: about kPdtWGs workgroups, each a 128-channel block and a run of 16-token tiles

@@ -17,12 +17,12 @@
 //
 // The two products have opposite memory profiles, so each has a kernel of its own:
 //  * k_proj_in reads x (T d bf16, the layer's large input) and writes only R + 2N values per
-//    token: a read-streaming kernel.  A workgroup of eight waves takes 64 tokens: four 16-token
-//    row tiles times two halves of the K range.  Per K stage the workgroup's threads load the x
-//    rows its tokens need (t-3 .. t) with row-contiguous 16-byte loads, the stage's conv
-//    parameters and its w_x operands, several stages ahead of their use, into a double-buffered
-//    LDS area; each lane then computes u for its token and 8 channels per MFMA K step and issues
-//    the MFMAs of all output columns.  The halves' sums are added in a fixed order through LDS
+//    token: a read-streaming kernel.  A workgroup takes 64 tokens: four 16-token row tiles times
+//    KP parts of the K range (four parts, 16 waves, up to 160 output columns; two beyond).  Per
+//    K stage the workgroup's threads load the x rows its tokens need (t-3 .. t) with
+//    row-contiguous 16-byte loads, the stage's conv parameters and its w_x operands, several
+//    stages ahead of their use, into a double-buffered LDS area; each lane then computes u for
+//    its token and 8 channels per MFMA K step and issues the MFMAs of all output columns.  The parts' sums are added in a fixed order through LDS
 //    (deterministic).  B and C go to their outputs, dt_in to the workspace as bf16 high and low
 //    parts [T][Rp] (zero past R).
 //  * k_proj_dt writes dt (T d bf16) from dt_in (T Rp, small): a write-streaming kernel with
@@ -52,37 +52,39 @@ constexpr int kProjK = 32;      // K per MFMA
 // k_proj_in
 constexpr int kPinRT = 4;                      // 16-token row tiles per workgroup
 constexpr int kPinTok = 16 * kPinRT;           // tokens per workgroup
-constexpr int kPinHalves = 2;                  // K halves
-constexpr int kPinWaves = kPinRT * kPinHalves;
-constexpr int kPinThreads = kPinWaves * kWave;
+constexpr int kPinPartThreads = kPinRT * kWave;  // threads per K part (one wave per row tile)
 constexpr int kPinXRows = kPinTok + kKS;       // staged x rows: t-3 .. t+63
 
-// Stage geometry of k_proj_in for NT output column tiles.  A stage holds KC channels (64, so that
-// every x row piece is a whole 128-byte line; 32 for the widest outputs, whose w_x operands
-// would not fit twice in LDS otherwise) for each K half: x [kPinXRows][KC + 8] bf16, the conv
-// weights [KC] float4 and biases [KC] float of those channels, then the KC / 32 MFMA K steps'
-// w_x operands [K step][4 K groups][Pp][8] bf16.
+// Stage geometry of k_proj_in for NT output column tiles.  The K range is split into KP parts,
+// each taken by kPinRT waves (one per 16-token row tile): four parts up to 10 column tiles
+// (16 waves per workgroup, four per SIMD), two for the widest outputs, whose operands would not
+// fit four times in LDS.  A stage holds KC channels (32 with four parts; 64 with two, so that
+// every x row piece is a whole 128-byte line, or 32 for the widest outputs) for each part: x
+// [kPinXRows][KC + 8] bf16, the conv weights [KC] float4 and biases [KC] float of those
+// channels, then the KC / 32 MFMA K steps' w_x operands [K step][4 K groups][Pp][8] bf16.
 template <int NT>
 struct PinGeo {
   static constexpr int Pp = NT * 16;
-  static constexpr int KC = NT <= 12 ? 64 : 32;
+  static constexpr int KP = NT <= 10 ? 4 : 2;              // K parts
+  static constexpr int THREADS = KP * kPinPartThreads;
+  static constexpr int KC = KP == 4 ? 32 : (NT <= 12 ? 64 : 32);
   static constexpr int SUB = KC / kProjK;                  // MFMA K steps per stage
   static constexpr int XSTRIDE = KC + 8;                   // bf16 per staged x row
-  static constexpr int XP = kPinXRows * KC / 8;            // 16-byte pieces per half: x,
+  static constexpr int XP = kPinXRows * KC / 8;            // 16-byte pieces per part: x,
   static constexpr int CWP = KC;                           // conv weights,
   static constexpr int CBP = KC / 4;                       // biases,
   static constexpr int WP = SUB * 4 * Pp;                  // w_x operands
   static constexpr int HP = XP + CWP + CBP + WP;
-  static constexpr int CWOFF = kPinXRows * XSTRIDE * 2;    // byte offsets within a half
+  static constexpr int CWOFF = kPinXRows * XSTRIDE * 2;    // byte offsets within a part
   static constexpr int CBOFF = CWOFF + KC * 16;
   static constexpr int WOFF = CBOFF + KC * 4;
-  static constexpr int HB = WOFF + WP * 16;                // bytes per half
-  static constexpr int L = (HP + kPinThreads / kPinHalves - 1) / (kPinThreads / kPinHalves);  // loads per thread and stage
-  static constexpr int D = NT <= 6 ? 4 : 1;                // stages in flight (1 or 4)
+  static constexpr int HB = WOFF + WP * 16;                // bytes per part
+  static constexpr int L = (HP + kPinPartThreads - 1) / kPinPartThreads;  // loads per thread and stage
+  static constexpr int D = KP == 2 && NT <= 6 ? 4 : 1;     // stages in flight
 };
 template <int NT>
-inline size_t pin_lds_bytes_t() {  // two stage buffers (+ a dummy slot); the halves' sums reuse them
-  const size_t stage = static_cast<size_t>(2) * kPinHalves * PinGeo<NT>::HB + 16;
+inline size_t pin_lds_bytes_t() {  // two stage buffers (+ a dummy slot); the parts' sums reuse them
+  const size_t stage = static_cast<size_t>(2) * PinGeo<NT>::KP * PinGeo<NT>::HB + 16;
   const size_t red = static_cast<size_t>(kPinRT) * NT * kWave * 16;
   return stage > red ? stage : red;
 }
@@ -160,23 +162,24 @@ __global__ void __launch_bounds__(kBlock) k_proj_pack(const uint16_t* __restrict
 
 // [dt_in | B | C] = u x w_x for 64 tokens per workgroup, NT = Pp / 16 output column tiles (a
 // template argument: the MFMAs run without guards); nks = dk / 32 MFMA K steps, grouped in
-// stages of G::SUB.  Wave w takes row tile w % 4 and K half w / 4 (the first half of the
-// stages, then the rest).  Stage g holds, for each half, everything its g-th stage needs (see
-// PinGeo); the four waves of a half share its w_x operands.  The 512 threads load stage g + D
+// stages of G::SUB.  Wave w takes row tile w % 4 and K part w / 4 (a consecutive run of the
+// stages).  Stage g holds, for each part, everything its g-th stage needs (see PinGeo); the four
+// waves of a part share its w_x operands.  The workgroup's threads load stage g + D
 // into registers while stage g runs; those are the only global loads of the loop (bar the
 // conv state of a sequence's first tokens), so waiting for stage g, which was issued first,
 // never waits for a later one.  Two LDS stage buffers and one barrier per stage.  LDS
-// (dynamic): the stage buffers; after the K loop, the second half's accumulators
+// (dynamic): the stage buffers; after the K loop, one part's accumulators
 // [row tile][NT][64 lanes] floatx4.
 template <int NT>
-__global__ void __launch_bounds__(kPinThreads) k_proj_in(
+__global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
     const uint16_t* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     const int32_t* __restrict__ cu, const float* __restrict__ conv_state, const uint16_t* __restrict__ wxP,
     uint16_t* __restrict__ dth, uint16_t* __restrict__ dtl, uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int S, int64_t T, int d, int N, int R, int Rp, int nks) {
   extern __shared__ __align__(16) unsigned char smem[];
   using G = PinGeo<NT>;
-  constexpr int Pp = G::Pp, HB = G::HB, HP = G::HP, L = G::L, D = G::D, SUB = G::SUB, KC = G::KC;
+  constexpr int Pp = G::Pp, HB = G::HB, HP = G::HP, L = G::L, D = G::D, SUB = G::SUB, KC = G::KC, KP = G::KP;
+  constexpr int THREADS = G::THREADS;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
@@ -185,10 +188,14 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
   const int kg = lane >> 4;   // 8-wide K group
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPinTok;
   const int64_t d64 = d;
+  // the nstg stages split into KP consecutive runs, the last ones one stage longer when they do
+  // not divide evenly; the loop runs nst (the longest run) stages
   const int nstg = (nks + SUB - 1) / SUB;
-  const int len0 = nstg / 2;
-  const int nst = nstg - len0;  // loop stages (the second half's; the first has len0 <= nst)
-  const int sbeg = h == 0 ? 0 : len0, slen = h == 0 ? len0 : nst;
+  const int sbase = nstg / KP, srem = nstg % KP;
+  auto part_len = [&](int q) { return sbase + (q >= KP - srem ? 1 : 0); };
+  auto part_beg = [&](int q) { return q * sbase + (q > KP - srem ? q - (KP - srem) : 0); };
+  const int nst = sbase + (srem > 0 ? 1 : 0);
+  const int sbeg = part_beg(h), slen = part_len(h);
 
   // this lane's token and its sequence (rows past T compute on a valid token and store nothing)
   int64_t t = t0 + rt * 16 + row;
@@ -197,25 +204,25 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
   const int64_t back = t - cu[s];  // tokens of the sequence before t
   const float* cs = conv_state + static_cast<int64_t>(s) * d64 * kKS;
 
-  // Waves 0-3 stage the first half's pieces and waves 4-7 the second's, so that a thread's stage
-  // index is wave-uniform.  The pieces of thread i of a half are p = i + 256 k (k < L): the x
+  // The four waves of part q stage part q's pieces, so that a thread's stage index is
+  // wave-uniform.  The pieces of thread i of a part are p = i + 256 k (k < L): the x
   // pieces (staged row p / (KC/8) = token t0 - 3 + p / (KC/8) clamped into 0 .. T-1, channels
   // 8 (p % (KC/8)) .. of the stage), KC conv weight rows (float4), KC / 4 pieces of four biases,
   // and the stage's w_x operand pieces (contiguous).  Each piece keeps a 64-bit base, the byte
-  // offset of its half's first stage, the bytes it advances per stage and the largest offset it
+  // offset of its part's first stage, the bytes it advances per stage and the largest offset it
   // may read: channels past d read clamped, valid addresses (their u is forced to 0); slots past
-  // the half's pieces load a valid address and go to a dummy slot.  (Offsets fit 32 bits for
+  // the part's pieces load a valid address and go to a dummy slot.  (Offsets fit 32 bits for
   // d <= 2^22, which the host checks.)
-  const int hs = w / kPinRT;                       // the half this wave stages (wave-uniform)
-  const int ht = tid - hs * (kPinThreads / kPinHalves);
+  const int hs = w / kPinRT;                       // the part this wave stages (wave-uniform)
+  const int ht = tid - hs * kPinPartThreads;
   const unsigned char* pbase[L];
   uint32_t poff[L], pinc[L], plim[L];
   int pdst[L];
   {
-    const int kb = (hs == 0 ? 0 : len0) * KC;  // the half's first channel
+    const int kb = part_beg(hs) * KC;  // the part's first channel
 #pragma unroll
     for (int k = 0; k < L; ++k) {
-      const int q = ht + (kPinThreads / kPinHalves) * k;
+      const int q = ht + kPinPartThreads * k;
       const bool real = q < HP;
       const int p = real ? q : G::XP + G::CWP + G::CBP;  // a w_x piece
       pdst[k] = hs * HB;
@@ -250,9 +257,9 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
       if (!real) pdst[k] = -1;  // staged nowhere
     }
   }
-  // stage g of a half of len stages (clamped to its last stage)
+  // stage g of a part of len stages (clamped to its last stage)
   auto rel_stage = [&](int g, int len) { return len > 0 ? (g < len ? g : len - 1) : 0; };
-  const int hlen = hs == 0 ? len0 : nst;
+  const int hlen = part_len(hs);
   auto load_stage = [&](int g, u32x4_t (&pf)[L]) {
     const uint32_t rel = static_cast<uint32_t>(rel_stage(g, hlen));  // wave-uniform
 #pragma unroll
@@ -261,9 +268,9 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
       pf[k] = *reinterpret_cast<const u32x4_t*>(pbase[k] + (o < plim[k] ? o : plim[k]));
     }
   };
-  // (pieces past both halves go to a 16-byte slot after the two stage buffers: no branch, so the
+  // (pieces past a part's own go to a 16-byte slot after the two stage buffers: no branch, so the
   // compiler's count of outstanding loads stays exact)
-  unsigned char* dummy = smem + 2 * kPinHalves * HB;
+  unsigned char* dummy = smem + 2 * KP * HB;
   auto write_stage = [&](unsigned char* buf, const u32x4_t (&pf)[L]) {
 #pragma unroll
     for (int k = 0; k < L; ++k) *reinterpret_cast<u32x4_t*>(pdst[k] >= 0 ? buf + pdst[k] : dummy) = pf[k];
@@ -273,7 +280,7 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // MFMA K step ks, the sub-th of the stage in buf (this wave's half)
+  // MFMA K step ks, the sub-th of the stage in buf (this wave's part)
   auto kstep = [&](const unsigned char* buf, int ks, int sub, auto state) {
     constexpr bool STATE = decltype(state)::value;
     const unsigned char* hb = buf + h * HB;
@@ -330,16 +337,31 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
     conv_e(std::integral_constant<int, 6>{});
     conv_e(std::integral_constant<int, 7>{});
     const u32x4_t* wo = reinterpret_cast<const u32x4_t*>(hb + G::WOFF) + (sub * 4 + kg) * Pp + row;
-    u32x4_t wb[NT];
+    if constexpr (KP == 2) {
+      u32x4_t wb[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) wb[j] = wo[j * 16];
-    // the high parts over all column tiles, then the low parts: consecutive MFMAs are independent
+      for (int j = 0; j < NT; ++j) wb[j] = wo[j * 16];
+      // the high parts over all column tiles, then the low parts: consecutive MFMAs are independent
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
+      for (int j = 0; j < NT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
+      for (int j = 0; j < NT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wb[j]), acc[j], 0, 0, 0);
+    } else {
+      // four waves per SIMD leave 128 VGPRs: each column tile's operands are held for two MFMAs
+      // only, the high part of tile j issued between the two of tile j - 1
+      u32x4_t wp = wo[0];
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, __builtin_bit_cast(bf16x8_t, wp), acc[0], 0, 0, 0);
+#pragma unroll
+      for (int j = 1; j < NT; ++j) {
+        const u32x4_t wn = wo[j * 16];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, __builtin_bit_cast(bf16x8_t, wn), acc[j], 0, 0, 0);
+        acc[j - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wp), acc[j - 1], 0, 0, 0);
+        wp = wn;
+      }
+      acc[NT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, __builtin_bit_cast(bf16x8_t, wp), acc[NT - 1], 0, 0, 0);
+    }
   };
 
   // A wave holding one of a sequence's first three tokens takes the loop that reads the conv state.
@@ -354,7 +376,7 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
     auto stage = [&](int g0, auto uc) {
       constexpr int u = decltype(uc)::value;
       const int g = g0 + u;
-      unsigned char* buf = smem + (g & 1) * (kPinHalves * HB);
+      unsigned char* buf = smem + (g & 1) * (KP * HB);
       write_stage(buf, pf[u]);  // waits for stage g's loads only (the earliest outstanding)
       load_stage(g + D, pf[u]);  // near the end a harmless repeat (clamped)
       __syncthreads();  // stage g visible; every wave done with stage g - 1 (the other buffer)
@@ -378,20 +400,22 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
   if (__any(back < kKS)) kloop(std::true_type{});
   else kloop(std::false_type{});
 
-  // The halves' sums: the second half leaves its accumulators in LDS and the first adds them to
-  // its own (first + second).  The sums then go through a float tile [64 tokens][OS] in LDS,
-  // so that every output leaves in contiguous runs: the workgroup's 64 rows of B, of C and of
-  // dt_in's two parts are each one contiguous block.
+  // The parts' sums, in a fixed order through one LDS area: the last part leaves its
+  // accumulators there, each part before it adds its own to them and leaves the sum, and the
+  // first part ends with (((part KP-1 + part KP-2) + ...) + part 0).  The sums then go through a
+  // float tile [64 tokens][OS] in LDS, so that every output leaves in contiguous runs: the
+  // workgroup's 64 rows of B, of C and of dt_in's two parts are each one contiguous block.
   floatx4_t* red = reinterpret_cast<floatx4_t*>(smem);
-  __syncthreads();  // every wave's K loop done: the stage buffers become the partial sums
-  if (h == 1) {
+  for (int q = KP - 1; q >= 0; --q) {
+    __syncthreads();  // the K loop done (first pass), or part q + 1's sums written
+    if (h == q) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) red[(static_cast<size_t>(rt) * NT + j) * kWave + lane] = acc[j];
-  }
-  __syncthreads();
-  if (h == 0) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] += red[(static_cast<size_t>(rt) * NT + j) * kWave + lane];
+      for (int j = 0; j < NT; ++j) {
+        floatx4_t& r = red[(static_cast<size_t>(rt) * NT + j) * kWave + lane];
+        if (q < KP - 1) acc[j] += r;
+        if (q > 0) r = acc[j];
+      }
+    }
   }
   __syncthreads();  // the partial sums are read: the area becomes the output tile
   const int OS = pin_out_stride(Pp, Rp);
@@ -411,7 +435,7 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
     const int npc = Rp / 8;
     uint16_t* hb = dth + t0 * Rp;
     uint16_t* lb = dtl + t0 * Rp;
-    for (int e = tid; e < nrows * npc; e += kPinThreads) {
+    for (int e = tid; e < nrows * npc; e += THREADS) {
       const int r = e / npc, c = (e % npc) * 8;
       const float4 a = *reinterpret_cast<const float4*>(ot + r * OS + c);
       const float4 b = *reinterpret_cast<const float4*>(ot + r * OS + c + 4);
@@ -434,7 +458,7 @@ __global__ void __launch_bounds__(kPinThreads) k_proj_in(
   {
     uint16_t* bb = B + t0 * N;
     uint16_t* cb_ = C + t0 * N;
-    for (int e = tid; e < nrows * N; e += kPinThreads) {
+    for (int e = tid; e < nrows * N; e += THREADS) {
       const int r = e / N, c = e % N;
       bb[e] = bf16_bits(ot[r * OS + R + c]);
       cb_[e] = bf16_bits(ot[r * OS + R + N + c]);
