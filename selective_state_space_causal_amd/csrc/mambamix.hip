@@ -555,7 +555,8 @@ int launch_backward(const BwdPlan& p, const BwdArgs& a, char* ws, hipStream_t st
 
 // the projection kernels for NT output column tiles (1 .. 18) and KR K steps of dt_in (1 .. 8)
 using KernIn = void (*)(const uint16_t*, const float*, const float*, const int32_t*, const float*, const uint16_t*,
-                        uint16_t*, uint16_t*, uint16_t*, uint16_t*, int, int64_t, int, int, int, int, int);
+                        uint16_t*, uint16_t*, uint16_t*, uint16_t*, int, int64_t, int, int, int, int, int, const float*,
+                       int);
 using KernDt = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, int, int);
 template <int... I>
 KernIn proj_in_table(int nt, std::integer_sequence<int, I...>) {
@@ -1080,7 +1081,9 @@ int mamba_mixer_project(const void* x, const float* conv_w, const float* conv_b,
   evs.mark(st);
   hipLaunchKernelGGL(kin, dim3(static_cast<unsigned>(cdiv(T, kPinTok))), dim3(proj_in_threads(nt)), lds, st,
                      static_cast<const uint16_t*>(x), conv_w, conv_b, cu_seqlens, conv_state, wxP, dth, dtl,
-                     static_cast<uint16_t*>(B), static_cast<uint16_t*>(C), S, T, d, N, R, p.Rp, p.dk / kProjK);
+                     static_cast<uint16_t*>(B), static_cast<uint16_t*>(C), S, T, d, N, R, p.Rp, p.dk / kProjK,
+                     reinterpret_cast<const float*>(reinterpret_cast<uintptr_t>(conv_state) & ~static_cast<uintptr_t>(15)),
+                     aligned(conv_state, 16) ? 1 : 0);
   // dt: about kPdtWGs workgroups, each a 128-channel block and a run of 16-token tiles
   const int64_t ntt = cdiv(T, 16);
   const int64_t G = std::max<int64_t>(1, std::min<int64_t>(cdiv(kPdtWGs, ncb), cdiv(ntt, kPdtWaves)));

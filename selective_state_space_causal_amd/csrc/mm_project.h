@@ -61,7 +61,10 @@ constexpr int kPinXRows = kPinTok + kKS;       // staged x rows: t-3 .. t+63
 // fit four times in LDS.  A stage holds KC channels (32 with four parts; 64 with two, so that
 // every x row piece is a whole 128-byte line, or 32 for the widest outputs) for each part: x
 // [kPinXRows][KC + 8] bf16, the conv weights [KC] float4 and biases [KC] float of those
-// channels, then the KC / 32 MFMA K steps' w_x operands [K step][4 K groups][Pp][8] bf16.
+// channels, the KC / 32 MFMA K steps' w_x operands [K step][4 K groups][Pp][8] bf16, then the
+// initial conv state [MS][KC][3] float of the workgroup's first MS sequences (the sequence of
+// its first token and the next ones), which the first three tokens of a sequence read in place
+// of x rows from before the sequence.
 template <int NT>
 struct PinGeo {
   static constexpr int Pp = NT * 16;
@@ -73,13 +76,20 @@ struct PinGeo {
   static constexpr int XP = kPinXRows * KC / 8;            // 16-byte pieces per part: x,
   static constexpr int CWP = KC;                           // conv weights,
   static constexpr int CBP = KC / 4;                       // biases,
-  static constexpr int WP = SUB * 4 * Pp;                  // w_x operands
-  static constexpr int HP = XP + CWP + CBP + WP;
+  static constexpr int WP = SUB * 4 * Pp;                  // w_x operands,
+  static constexpr int CSP = KC * kKS / 4;                 // and per staged sequence, its conv state
+  static constexpr int HP0 = XP + CWP + CBP + WP;
+  static constexpr int L = (HP0 + kPinPartThreads - 1) / kPinPartThreads;  // loads per thread and stage
+  // sequences whose initial conv state is staged: as many (up to 3) as fit in the load slots
+  // the other pieces leave free
+  static constexpr int MS0 = (L * kPinPartThreads - HP0) / CSP;
+  static constexpr int MS = MS0 < 3 ? MS0 : 3;
+  static constexpr int HP = HP0 + MS * CSP;
   static constexpr int CWOFF = kPinXRows * XSTRIDE * 2;    // byte offsets within a part
   static constexpr int CBOFF = CWOFF + KC * 16;
   static constexpr int WOFF = CBOFF + KC * 4;
-  static constexpr int HB = WOFF + WP * 16;                // bytes per part
-  static constexpr int L = (HP + kPinPartThreads - 1) / kPinPartThreads;  // loads per thread and stage
+  static constexpr int CSOFF = WOFF + WP * 16;
+  static constexpr int HB = CSOFF + MS * KC * kKS * 4;     // bytes per part
   static constexpr int D = KP == 2 && NT <= 6 ? 4 : 1;     // stages in flight
 };
 template <int NT>
@@ -175,7 +185,7 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
     const uint16_t* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     const int32_t* __restrict__ cu, const float* __restrict__ conv_state, const uint16_t* __restrict__ wxP,
     uint16_t* __restrict__ dth, uint16_t* __restrict__ dtl, uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    int S, int64_t T, int d, int N, int R, int Rp, int nks) {
+    int S, int64_t T, int d, int N, int R, int Rp, int nks, const float* __restrict__ cs_stage, int cs16) {
   extern __shared__ __align__(16) unsigned char smem[];
   using G = PinGeo<NT>;
   constexpr int Pp = G::Pp, HB = G::HB, HP = G::HP, L = G::L, D = G::D, SUB = G::SUB, KC = G::KC, KP = G::KP;
@@ -203,12 +213,22 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
   const int s = seq_of(cu, S, t);
   const int64_t back = t - cu[s];  // tokens of the sequence before t
   const float* cs = conv_state + static_cast<int64_t>(s) * d64 * kKS;
+  // the staged conv states are those of sequences s_first .. s_first + MS - 1, loaded from
+  // cs_stage: conv_state when it is 16-byte aligned (cs16), else conv_state rounded down to 16
+  // bytes (in the same 16-byte block, so mapped) and not used; a wave whose lanes before the
+  // fourth token of their sequence all have theirs staged reads them from LDS, any other wave
+  // from global memory
+  const int s_first = seq_of(cu, S, t0);
+  const bool cs_lds = G::MS > 0 && cs16 != 0 && !__any(back < kKS && s - s_first >= G::MS);
+  const int js = s - s_first;
 
   // The four waves of part q stage part q's pieces, so that a thread's stage index is
   // wave-uniform.  The pieces of thread i of a part are p = i + 256 k (k < L): the x
   // pieces (staged row p / (KC/8) = token t0 - 3 + p / (KC/8) clamped into 0 .. T-1, channels
   // 8 (p % (KC/8)) .. of the stage), KC conv weight rows (float4), KC / 4 pieces of four biases,
-  // and the stage's w_x operand pieces (contiguous).  Each piece keeps a 64-bit base, the byte
+  // the staged sequences' conv state pieces (KC channels x 3 floats each, contiguous), and the
+  // stage's w_x operand pieces (contiguous; last, so that the load slots that hold only w_x
+  // pieces keep wave-uniform bases and steps).  Each piece keeps a 64-bit base, the byte
   // offset of its part's first stage, the bytes it advances per stage and the largest offset it
   // may read: channels past d read clamped, valid addresses (their u is forced to 0); slots past
   // the part's pieces load a valid address and go to a dummy slot.  (Offsets fit 32 bits for
@@ -224,7 +244,8 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
     for (int k = 0; k < L; ++k) {
       const int q = ht + kPinPartThreads * k;
       const bool real = q < HP;
-      const int p = real ? q : G::XP + G::CWP + G::CBP;  // a w_x piece
+      constexpr int P_CS = G::XP + G::CWP + G::CBP, P_W = P_CS + G::MS * G::CSP;
+      const int p = real ? q : P_W;  // a w_x piece
       pdst[k] = hs * HB;
       if (p < G::XP) {
         int64_t tok = t0 - kKS + p / (KC / 8);
@@ -240,14 +261,22 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
         pinc[k] = KC * 16;
         plim[k] = static_cast<uint32_t>(d - 1) * 16u;
         pdst[k] += G::CWOFF + (p - G::XP) * 16;
-      } else if (p < G::XP + G::CWP + G::CBP) {
+      } else if (p < P_CS) {
         pbase[k] = reinterpret_cast<const unsigned char*>(conv_b);
         poff[k] = static_cast<uint32_t>(kb + 4 * (p - G::XP - G::CWP)) * 4u;
         pinc[k] = KC * 4;
         plim[k] = static_cast<uint32_t>(d - 4) * 4u;
         pdst[k] += G::CBOFF + (p - G::XP - G::CWP) * 16;
+      } else if (p < P_W) {  // conv state: sequence s_first + jj (clamped to S - 1), 4 floats
+        const int jj = (p - P_CS) / G::CSP, pp = (p - P_CS) % G::CSP;
+        const int sj = s_first + jj < S ? s_first + jj : S - 1;
+        pbase[k] = reinterpret_cast<const unsigned char*>(cs_stage) + static_cast<int64_t>(sj) * d64 * kKS * 4;
+        poff[k] = static_cast<uint32_t>(kb * kKS + 4 * pp) * 4u;
+        pinc[k] = KC * kKS * 4;
+        plim[k] = static_cast<uint32_t>(d * kKS - 4) * 4u;
+        pdst[k] += G::CSOFF + (p - P_CS) * 16;
       } else {  // w_x: a stage's operands are SUB * 4 Pp contiguous pieces
-        const int pw = p - G::XP - G::CWP - G::CBP;
+        const int pw = p - P_W;
         pbase[k] = reinterpret_cast<const unsigned char*>(wxP);
         poff[k] = static_cast<uint32_t>(kb / kProjK * 4 * Pp + pw) * 16u;
         pinc[k] = SUB * 4 * Pp * 16;
@@ -299,12 +328,28 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
       }
     }
     if (STATE && back < kKS && live) {  // rows before the sequence: its initial conv state
+      if (cs_lds) {
+        // one lane offset per row, made opaque so that the eight channels' reads keep it and
+        // differ only in their immediate offsets (hoisted per channel, the offsets would take
+        // 24 registers)
 #pragma unroll
-      for (int r = 0; r < kKS; ++r) {
-        if (back - (kKS - r) < 0) {
-          const int64_t col = back + r;
+        for (int r = 0; r < kKS; ++r) {
+          if (back - (kKS - r) < 0) {
+            int lo = ((js * KC + sub * kProjK + kg * 8) * kKS + static_cast<int>(back) + r) * 4;
+            asm volatile("" : "+v"(lo));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xr[r][e] = cs[static_cast<int64_t>(c + e) * kKS + col];
+            for (int e = 0; e < 8; ++e) xr[r][e] = *reinterpret_cast<const float*>(hb + G::CSOFF + lo + e * kKS * 4);
+          }
+        }
+      } else {  // (the same opaque per-row address)
+#pragma unroll
+        for (int r = 0; r < kKS; ++r) {
+          if (back - (kKS - r) < 0) {
+            const float* gp = cs + (static_cast<int64_t>(c) * kKS + back + r);
+            asm volatile("" : "+v"(gp));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[r][e] = gp[e * kKS];
+          }
         }
       }
     }

@@ -123,3 +123,24 @@ def test_project_m1p4b_width():
     o = oracle.project(f["x"], f["conv_w"], f["conv_b"], f["cu"], f["cs"], f["w_x"], f["w_dt"], R, N)
     w = [_close(dt, o["dt"], "dt"), _close(B, o["B"], "B"), _close(C, o["C"], "C")]
     log(f"[proj] 1.4B width: worst err/bound dt {w[0]:.3g} B {w[1]:.3g} C {w[2]:.3g}")
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_project_conv_state_paths(offset):
+    """Sequences that start inside a 64-token tile read their initial conv state either from the
+    workgroup's staged copy (up to three sequences per tile, conv_state 16-byte aligned) or from
+    global memory (more sequences in the tile, or conv_state only 4-byte aligned: offset 1 float).
+    Tiles here hold 1, 3 and 5 sequence starts; every output against the oracle."""
+    lens, d, N, R = [64, 20, 30, 14, 9, 7, 5, 40, 3, 2, 90], 4096, 16, 128
+    f = _case(300 + offset, lens, d, N, R)
+    S = len(lens)
+    flat = torch.zeros(S * d * 3 + 4, dtype=torch.float32, device="cuda")
+    cs = flat[offset:offset + S * d * 3].view(S, d, 3)
+    cs.copy_(dev(f["cs"]))
+    log(f"[proj] conv state paths: lens={lens} offset={offset} (ptr % 16 = {cs.data_ptr() % 16})")
+    dt, B, C = mm.project(dev(f["x"]), dev(f["conv_w"]), dev(f["conv_b"]), dev(f["cu"]), cs, dev(f["w_x"]),
+                          dev(f["w_dt"]))
+    torch.cuda.synchronize()
+    o = oracle.project(f["x"], f["conv_w"], f["conv_b"], f["cu"], f["cs"], f["w_x"], f["w_dt"], R, N)
+    w = [_close(host(dt), o["dt"], "dt"), _close(host(B), o["B"], "B"), _close(host(C), o["C"], "C")]
+    log(f"[proj] conv state paths offset {offset}: worst err/bound dt {w[0]:.3g} B {w[1]:.3g} C {w[2]:.3g}")
