@@ -110,6 +110,11 @@ constexpr int kPdtCh = 128;                // channels per workgroup (8 column t
 constexpr int kPdtTiles = kPdtCh / 16;
 constexpr int kPdtOStride = kPdtCh + 8;    // bf16 per row of a wave's output tile (272 bytes)
 constexpr int kPdtWGs = 768;               // about three workgroups per CU
+// a raw buffer resource's fourth word on gfx9-family targets (32-bit data format, no swizzle,
+// range checked against the byte count), and a store offset past any range k_proj_dt makes
+// (ranges stay below 16 rows x 2^22 channels x 2 bytes = 2^27)
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufPastEnd = 0x7FFFFFF0;
 inline size_t pdt_lds_bytes(int KR) {      // the block's w_dt operands, then per wave an output tile
   return static_cast<size_t>(KR) * 4 * kPdtCh * 16 + static_cast<size_t>(kPdtWaves) * 16 * kPdtOStride * 2;
 }
@@ -592,13 +597,22 @@ __global__ void __launch_bounds__(kPdtThreads) k_proj_dt(const uint16_t* __restr
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's tile written before it reads it
+    {
+      // buffer stores over the tile's rows: the hardware drops the stores of rows past T (past
+      // the range) and of lanes past d (sent past it).  With no branch around them, the
+      // compiler's count of outstanding memory operations stays exact, so its wait for the next
+      // tile's dt_in loads does not also wait for these stores to complete.
+      const int64_t r0 = tt * 16;
+      const int nr = T - r0 < 16 ? static_cast<int>(T - r0) : 16;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(dt + r0 * d64, 0, nr * d * 2, kBufWord3);
 #pragma unroll
-    for (int k = 0; k < 16 * kPdtCh / 8 / kWave; ++k) {
-      const int i = lane + kWave * k;
-      const int r = i / (kPdtCh / 8), part = i % (kPdtCh / 8);
-      const int64_t tg = tt * 16 + r;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + r * kPdtOStride + part * 8);
-      if (tg < T && c0 + part * 8 < d) *reinterpret_cast<u32x4_t*>(dt + tg * d64 + c0 + part * 8) = v;
+      for (int k = 0; k < 16 * kPdtCh / 8 / kWave; ++k) {
+        const int i = lane + kWave * k;
+        const int r = i / (kPdtCh / 8), part = i % (kPdtCh / 8);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + r * kPdtOStride + part * 8);
+        const int off = c0 + part * 8 < d ? (r * d + c0 + part * 8) * 2 : kBufPastEnd;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+      }
     }
 #pragma unroll
     for (int k = 0; k < 2 * KR; ++k) acur[k] = anxt[k];
