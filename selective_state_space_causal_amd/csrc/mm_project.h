@@ -58,8 +58,9 @@ constexpr int kPinXRows = kPinTok + kKS;       // staged x rows: t-3 .. t+63
 // Stage geometry of k_proj_in for NT output column tiles.  The K range is split into KP parts,
 // each taken by kPinRT waves (one per 16-token row tile): four parts up to 10 column tiles
 // (16 waves per workgroup, four per SIMD), two for the widest outputs, whose operands would not
-// fit four times in LDS.  A stage holds KC channels (32 with four parts; 64 with two, so that
-// every x row piece is a whole 128-byte line, or 32 for the widest outputs) for each part: x
+// fit four times in LDS.  A stage holds KC channels (32 with four parts, whose neighbouring
+// pieces make whole 128-byte lines of x; 64 with two, a whole line each, or 32 for the widest
+// outputs) for each part: x
 // [kPinXRows][KC + 8] bf16, the conv weights [KC] float4 and biases [KC] float of those
 // channels, the KC / 32 MFMA K steps' w_x operands [K step][4 K groups][Pp][8] bf16, then the
 // initial conv state [MS][KC][3] float of the workgroup's first MS sequences (the sequence of
@@ -177,9 +178,9 @@ __global__ void __launch_bounds__(kBlock) k_proj_pack(const uint16_t* __restrict
 
 // [dt_in | B | C] = u x w_x for 64 tokens per workgroup, NT = Pp / 16 output column tiles (a
 // template argument: the MFMAs run without guards); nks = dk / 32 MFMA K steps, grouped in
-// stages of G::SUB.  Wave w takes row tile w % 4 and K part w / 4 (a consecutive run of the
-// stages).  Stage g holds, for each part, everything its g-th stage needs (see PinGeo); the four
-// waves of a part share its w_x operands.  The workgroup's threads load stage g + D
+// stages of G::SUB.  Wave w takes row tile w % 4 and K part w / 4 (its share of the K range, as
+// laid out below).  Stage g holds, for each part, everything its g-th stage needs (see PinGeo);
+// the four waves of a part share its w_x operands.  The workgroup's threads load stage g + D
 // into registers while stage g runs; those are the only global loads of the loop (bar the
 // conv state of a sequence's first tokens), so waiting for stage g, which was issued first,
 // never waits for a later one.  Two LDS stage buffers and one barrier per stage.  LDS
@@ -203,14 +204,28 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
   const int kg = lane >> 4;   // 8-wide K group
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPinTok;
   const int64_t d64 = d;
-  // the nstg stages split into KP consecutive runs, the last ones one stage longer when they do
-  // not divide evenly; the loop runs nst (the longest run) stages
+  // The nstg units of KC channels (SUB MFMA K steps each) are grouped by 128-byte line of x: U
+  // units per line (two of 32 channels, or one of 64).  The lines split into GR = KP / U
+  // consecutive runs of H lines, one per group of U parts, and part q takes unit q % U of each
+  // line of run q / U: at stage g, line g of its run.  So the U parts of a group read the two
+  // halves of a line at the same stage (one part running through a range of its own would
+  // read them one stage apart, and at row strides of a power of two the line is then often
+  // gone from the L2: 1.5x the algorithmic HBM bytes at d_inner 4096), while the GR runs keep
+  // the workgroup's reads at GR places of the rows (one place, all parts side by side, was 5%
+  // slower at d_inner 4096).  The loop runs nst = H stages.
   const int nstg = (nks + SUB - 1) / SUB;
-  const int sbase = nstg / KP, srem = nstg % KP;
-  auto part_len = [&](int q) { return sbase + (q >= KP - srem ? 1 : 0); };
-  auto part_beg = [&](int q) { return q * sbase + (q > KP - srem ? q - (KP - srem) : 0); };
-  const int nst = sbase + (srem > 0 ? 1 : 0);
-  const int sbeg = part_beg(h), slen = part_len(h);
+  constexpr int U = KC == 32 ? 2 : 1;  // units per 128-byte line of x
+  constexpr int GR = KP / U;           // line streams
+  const int nl = (nstg + U - 1) / U;
+  const int H = (nl + GR - 1) / GR;    // lines per stream
+  auto part_len = [&](int q) {
+    const int n = (nstg - q % U + U - 1) / U - (q / U) * H;
+    return n < 0 ? 0 : (n < H ? n : H);
+  };
+  auto part_unit0 = [&](int q) { return (q / U) * H * U + q % U; };
+  const int nst = H;
+  const int slen = part_len(h);
+  const int u0 = part_unit0(h);
 
   // this lane's token and its sequence (rows past T compute on a valid token and store nothing)
   int64_t t = t0 + rt * 16 + row;
@@ -244,7 +259,7 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
   uint32_t poff[L], pinc[L], plim[L];
   int pdst[L];
   {
-    const int kb = part_beg(hs) * KC;  // the part's first channel
+    const int kb = part_unit0(hs) * KC;  // the part's first channel
 #pragma unroll
     for (int k = 0; k < L; ++k) {
       const int q = ht + kPinPartThreads * k;
@@ -257,19 +272,19 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
         tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);
         pbase[k] = reinterpret_cast<const unsigned char*>(x + tok * d64);
         poff[k] = static_cast<uint32_t>(kb + 8 * (p % (KC / 8))) * 2u;
-        pinc[k] = KC * 2;
+        pinc[k] = U * KC * 2;
         plim[k] = static_cast<uint32_t>(d - 8) * 2u;
         pdst[k] += (p / (KC / 8)) * G::XSTRIDE * 2 + (p % (KC / 8)) * 16;
       } else if (p < G::XP + G::CWP) {
         pbase[k] = reinterpret_cast<const unsigned char*>(conv_w);
         poff[k] = static_cast<uint32_t>(kb + (p - G::XP)) * 16u;
-        pinc[k] = KC * 16;
+        pinc[k] = U * KC * 16;
         plim[k] = static_cast<uint32_t>(d - 1) * 16u;
         pdst[k] += G::CWOFF + (p - G::XP) * 16;
       } else if (p < P_CS) {
         pbase[k] = reinterpret_cast<const unsigned char*>(conv_b);
         poff[k] = static_cast<uint32_t>(kb + 4 * (p - G::XP - G::CWP)) * 4u;
-        pinc[k] = KC * 4;
+        pinc[k] = U * KC * 4;
         plim[k] = static_cast<uint32_t>(d - 4) * 4u;
         pdst[k] += G::CBOFF + (p - G::XP - G::CWP) * 16;
       } else if (p < P_W) {  // conv state: sequence s_first + jj (clamped to S - 1), 4 floats
@@ -277,14 +292,14 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
         const int sj = s_first + jj < S ? s_first + jj : S - 1;
         pbase[k] = reinterpret_cast<const unsigned char*>(cs_stage) + static_cast<int64_t>(sj) * d64 * kKS * 4;
         poff[k] = static_cast<uint32_t>(kb * kKS + 4 * pp) * 4u;
-        pinc[k] = KC * kKS * 4;
+        pinc[k] = U * KC * kKS * 4;
         plim[k] = static_cast<uint32_t>(d * kKS - 4) * 4u;
         pdst[k] += G::CSOFF + (p - P_CS) * 16;
       } else {  // w_x: a stage's operands are SUB * 4 Pp contiguous pieces
         const int pw = p - P_W;
         pbase[k] = reinterpret_cast<const unsigned char*>(wxP);
         poff[k] = static_cast<uint32_t>(kb / kProjK * 4 * Pp + pw) * 16u;
-        pinc[k] = SUB * 4 * Pp * 16;
+        pinc[k] = U * SUB * 4 * Pp * 16;
         plim[k] = static_cast<uint32_t>(nks * 4 * Pp - 1) * 16u;  // the last operand piece
         pdst[k] += G::WOFF + pw * 16;
       }
@@ -433,7 +448,7 @@ __global__ void __launch_bounds__(PinGeo<NT>::THREADS) k_proj_in(
       if (g < slen) {
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub) {
-          const int ks = (sbeg + g) * SUB + sub;
+          const int ks = (u0 + g * U) * SUB + sub;
           if (ks < nks) kstep(buf, ks, sub, state);
         }
       }
