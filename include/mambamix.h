@@ -388,7 +388,9 @@ size_t mamba_mixer_checkpoint_bytes(int32_t S, int64_t T, int32_t d);
  *
  *   x            [T, d]      bf16   raw SSM-path input (before the conv), 16-byte aligned
  *   conv_w [d, K], conv_b [d]  f32  16-byte aligned;  cu_seqlens [S+1]
- *   conv_state   [S, d, K-1] f32    the INITIAL conv state (read only)
+ *   conv_state   [S, d, K-1] f32    the INITIAL conv state (read only); 4-byte aligned, and when
+ *                                   16-byte aligned the kernel stages it with the x tiles (faster
+ *                                   for tiles where sequences start)
  *   w_x          [d, R+2N]   bf16   input-major: columns 0..R-1 are w_dt_in, then w_B, then w_C
  *   w_dt         [R, d]      bf16   w_dt_out
  *   dt           [T, d]      bf16   out, 16-byte aligned
