@@ -116,6 +116,9 @@ constexpr int kPdtWGs = 768;               // about three workgroups per CU
 // (ranges stay below 16 rows x 2^22 channels x 2 bytes = 2^27)
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kBufPastEnd = 0x7FFFFFF0;
+// cache-policy operand of the buffer stores: nontemporal (dt is written once and not read back
+// by this call; the hint saved 5-10% of k_proj_dt's time)
+constexpr int kBufNontemporal = 2;
 inline size_t pdt_lds_bytes(int KR) {      // the block's w_dt operands, then per wave an output tile
   return static_cast<size_t>(KR) * 4 * kPdtCh * 16 + static_cast<size_t>(kPdtWaves) * 16 * kPdtOStride * 2;
 }
@@ -626,7 +629,7 @@ __global__ void __launch_bounds__(kPdtThreads) k_proj_dt(const uint16_t* __restr
         const int r = i / (kPdtCh / 8), part = i % (kPdtCh / 8);
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + r * kPdtOStride + part * 8);
         const int off = c0 + part * 8 < d ? (r * d + c0 + part * 8) * 2 : kBufPastEnd;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kBufNontemporal);
       }
     }
 #pragma unroll
